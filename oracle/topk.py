@@ -1,0 +1,73 @@
+"""Python entry to the C++ oracle (``oracle_topk.cpp``). TEST INFRASTRUCTURE ONLY.
+
+The library is built with g++ on first use (or by ``build()``); it is plain host C++.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_topk.cpp")
+_LIB = os.path.join(_HERE, "liboracle_topk.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle library in place (g++, -O2, pthreads). Returns its path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-pthread", _SRC, "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            lib.oracle_topk.restype = ctypes.c_int
+            lib.oracle_topk.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+            lib.oracle_hw_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def hw_threads() -> int:
+    return int(_load().oracle_hw_threads())
+
+
+def topk(x: np.ndarray, k: int, values: bool = True, indices: bool = True,
+         threads: Optional[int] = None) -> Tuple[Optional[np.ndarray], Optional[np.ndarray]]:
+    """Top-k of every row of ``x`` (2-D; uint16 = bf16 bits, float32 = fp32).
+
+    Returns (values [rows,k] in the input's dtype, indices [rows,k] int32); either may be
+    skipped. Ordering: value descending, +0 before -0, then index ascending.
+    """
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D")
+    if x.dtype == np.uint16:
+        dtype = 0
+    elif x.dtype == np.float32:
+        dtype = 1
+    else:
+        raise ValueError("x must be uint16 (bf16 bits) or float32")
+    x = np.ascontiguousarray(x)
+    rows, n = x.shape
+    vals = np.empty((rows, k), x.dtype) if values else None
+    idx = np.empty((rows, k), np.int32) if indices else None
+    rc = _load().oracle_topk(x.ctypes.data, rows, n, n, int(k), dtype,
+                             vals.ctypes.data if vals is not None else None,
+                             idx.ctypes.data if idx is not None else None, int(threads or 0))
+    if rc != 0:
+        raise ValueError(f"oracle_topk rejected the arguments (rows={rows}, n={n}, k={k})")
+    return vals, idx
