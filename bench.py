@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark: effective input GB/s of one DeepSelect top-k call on one MI355X.
+
+A step is one whole top-k call (select kernel over every row slice, then the merge kernel)
+over one batch of synthetic input already resident in HBM. Timing: W warmup steps, then K
+steps between two events on the launch stream, each step reading a different copy of the
+input from a pool of >= 512 MiB, so the 256 MB Infinity Cache cannot serve it (cold). The
+same loop over one buffer is reported as the warm figure. Events around every launch give
+the select kernel's own average duration (the roofline figure). The CPU oracle is timed on
+the host cores on a bounded sample of the same workload.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "effective input GB/s per top-k call (and % of HBM peak) at 1 MI355X"
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def upload(x, torch):
+    import numpy as np
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(x).cuda()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("ds_kernels.hip", "ds_api.cpp", "ds_internal.h"):
+        with open(os.path.join(ROOT, "top_selection_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, digest: str):
+    """HBM bytes per select launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"select_kernel_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic:"):
+                for kv in line.split()[1:]:
+                    key, _, val = kv.partition("=")
+                    vals[key] = val
+    if vals.get("source") != digest or "bytes_per_launch" not in vals:
+        return None
+    return float(vals["bytes_per_launch"])
+
+
+def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True):
+    import numpy as np
+    from workloads import gen
+
+    log(f"[bench] generating {w.name}: {w.rows} x {w.n} {gen.DTYPE_NAMES[w.dtype]}")
+    x = w.make()
+    xd = upload(x, torch)
+    in_bytes = w.input_bytes()
+    copies = max(1, math.ceil(pool_mib * 2 ** 20 / in_bytes))
+    pool = [xd] + [xd.clone() for _ in range(copies - 1)]
+    rows, n = w.rows, w.n
+    plan = ts.ds_topk_plan(rows, n, k, w.dtype)
+    wsb = ts.ds_topk_workspace_size(rows, n, k, w.dtype)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    vals = torch.empty((rows, k), dtype=xd.dtype, device="cuda")
+    idx = None if w.values_only else torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(src):
+        ts.ds_topk_slices(src, k, seed=seed, workspace=ws, out_vals=vals, out_idx=idx, indices=idx is not None)
+        ts.ds_topk_merge(rows, n, k, w.dtype, seed=seed, workspace=ws, out_vals=vals, out_idx=idx)
+
+    log(f"[bench] {w.name}: plan {plan}, pool {copies} copies, warmup {warmup}")
+    for i in range(warmup):
+        step(pool[i % copies])
+    torch.cuda.synchronize()
+
+    def timed(get_src):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        mids = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(steps):
+            a, b = mids[i]
+            a.record(stream)
+            ts.ds_topk_slices(get_src(i), k, seed=seed, workspace=ws, out_vals=vals, out_idx=idx,
+                              indices=idx is not None)
+            b.record(stream)
+            ts.ds_topk_merge(rows, n, k, w.dtype, seed=seed, workspace=ws, out_vals=vals, out_idx=idx)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        total = t0.elapsed_time(t1)
+        sel = [a.elapsed_time(b) for a, b in mids]
+        return total / steps, sum(sel) / len(sel)
+
+    ms_cold, sel_cold = timed(lambda i: pool[i % copies])
+    log(f"[bench] {w.name} cold: {ms_cold * 1e3:.2f} us/call, select {sel_cold * 1e3:.2f} us")
+    ms_warm, sel_warm = timed(lambda i: pool[0])
+    log(f"[bench] {w.name} warm: {ms_warm * 1e3:.2f} us/call, select {sel_warm * 1e3:.2f} us")
+
+    parity = None
+    if verify:
+        from oracle import topk as otk
+        step(pool[-1])
+        torch.cuda.synchronize()
+        want_v, want_i = otk.topk(x, k, indices=idx is not None)
+        got_v = vals.view(torch.int16).cpu().numpy().view(np.uint16) if x.dtype == np.uint16 else vals.cpu().numpy()
+        ok = np.array_equal(got_v.view(np.uint8), want_v.view(np.uint8))
+        if idx is not None:
+            ok = ok and np.array_equal(idx.cpu().numpy(), want_i)
+        parity = "bit-exact" if ok else "MISMATCH"
+        log(f"[bench] {w.name} parity vs oracle: {parity}")
+    del pool
+    return dict(x=x, plan=plan, copies=copies, ms_cold=ms_cold, sel_cold=sel_cold, ms_warm=ms_warm,
+                sel_warm=sel_warm, in_bytes=in_bytes, parity=parity, ws_bytes=wsb)
+
+
+def cpu_baseline(w, k, x, seconds):
+    from oracle import topk as otk
+    threads = otk.hw_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        otk.topk(x, k, indices=not w.values_only, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = w.input_bytes() * reps / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full passes of the {w.name} batch ({w.rows} rows x {w.n}) in {el:.1f} s: "
+                      f"C++ full sort per row, rows spread over {threads} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2_indexer")
+    ap.add_argument("--k", type=int, default=None)
+    ap.add_argument("--pool-mib", type=float, default=512.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across GPUs "
+              "without communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import top_selection_amd as ts
+    from workloads import gen
+
+    torch.cuda.set_device(0)
+    w = gen.WORKLOADS[args.workload]
+    k = args.k or w.ks[0]
+    r = time_workload(ts, torch, w, k, args.steps, args.warmup, args.pool_mib)
+    value = r["in_bytes"] / (r["ms_cold"] * 1e-3) / 1e9
+    sel_gbs = r["in_bytes"] / (r["sel_cold"] * 1e-3) / 1e9
+    digest = source_digest()
+    traffic = read_traffic(w.name, digest)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_cold"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": gen.DTYPE_NAMES[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "n": w.n, "k": k, "elem": gen.DTYPE_NAMES[w.dtype],
+                   "values_only": w.values_only, "block": r["plan"]["block"], "slack": r["plan"]["slack"],
+                   "slices": r["plan"]["slices"], "waves": r["plan"]["waves"], "input_pool_copies": r["copies"],
+                   "cold_inputs": True, "description": w.description},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "warm": {"value": round(r["in_bytes"] / (r["ms_warm"] * 1e-3) / 1e9, 2), "ms_per_step": round(r["ms_warm"], 6),
+                 "note": "same input buffer every step (may be served by the Infinity Cache)"},
+        "pages_style_gbs": round((r["in_bytes"] + w.rows * k * (w.elem_bytes + (0 if w.values_only else 4)))
+                                 / (r["ms_cold"] * 1e-3) / 1e9, 2),
+        "parity": r["parity"],
+        "roofline": {"bound": "hbm", "kernel": "select_kernel", "achieved": round(sel_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(sel_gbs / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(r["sel_cold"] * 1e3, 3),
+                     "algorithmic_bytes_per_launch": r["in_bytes"],
+                     "traffic": traffic, "source": digest},
+    }
+    if not args.no_secondary:
+        sec = {}
+        for name in ("c3_sampler",):
+            if name == w.name:
+                continue
+            sw = gen.WORKLOADS[name]
+            s = time_workload(ts, torch, sw, sw.ks[0], max(20, args.steps // 2), args.warmup, args.pool_mib)
+            sv = s["in_bytes"] / (s["ms_cold"] * 1e-3) / 1e9
+            sec[name] = {"value": round(sv, 2), "unit": "GB/s", "pct_of_hbm_peak": round(100 * sv / HBM_PEAK_GBS, 2),
+                         "ms_per_step": round(s["ms_cold"], 6), "select_us": round(s["sel_cold"] * 1e3, 3),
+                         "warm_value": round(s["in_bytes"] / (s["ms_warm"] * 1e-3) / 1e9, 2),
+                         "plan": s["plan"], "parity": s["parity"]}
+        out["secondary"] = sec
+    if not args.no_cpu:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(w, k, r["x"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0 if r["parity"] != "MISMATCH" else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

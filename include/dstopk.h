@@ -1,0 +1,167 @@
+/*
+ * dstopk.h -- DeepSelect row-wise top-k selection for AMD Instinct MI355X (gfx950).
+ *
+ * The method is DeepSelect as given in the DeepSelect design note ("Algorithm",
+ * DeepSelectTopk pseudocode): keep a threshold T; read the row once, in blocks of B
+ * elements taken in a random order that does not depend on the data; append the
+ * elements that beat T to an on-chip candidate buffer; when the buffer holds at least
+ * k + B2 entries, reduce it to the k best with a radix select and raise T to the
+ * smallest of them; after the last block, one more radix select gives the answer.
+ * Long rows can be cut into slices that run the method independently; a merge step
+ * then selects the k best of the slices' survivors (the cluster split of the design
+ * note's "Implementation" section, here through a device workspace).
+ *
+ * Result contract (the plain definition the method reaches exactly):
+ *   for every row r, the k largest elements of x[r, 0..N) under the total order
+ *   "larger value first; +0 before -0; then smaller index first", written in that
+ *   order. Values are the input's own bit patterns; indices are int32, relative to the
+ *   row. The result does not depend on `seed`, the block size or the slicing.
+ *
+ * Conventions for every entry point:
+ *   - x, out_vals, out_idx, workspace and stats are DEVICE pointers (HIP).
+ *   - stream is a hipStream_t passed as void*; NULL is the default stream.
+ *   - All work is enqueued on `stream`; calls are asynchronous and never synchronise.
+ *   - Arguments are validated on the host before anything is enqueued; an invalid call
+ *     returns a negative status and enqueues nothing.
+ *   - Precondition: x holds no NaN (the output is unspecified otherwise); +-inf and
+ *     +-0 are allowed.
+ *   - No entry point keeps a pointer after it returns.
+ */
+#ifndef DSTOPK_H
+#define DSTOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define DS_BF16 0 /* bfloat16, 2 bytes, the Lightning Indexer scores */
+#define DS_FP32 1 /* float32, 4 bytes, the sampler logits */
+
+/* status codes */
+#define DS_OK 0
+#define DS_ERR_INVALID_ARG (-1) /* bad sizes, k, pointers or dtype */
+#define DS_ERR_UNSUPPORTED (-2) /* a forced configuration this build has no kernel for */
+#define DS_ERR_ALIGNMENT (-3)   /* x or row_stride*elem_bytes not a multiple of 16 bytes */
+#define DS_ERR_WORKSPACE (-4)   /* workspace missing or smaller than ds_topk_workspace_size */
+#define DS_ERR_LAUNCH (-5)      /* the HIP runtime refused a launch or an allocation */
+#define DS_ERR_DEVICE (-6)      /* no usable gfx950 device, or a device query failed */
+
+#define DS_MAX_K 4096 /* the largest supported k (DeepSelect supports topk <= 4096) */
+
+/*
+ * Launch configuration. Zero in any field means "choose automatically".
+ *   block   B: elements per block; a multiple of 512 (bf16) or 256 (fp32) equal to
+ *              waves * chunks_per_wave * that chunk size for one of the built kernels.
+ *   slack   B2: the buffer is compacted when it holds >= k + B2 entries (B2 >= 1).
+ *   slices  S: workgroups per row (the split-row path when > 1).
+ *   waves   64-lane waves per workgroup.
+ */
+typedef struct ds_config {
+  int32_t block;
+  int32_t slack;
+  int32_t slices;
+  int32_t waves;
+} ds_config;
+
+/*
+ * Per-(row, slice) counters of one run, filled when ds_topk_ex gets a stats pointer.
+ * Names follow the design note's analysis section.
+ */
+typedef struct ds_stats {
+  uint64_t appended;    /* A: elements appended to the candidate buffer */
+  uint64_t compactions; /* R: in-loop radix-select compactions */
+  uint64_t work;        /* W: summed input sizes of all compactions, the final one included */
+  uint64_t max_len;     /* largest buffer length after a block's appends */
+  uint64_t reads;       /* elements read from x */
+  uint64_t index_sum;   /* sum of the row indices of the elements read */
+  uint64_t monotone;    /* 1 if every new threshold ranked at or below the previous one */
+  uint64_t slice_lo;    /* first row index of the slice */
+  uint64_t slice_len;   /* elements in the slice */
+  uint64_t block;       /* B used */
+  uint64_t slack;       /* B2 used */
+  uint64_t reserved;
+} ds_stats;
+
+/*
+ * ds_topk -- top-k of every row.
+ *   x          device, rows x row_stride elements of `dtype`; row r starts at
+ *              x + r*row_stride elements. 16-byte aligned; row_stride*elem_bytes a
+ *              multiple of 16 (DS_ERR_ALIGNMENT otherwise).
+ *   rows       >= 0; rows == 0 returns DS_OK and enqueues nothing.
+ *   n          elements per row, 1 <= n <= 2^31 - 1; row_stride >= n.
+ *   k          1 <= k <= min(DS_MAX_K, n).
+ *   dtype      DS_BF16 or DS_FP32.
+ *   seed       picks the block order only; it never changes the result.
+ *   out_vals   device [rows, k] of `dtype` (bit patterns of the selected elements), or NULL.
+ *   out_idx    device [rows, k] int32, or NULL (values only). Not both NULL.
+ *   stream     hipStream_t as void*.
+ * When the split path needs scratch memory, ds_topk takes it from a per-device cache that
+ * grows on demand (hipMalloc on the calling thread, the first time a larger size is
+ * needed) and lives until the library is unloaded. Use ds_topk_ex to pass it instead.
+ */
+int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
+            void* out_vals, int32_t* out_idx, void* stream);
+
+/*
+ * ds_topk_plan -- the configuration ds_topk / ds_topk_ex would use (cfg may force some
+ * fields; NULL = all automatic). Writes it to *out. Host only, no device call except a
+ * one-time query of the current device's compute-unit count.
+ */
+int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, ds_config* out);
+
+/*
+ * ds_topk_workspace_size -- bytes of device workspace ds_topk_ex needs for this call
+ * (0 when the plan has one slice per row). Writes it to *bytes.
+ */
+int ds_topk_workspace_size(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, size_t* bytes);
+
+/*
+ * ds_topk_ex -- ds_topk with a caller workspace, a forced configuration and counters.
+ *   workspace  device, >= ds_topk_workspace_size bytes, 256-byte aligned; may be NULL when
+ *              that size is 0. Its contents on entry do not matter; it is overwritten.
+ *   cfg        NULL or fields to force (see ds_config).
+ *   stats      NULL, or device [rows, slices] ds_stats filled by the select kernel.
+ * Allocates nothing.
+ */
+int ds_topk_ex(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
+               void* out_vals, int32_t* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
+               ds_stats* stats, void* stream);
+
+/*
+ * ds_topk_slices / ds_topk_merge -- ds_topk_ex as its two launches, for callers that
+ * want to time or overlap them separately. ds_topk_slices runs the select kernel: with one
+ * slice per row it writes the final outputs; otherwise it writes every slice's k survivors
+ * to the workspace. ds_topk_merge then reduces each row's survivors to the sorted top-k
+ * (it enqueues nothing when the plan has one slice). Both take the same arguments as
+ * ds_topk_ex (merge ignores x, row_stride and stats) and must be given the same rows, n, k,
+ * dtype, seed, cfg and workspace; the pair then equals one ds_topk_ex call.
+ */
+int ds_topk_slices(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
+                   void* out_vals, int32_t* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
+                   ds_stats* stats, void* stream);
+int ds_topk_merge(int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void* out_vals, int32_t* out_idx,
+                  void* workspace, size_t ws_bytes, const ds_config* cfg, void* stream);
+
+/*
+ * ds_probe_read -- measurement aid, not part of top-k: streams `bytes` (a multiple of
+ * 16, 16-byte aligned) from src with the same 16-byte loads the scan uses and writes
+ * one 32-bit word per workgroup to sink (device, >= ds_probe_sink_words(bytes) words).
+ */
+int ds_probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+int64_t ds_probe_sink_words(int64_t bytes);
+
+/* ds_probe_copy -- measurement aid: a plain 16-byte-vector copy of `bytes` (multiple of 16). */
+int ds_probe_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/* ds_status_string -- a static, human-readable name for a status code. */
+const char* ds_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSTOPK_H */

@@ -1,0 +1,83 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/dstopk.h declares, and rejects invalid calls before touching the device."""
+import ctypes
+
+import pytest
+
+import top_selection_amd as ts
+
+FAKE = 0x10000  # a 16-byte aligned address; never dereferenced by a rejected call
+
+
+def test_exports_every_declared_symbol():
+    names = ts.header_functions()
+    assert {"ds_topk", "ds_topk_ex", "ds_topk_plan", "ds_topk_workspace_size", "ds_status_string",
+            "ds_probe_read", "ds_probe_copy", "ds_probe_sink_words", "ds_topk_slices", "ds_topk_merge"} <= set(names)
+    lib = ts.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, name in [(0, "DS_OK"), (-1, "DS_ERR_INVALID_ARG"), (-2, "DS_ERR_UNSUPPORTED"),
+                       (-3, "DS_ERR_ALIGNMENT"), (-4, "DS_ERR_WORKSPACE"), (-5, "DS_ERR_LAUNCH"),
+                       (-6, "DS_ERR_DEVICE")]:
+        assert ts.ds_status_string(code) == name
+
+
+def _call(x=FAKE, rows=4, n=1024, stride=None, k=8, dtype=ts.BF16, vals=FAKE, idx=FAKE):
+    return ts.lib().ds_topk(x, rows, n, n if stride is None else stride, k, dtype, 1, vals, idx, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), ts.DS_ERR_INVALID_ARG),
+    (dict(k=1025, n=1024), ts.DS_ERR_INVALID_ARG),          # k > N
+    (dict(k=4097, n=10000), ts.DS_ERR_UNSUPPORTED),          # k > 4096
+    (dict(n=0), ts.DS_ERR_INVALID_ARG),
+    (dict(n=2 ** 31), ts.DS_ERR_INVALID_ARG),
+    (dict(rows=-1), ts.DS_ERR_INVALID_ARG),
+    (dict(stride=1000), ts.DS_ERR_INVALID_ARG),             # row_stride < N
+    (dict(dtype=2), ts.DS_ERR_INVALID_ARG),
+    (dict(x=None), ts.DS_ERR_INVALID_ARG),
+    (dict(vals=None, idx=None), ts.DS_ERR_INVALID_ARG),
+    (dict(x=FAKE + 8), ts.DS_ERR_ALIGNMENT),
+    (dict(n=1001, stride=1001), ts.DS_ERR_ALIGNMENT),        # 2002-byte rows
+])
+def test_rejects_before_launch(kw, code):
+    assert _call(**kw) == code
+
+
+def test_empty_rows_is_a_no_op():
+    assert _call(rows=0) == ts.DS_OK
+
+
+def test_workspace_rejected_without_touching_device():
+    cfg = ts._binding.ds_config(0, 0, 4, 0)
+    st = ts.lib().ds_topk_ex(FAKE, 2, 65536, 65536, 64, ts.BF16, 0, FAKE, FAKE, None, 0, ctypes.byref(cfg), None,
+                             None)
+    assert st == ts.DS_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("dtype", [ts.BF16, ts.FP32])
+@pytest.mark.parametrize("n,k,slices", [(32768, 512, 1), (131072, 512, 8), (129280, 512, 2), (1 << 20, 4096, 16),
+                                        (268435456, 32, 512), (5000, 77, 3), (300, 300, 1)])
+def test_forced_plans(dtype, n, k, slices):
+    p = ts.ds_topk_plan(8, n, k, dtype, {"slices": slices})
+    chunk = 512 if dtype == ts.BF16 else 256
+    assert p["block"] % chunk == 0
+    assert p["slices"] == slices
+    assert p["slack"] >= 1
+    per = -(-n // slices)
+    assert p["slices"] == -(-n // (-(-per // p["block"]) * p["block"]))
+    ws = ts.ds_topk_workspace_size(8, n, k, dtype, {"slices": slices})
+    assert ws == (0 if slices == 1 else 8 * slices * k * 8)
+
+
+def test_forced_block_sizes():
+    assert ts.ds_topk_plan(4, 32768, 512, ts.BF16, {"block": 1024, "slack": 1024, "slices": 1})["waves"] == 2
+    with pytest.raises(ts.DSError) as e:
+        ts.ds_topk_plan(4, 32768, 512, ts.BF16, {"block": 1000, "slices": 1})
+    assert e.value.status == ts.DS_ERR_UNSUPPORTED
+    with pytest.raises(ts.DSError) as e:  # too many slices for the row: one would be empty
+        ts.ds_topk_plan(1, 4096, 16, ts.FP32, {"slices": 64})
+    assert e.value.status == ts.DS_ERR_UNSUPPORTED

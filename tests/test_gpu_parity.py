@@ -1,0 +1,148 @@
+"""Bit-exact parity of the HIP path with the CPU oracle (values and indices, tolerance 0).
+
+Every call goes through the C ABI (the ctypes binding). Inputs are the seeded workload
+recipes (reduced row counts, then the full sizes in the launch configuration the
+benchmark times) plus edge families and a fuzz sweep; the expected values come from the
+oracle only.
+"""
+import numpy as np
+import pytest
+
+import top_selection_amd as ts
+from gpu_util import assert_same, run_gpu, say
+from oracle import model
+from oracle import topk as otk
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(x, k, label, seed=1, cfg=None, values=True, indices=True, pad_to=0):
+    say(f"[gpu] {label}: rows={x.shape[0]} n={x.shape[1]} k={k} dtype={x.dtype} cfg={cfg} seed={seed}")
+    gv, gi, _ = run_gpu(x, k, seed=seed, cfg=cfg, values=values, indices=indices, pad_to=pad_to)
+    wv, wi = otk.topk(x, k)
+    assert_same(x, k, gv, gi, wv if values else None, wi if indices else None, label)
+
+
+def test_smoke_small():
+    x = gen.WORKLOADS["c1_small"].make(rows=2, n=4096)
+    _check(x, 64, "smoke")
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_c1_small_forced_blocks(seed):
+    w = gen.WORKLOADS["c1_small"]
+    x = w.make()
+    _check(x, 512, "c1", seed=seed, cfg={"block": 1024, "slack": 1024, "slices": 1})
+    _check(x, 512, "c1-auto", seed=seed)
+
+
+@pytest.mark.parametrize("slices", [0, 1, 3, 8])
+def test_c2_indexer_rows(slices):
+    x = gen.WORKLOADS["c2_indexer"].make(rows=6)
+    _check(x, 512, f"c2 slices={slices}", cfg=None if slices == 0 else {"slices": slices})
+
+
+@pytest.mark.parametrize("slices", [0, 1, 2])
+def test_c3_sampler_rows(slices):
+    x = gen.WORKLOADS["c3_sampler"].make(rows=5)
+    _check(x, 512, f"c3 slices={slices}", cfg=None if slices == 0 else {"slices": slices})
+
+
+@pytest.mark.parametrize("k", [512, 4096])
+def test_c4_long_full(k):
+    x = gen.WORKLOADS["c4_long"].make()
+    _check(x, k, f"c4 k={k}")
+
+
+def test_c5_reduced():
+    x = gen.WORKLOADS["c5_giant"].make(n=1 << 22)
+    _check(x, 32, "c5-reduced", indices=False)
+    _check(x, 32, "c5-reduced-idx")
+
+
+@pytest.mark.parametrize("name", ["c2_indexer", "c3_sampler"])
+def test_full_size_bench_shapes(name):
+    w = gen.WORKLOADS[name]
+    x = w.make()
+    _check(x, w.ks[0], f"{name}-full")
+
+
+def test_c5_full_size():
+    w = gen.WORKLOADS["c5_giant"]
+    x = w.make()
+    _check(x, 32, "c5-full", indices=False)
+
+
+FAMILIES = ["normal", "ascending", "descending", "constant", "ties", "specials", "tiny", "neg"]
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+@pytest.mark.parametrize("family", FAMILIES)
+def test_edge_families(family, dtype):
+    for n, k in [(1, 1), (7, 3), (513, 512), (3000, 1), (3000, 3000), (20000, 4096), (70001, 777)]:
+        x = gen.rows_family(family, dtype, 5, 3, n)
+        _check(x, k, f"{family}")
+
+
+def test_strided_rows_and_output_modes():
+    x = gen.rows_family("ties", gen.FP32, 9, 4, 9000)
+    _check(x, 100, "strided", pad_to=9004)
+    xb = gen.rows_family("normal", gen.BF16, 9, 4, 9000)
+    _check(xb, 100, "strided-bf16", pad_to=9016)
+    _check(xb, 100, "values-only", indices=False)
+    _check(xb, 100, "indices-only", values=False)
+
+
+def test_fuzz():
+    g = np.random.default_rng(2024)
+    for t in range(60):
+        dtype = gen.BF16 if g.random() < 0.5 else gen.FP32
+        rows = int(g.integers(1, 17))
+        n = int(np.exp(g.uniform(0, np.log(300000))))
+        k = int(g.integers(1, min(4096, n) + 1))
+        fam = FAMILIES[int(g.integers(0, len(FAMILIES)))]
+        x = gen.rows_family(fam, dtype, int(g.integers(0, 1 << 30)), rows, n)
+        cfg = None
+        if g.random() < 0.4:
+            maxs = max(1, n // 2048)
+            cfg = {"slices": int(g.integers(1, min(maxs, 32) + 1))}
+        try:
+            _check(x, k, f"fuzz#{t} {fam}", seed=int(g.integers(0, 1 << 40)), cfg=cfg)
+        except ts.DSError as e:
+            assert e.status == ts.DS_ERR_UNSUPPORTED and cfg is not None, str(e)
+
+
+@pytest.mark.parametrize("dtype,n,k,block,slack,slices", [
+    (gen.BF16, 50000, 100, 1024, 333, 3),
+    (gen.FP32, 129280, 512, 1024, 1024, 1),
+    (gen.BF16, 262144, 512, 1024, 1024, 1),
+    (gen.FP32, 70000, 64, 2048, 100, 4),
+])
+def test_counters_match_model(dtype, n, k, block, slack, slices):
+    """The kernel's A, R, W, max buffer length and read checksums equal the CPU model's under
+    the same Feistel block order, B, B2 and slicing."""
+    x = gen.rows_family("normal", dtype, 17, 2, n)
+    x[1] = gen.rows_family("ascending", dtype, 18, 1, n)[0]
+    cfg = {"block": block, "slack": slack, "slices": slices}
+    seed = 99
+    say(f"[gpu] counters: n={n} k={k} cfg={cfg}")
+    gv, gi, (plan, st) = run_gpu(x, k, seed=seed, cfg=cfg, stats=True)
+    wv, wi = otk.topk(x, k)
+    assert_same(x, k, gv, gi, wv, wi, "counters-run")
+    for r in range(x.shape[0]):
+        slice_len = int(st[r, 0]["slice_len"])
+        _, mst = model.deepselect_row(x[r], k, plan["block"], plan["slack"], "feistel", seed=seed, row_id=r,
+                                      slice_len=slice_len)
+        assert len(mst) == plan["slices"]
+        for s, ms in enumerate(mst):
+            g = st[r, s]
+            lo = s * slice_len
+            ln = min(slice_len, n - lo)
+            assert int(g["slice_lo"]) == lo and int(g["slice_len"]) == ln
+            assert int(g["reads"]) == ln
+            assert int(g["index_sum"]) == ln * lo + ln * (ln - 1) // 2
+            assert int(g["monotone"]) == 1
+            assert (int(g["appended"]), int(g["compactions"]), int(g["work"]), int(g["max_len"])) == \
+                (ms.A, ms.R, ms.W, ms.max_len), (r, s)
+            assert int(g["max_len"]) <= k + plan["slack"] + plan["block"] - 1

@@ -1,0 +1,377 @@
+// C ABI of the DeepSelect top-k library: argument validation, the launch planner, the
+// workspace cache of ds_topk, and dispatch to the HIP kernels. Validation is pure host
+// code and runs before any HIP call, so every error path works without a GPU.
+#include <algorithm>
+#include <mutex>
+#include <unordered_map>
+
+#include "ds_internal.h"
+
+namespace {
+
+using ds::kNumSelectShapes;
+using ds::kSelectShapes;
+
+constexpr int64_t kMaxLdsBytes = 160 * 1024;    // LDS per workgroup on gfx950
+constexpr int64_t kMaxSliceBytes = 0x7FFFFF00;  // buffer offsets are 31-bit
+constexpr int kChunkBf16 = 512, kChunkFp32 = 256;
+constexpr int kMergeBlock = ds::kMergeShape.waves * ds::kMergeShape.cpw * 128;
+
+int elem_bytes(int dtype) { return dtype == DS_BF16 ? 2 : 4; }
+int chunk_elems(int dtype) { return dtype == DS_BF16 ? kChunkBf16 : kChunkFp32; }
+
+int pow2_at_least(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+struct Plan {
+  int dtype;
+  int shape;        // index into kSelectShapes
+  int block;        // B
+  int slack;        // B2
+  int slices;       // S
+  int64_t slice_len;
+  int sort_cap;
+  size_t lds;
+  // merge (slices > 1)
+  int mslack;
+  size_t mlds;
+  size_t ws_bytes;
+};
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -1;
+  cache[dev] = cus;
+  return cus;
+}
+
+int check_basic(int64_t rows, int64_t n, int k, int dtype) {
+  if (dtype != DS_BF16 && dtype != DS_FP32) return DS_ERR_INVALID_ARG;
+  if (rows < 0 || n < 1 || n > INT32_MAX) return DS_ERR_INVALID_ARG;
+  if (k < 1 || k > n) return DS_ERR_INVALID_ARG;
+  if (k > DS_MAX_K) return DS_ERR_UNSUPPORTED;
+  return DS_OK;
+}
+
+// Choose B, B2, slices and the kernel shape; cfg fields that are non-zero are forced.
+// cus is the device's compute-unit count (only used when slices are automatic).
+int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
+  int st = check_basic(rows, n, k, dtype);
+  if (st != DS_OK) return st;
+  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0};
+  if (c.block < 0 || c.slack < 0 || c.slices < 0 || c.waves < 0) return DS_ERR_INVALID_ARG;
+  const int chunk = chunk_elems(dtype);
+  const int eb = elem_bytes(dtype);
+
+  // kernel shape: the forced block/waves, else the default per element type
+  int shape = -1;
+  if (c.block || c.waves) {
+    for (int s = 0; s < kNumSelectShapes; ++s) {
+      const int b = kSelectShapes[s].waves * kSelectShapes[s].cpw * chunk;
+      if (c.block && b != c.block) continue;
+      if (c.waves && kSelectShapes[s].waves != c.waves) continue;
+      if (shape < 0 || (!c.waves && kSelectShapes[s].waves == 4)) shape = s;
+    }
+    if (shape < 0) return DS_ERR_UNSUPPORTED;
+  } else {
+    shape = dtype == DS_BF16 ? 1 : 2;  // bf16: 4 waves x 1 chunk (B=2048); fp32: 4 x 2 (B=2048)
+  }
+  const int block = kSelectShapes[shape].waves * kSelectShapes[shape].cpw * chunk;
+  const int sort_cap = pow2_at_least(k);
+  int slack = c.slack ? c.slack : (k > block ? k : block);
+  if (slack + block < sort_cap) {
+    if (c.slack) return DS_ERR_UNSUPPORTED;  // the final sort runs in the append region
+    slack = sort_cap - block;
+  }
+
+  // slices: enough workgroups to fill the device twice, each slice at least 4 blocks and 8k
+  int64_t slices;
+  if (c.slices) {
+    slices = c.slices;
+  } else {
+    const int64_t want = cus > 0 ? (2 * static_cast<int64_t>(cus) + (rows > 0 ? rows : 1) - 1) / (rows > 0 ? rows : 1) : 1;
+    const int64_t min_len = std::max<int64_t>(4 * static_cast<int64_t>(block), 8 * static_cast<int64_t>(k));
+    const int64_t most = std::max<int64_t>(1, n / min_len);
+    slices = std::max<int64_t>(1, std::min(want, most));
+  }
+  const int64_t min_slices = (n * eb + kMaxSliceBytes - 1) / kMaxSliceBytes;
+  if (slices < min_slices) {
+    if (c.slices) return DS_ERR_UNSUPPORTED;
+    slices = min_slices;
+  }
+  int64_t per = (n + slices - 1) / slices;
+  int64_t slice_len = (per + block - 1) / block * block;
+  if (slice_len * eb > kMaxSliceBytes) slice_len = kMaxSliceBytes / eb / block * block;
+  slices = (n + slice_len - 1) / slice_len;
+  if (c.slices && slices != c.slices) return DS_ERR_UNSUPPORTED;  // forced count leaves an empty slice
+  if (rows * slices > INT32_MAX) return DS_ERR_UNSUPPORTED;
+
+  const size_t lds = ds::select_lds_bytes(k, block, slack, kSelectShapes[shape].waves);
+  if (static_cast<int64_t>(lds) > kMaxLdsBytes) return DS_ERR_UNSUPPORTED;
+
+  Plan p{};
+  p.dtype = dtype;
+  p.shape = shape;
+  p.block = block;
+  p.slack = slack;
+  p.slices = static_cast<int>(slices);
+  p.slice_len = slice_len;
+  p.sort_cap = sort_cap;
+  p.lds = lds;
+  if (slices > 1) {
+    int ms = k > kMergeBlock ? k : kMergeBlock;
+    if (ms + kMergeBlock < sort_cap) ms = sort_cap - kMergeBlock;
+    p.mslack = ms;
+    p.mlds = ds::select_lds_bytes(k, kMergeBlock, ms, ds::kMergeShape.waves);
+    if (static_cast<int64_t>(p.mlds) > kMaxLdsBytes) return DS_ERR_UNSUPPORTED;
+    const int64_t entries = slices * static_cast<int64_t>(k);
+    if (entries * 8 > kMaxSliceBytes) return DS_ERR_UNSUPPORTED;
+    p.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>(entries) * 8;
+  }
+  *out = p;
+  return DS_OK;
+}
+
+int check_call(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, const void* out_vals,
+               const int32_t* out_idx) {
+  int st = check_basic(rows, n, k, dtype);
+  if (st != DS_OK) return st;
+  if (row_stride < n) return DS_ERR_INVALID_ARG;
+  if (rows == 0) return DS_OK;
+  if (!x || (!out_vals && !out_idx)) return DS_ERR_INVALID_ARG;
+  const int eb = elem_bytes(dtype);
+  if (row_stride > (INT64_MAX / eb) / (rows > 0 ? rows : 1)) return DS_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || ((row_stride * eb) & 15) != 0) return DS_ERR_ALIGNMENT;
+  return DS_OK;
+}
+
+int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, uint64_t seed,
+               void* out_vals, int32_t* out_idx, void* ws, ds_stats* stats, hipStream_t stream) {
+  (void)hipGetLastError();  // clear a stale error so a launch failure is reported as ours
+  ds::SelectParams sp{};
+  sp.x = static_cast<const uint8_t*>(x);
+  sp.row_stride_bytes = row_stride * elem_bytes(pl.dtype);
+  sp.n = n;
+  sp.slice_len = pl.slice_len;
+  sp.slices = pl.slices;
+  sp.k = k;
+  sp.slack = pl.slack;
+  sp.sort_cap = pl.sort_cap;
+  sp.seed = seed;
+  sp.ws = static_cast<uint2*>(ws);
+  sp.out_vals = out_vals;
+  sp.out_idx = out_idx;
+  sp.stats = stats;
+  return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
+}
+
+int run_merge(const Plan& pl, int64_t rows, int k, uint64_t seed, void* out_vals, int32_t* out_idx, void* ws,
+              hipStream_t stream) {
+  if (pl.slices <= 1) return DS_OK;
+  (void)hipGetLastError();
+  ds::MergeParams mp{};
+  mp.ws = static_cast<const uint2*>(ws);
+  mp.entries = static_cast<int64_t>(pl.slices) * k;
+  mp.k = k;
+  mp.slack = pl.mslack;
+  mp.sort_cap = pl.sort_cap;
+  mp.seed = seed;
+  mp.out_vals = out_vals;
+  mp.out_idx = out_idx;
+  return ds::launch_merge(pl.dtype, mp, rows, pl.mlds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
+}
+
+int run(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, uint64_t seed,
+        void* out_vals, int32_t* out_idx, void* ws, ds_stats* stats, hipStream_t stream) {
+  int st = run_select(pl, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, stats, stream);
+  if (st != DS_OK) return st;
+  return run_merge(pl, rows, k, seed, out_vals, out_idx, ws, stream);
+}
+
+// Plan a call that brings its own workspace; validates the workspace against the plan.
+int plan_with_workspace(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, void* workspace,
+                        size_t ws_bytes, Plan* p) {
+  int cus = 0;
+  if (!(cfg && cfg->slices)) {
+    cus = device_cu_count();
+    if (cus <= 0) return DS_ERR_DEVICE;
+  }
+  int st = make_plan(rows, n, k, dtype, cfg, cus, p);
+  if (st != DS_OK) return st;
+  if (p->ws_bytes) {
+    if (!workspace || ws_bytes < p->ws_bytes) return DS_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return DS_ERR_ALIGNMENT;
+  }
+  return DS_OK;
+}
+
+// Per-device workspace cache for ds_topk: grows on demand, freed at unload.
+struct WsCache {
+  std::mutex mu;
+  std::unordered_map<int, std::pair<void*, size_t>> bufs;
+  ~WsCache() {
+    for (auto& kv : bufs) {
+      if (kv.second.first) {
+        int old = 0;
+        if (hipGetDevice(&old) == hipSuccess && hipSetDevice(kv.first) == hipSuccess) {
+          (void)hipFree(kv.second.first);
+          (void)hipSetDevice(old);
+        }
+      }
+    }
+  }
+};
+WsCache& ws_cache() {
+  static WsCache c;
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ds_status_string(int status) {
+  switch (status) {
+    case DS_OK: return "DS_OK";
+    case DS_ERR_INVALID_ARG: return "DS_ERR_INVALID_ARG";
+    case DS_ERR_UNSUPPORTED: return "DS_ERR_UNSUPPORTED";
+    case DS_ERR_ALIGNMENT: return "DS_ERR_ALIGNMENT";
+    case DS_ERR_WORKSPACE: return "DS_ERR_WORKSPACE";
+    case DS_ERR_LAUNCH: return "DS_ERR_LAUNCH";
+    case DS_ERR_DEVICE: return "DS_ERR_DEVICE";
+    default: return "DS_ERR_UNKNOWN";
+  }
+}
+
+int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, ds_config* out) {
+  if (!out) return DS_ERR_INVALID_ARG;
+  int st = check_basic(rows, n, k, dtype);
+  if (st != DS_OK) return st;
+  int cus = 0;
+  if (!(cfg && cfg->slices)) {
+    cus = device_cu_count();
+    if (cus <= 0) return DS_ERR_DEVICE;
+  }
+  Plan p;
+  st = make_plan(rows, n, k, dtype, cfg, cus, &p);
+  if (st != DS_OK) return st;
+  out->block = p.block;
+  out->slack = p.slack;
+  out->slices = p.slices;
+  out->waves = kSelectShapes[p.shape].waves;
+  return DS_OK;
+}
+
+int ds_topk_workspace_size(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, size_t* bytes) {
+  if (!bytes) return DS_ERR_INVALID_ARG;
+  int st = check_basic(rows, n, k, dtype);
+  if (st != DS_OK) return st;
+  int cus = 0;
+  if (!(cfg && cfg->slices)) {
+    cus = device_cu_count();
+    if (cus <= 0) return DS_ERR_DEVICE;
+  }
+  Plan p;
+  st = make_plan(rows, n, k, dtype, cfg, cus, &p);
+  if (st != DS_OK) return st;
+  *bytes = p.ws_bytes;
+  return DS_OK;
+}
+
+int ds_topk_ex(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
+               void* out_vals, int32_t* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
+               ds_stats* stats, void* stream) {
+  int st = check_call(x, rows, n, row_stride, k, dtype, out_vals, out_idx);
+  if (st != DS_OK || rows == 0) return st;
+  Plan p;
+  st = plan_with_workspace(rows, n, k, dtype, cfg, workspace, ws_bytes, &p);
+  if (st != DS_OK) return st;
+  return run(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, workspace, stats,
+             static_cast<hipStream_t>(stream));
+}
+
+int ds_topk_slices(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
+                   void* out_vals, int32_t* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
+                   ds_stats* stats, void* stream) {
+  int st = check_call(x, rows, n, row_stride, k, dtype, out_vals, out_idx);
+  if (st != DS_OK || rows == 0) return st;
+  Plan p;
+  st = plan_with_workspace(rows, n, k, dtype, cfg, workspace, ws_bytes, &p);
+  if (st != DS_OK) return st;
+  return run_select(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, workspace, stats,
+                    static_cast<hipStream_t>(stream));
+}
+
+int ds_topk_merge(int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void* out_vals, int32_t* out_idx,
+                  void* workspace, size_t ws_bytes, const ds_config* cfg, void* stream) {
+  int st = check_basic(rows, n, k, dtype);
+  if (st != DS_OK || rows == 0) return st;
+  if (!out_vals && !out_idx) return DS_ERR_INVALID_ARG;
+  Plan p;
+  st = plan_with_workspace(rows, n, k, dtype, cfg, workspace, ws_bytes, &p);
+  if (st != DS_OK) return st;
+  return run_merge(p, rows, k, seed, out_vals, out_idx, workspace, static_cast<hipStream_t>(stream));
+}
+
+int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
+            void* out_vals, int32_t* out_idx, void* stream) {
+  int st = check_call(x, rows, n, row_stride, k, dtype, out_vals, out_idx);
+  if (st != DS_OK || rows == 0) return st;
+  const int cus = device_cu_count();
+  if (cus <= 0) return DS_ERR_DEVICE;
+  Plan p;
+  st = make_plan(rows, n, k, dtype, nullptr, cus, &p);
+  if (st != DS_OK) return st;
+  void* ws = nullptr;
+  if (p.ws_bytes) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_DEVICE;
+    WsCache& c = ws_cache();
+    std::lock_guard<std::mutex> g(c.mu);
+    auto& slot = c.bufs[dev];
+    if (slot.second < p.ws_bytes) {
+      if (slot.first) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(slot.first);
+        slot = {nullptr, 0};
+      }
+      void* ptr = nullptr;
+      if (hipMalloc(&ptr, p.ws_bytes) != hipSuccess) return DS_ERR_LAUNCH;
+      slot = {ptr, p.ws_bytes};
+    }
+    ws = slot.first;
+    return run(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, nullptr, static_cast<hipStream_t>(stream));
+  }
+  return run(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int64_t ds_probe_sink_words(int64_t bytes) { return bytes <= 0 ? 0 : ds::probe_read_groups(bytes); }
+
+int ds_probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes <= 0 || (bytes & 15) != 0) return DS_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) != 0) return DS_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return ds::launch_probe_read(src, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess ? DS_OK
+                                                                                                  : DS_ERR_LAUNCH;
+}
+
+int ds_probe_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (!src || !dst || bytes <= 0 || (bytes & 15) != 0) return DS_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (reinterpret_cast<uintptr_t>(dst) & 15) != 0)
+    return DS_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return ds::launch_probe_copy(dst, src, bytes, static_cast<hipStream_t>(stream)) == hipSuccess ? DS_OK
+                                                                                                  : DS_ERR_LAUNCH;
+}
+
+}  // extern "C"

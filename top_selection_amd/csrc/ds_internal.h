@@ -1,0 +1,66 @@
+// Internal interface between the C-ABI layer (ds_api.cpp) and the HIP kernels
+// (ds_kernels.hip). Not installed; the public interface is include/dstopk.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dstopk.h"
+
+namespace ds {
+
+// One workgroup runs DeepSelect over one slice [slice*slice_len, min(n, (slice+1)*slice_len))
+// of one row. Candidates live in LDS as (key, index) pairs.
+struct SelectParams {
+  const uint8_t* x;          // row 0, slice 0
+  int64_t row_stride_bytes;  // bytes between rows
+  int64_t n;                 // elements per row
+  int64_t slice_len;         // elements per slice, a multiple of the block size
+  int32_t slices;            // workgroups per row
+  int32_t k;
+  int32_t slack;             // B2
+  int32_t sort_cap;          // power of two >= k (final sort width)
+  uint64_t seed;
+  uint2* ws;                 // slices > 1: survivors [rows][slices][k] as (key, index)
+  void* out_vals;            // slices == 1: sorted output values [rows][k]
+  int32_t* out_idx;          // slices == 1: sorted output indices [rows][k]
+  ds_stats* stats;           // NULL or [rows][slices]
+};
+
+// One workgroup per row runs DeepSelect over the row's slices*k survivors.
+struct MergeParams {
+  const uint2* ws;     // [rows][entries] (key, index)
+  int64_t entries;     // slices * k
+  int32_t k;
+  int32_t slack;
+  int32_t sort_cap;
+  uint64_t seed;
+  void* out_vals;
+  int32_t* out_idx;
+};
+
+// A compiled kernel shape: waves per workgroup and 16-byte chunks per wave per block.
+struct Shape {
+  int waves;
+  int cpw;
+};
+
+// Select-kernel shapes built for each element type. The block size is
+// waves * cpw * 64 lanes * (16 / elem_bytes) elements.
+constexpr Shape kSelectShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}, {8, 2}, {4, 4}, {8, 4}};
+constexpr int kNumSelectShapes = sizeof(kSelectShapes) / sizeof(kSelectShapes[0]);
+constexpr Shape kMergeShape = {4, 4};  // 4 waves x 4 chunks x 128 entries = 2048 entries per block
+
+// LDS bytes a select/merge workgroup needs.
+size_t select_lds_bytes(int k, int block, int slack, int waves);
+
+// Launchers; return hipSuccess or the launch error.
+hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,
+                         hipStream_t stream);
+hipError_t launch_merge(int dtype, const MergeParams& p, int64_t rows, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+int64_t probe_read_groups(int64_t bytes);
+hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
+}  // namespace ds
