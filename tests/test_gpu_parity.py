@@ -131,7 +131,8 @@ def test_counters_match_model(dtype, n, k, block, slack, slices):
     wv, wi = otk.topk(x, k)
     assert_same(x, k, gv, gi, wv, wi, "counters-run")
     for r in range(x.shape[0]):
-        slice_len = int(st[r, 0]["slice_len"])
+        per = -(-n // plan["slices"])
+        slice_len = -(-per // plan["block"]) * plan["block"]  # the planner's slice length
         _, mst = model.deepselect_row(x[r], k, plan["block"], plan["slack"], "feistel", seed=seed, row_id=r,
                                       slice_len=slice_len)
         assert len(mst) == plan["slices"]

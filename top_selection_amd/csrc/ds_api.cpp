@@ -136,7 +136,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
     if (static_cast<int64_t>(p.mlds) > kMaxLdsBytes) return DS_ERR_UNSUPPORTED;
     const int64_t entries = slices * static_cast<int64_t>(k);
     if (entries * 8 > kMaxSliceBytes) return DS_ERR_UNSUPPORTED;
-    p.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>(entries) * 8;
+    p.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>((entries + 1) & ~int64_t(1)) * 8;
   }
   *out = p;
   return DS_OK;
@@ -169,6 +169,7 @@ int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t r
   sp.sort_cap = pl.sort_cap;
   sp.seed = seed;
   sp.ws = static_cast<uint2*>(ws);
+  sp.ws_row_entries = (static_cast<int64_t>(pl.slices) * k + 1) & ~int64_t(1);
   sp.out_vals = out_vals;
   sp.out_idx = out_idx;
   sp.stats = stats;
@@ -182,6 +183,7 @@ int run_merge(const Plan& pl, int64_t rows, int k, uint64_t seed, void* out_vals
   ds::MergeParams mp{};
   mp.ws = static_cast<const uint2*>(ws);
   mp.entries = static_cast<int64_t>(pl.slices) * k;
+  mp.row_entries = (mp.entries + 1) & ~int64_t(1);
   mp.k = k;
   mp.slack = pl.mslack;
   mp.sort_cap = pl.sort_cap;

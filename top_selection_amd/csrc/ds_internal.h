@@ -22,7 +22,8 @@ struct SelectParams {
   int32_t slack;             // B2
   int32_t sort_cap;          // power of two >= k (final sort width)
   uint64_t seed;
-  uint2* ws;                 // slices > 1: survivors [rows][slices][k] as (key, index)
+  uint2* ws;                 // slices > 1: survivors, row r at ws + r*ws_row_entries, slice s at +s*k
+  int64_t ws_row_entries;    // slices*k rounded up to even (16-byte rows)
   void* out_vals;            // slices == 1: sorted output values [rows][k]
   int32_t* out_idx;          // slices == 1: sorted output indices [rows][k]
   ds_stats* stats;           // NULL or [rows][slices]
@@ -30,8 +31,9 @@ struct SelectParams {
 
 // One workgroup per row runs DeepSelect over the row's slices*k survivors.
 struct MergeParams {
-  const uint2* ws;     // [rows][entries] (key, index)
+  const uint2* ws;     // row r's entries at ws + r*row_entries
   int64_t entries;     // slices * k
+  int64_t row_entries; // entries rounded up to even
   int32_t k;
   int32_t slack;
   int32_t sort_cap;

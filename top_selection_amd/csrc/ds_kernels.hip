@@ -59,20 +59,67 @@ __device__ __forceinline__ uint32_t popc(uint64_t m) { return static_cast<uint32
 
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ __forceinline__ uint32_t shfl(uint32_t v, uint32_t src_lane) {
-  return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(static_cast<int>(src_lane << 2), static_cast<int>(v)));
+// Value held by lane (lane ^ m), m a power of two below 64. Lane mappings (checked on
+// gfx950): quad_perm 0xB1 / 0x4E swap neighbours at distance 1 / 2, row_ror:8 swaps the
+// halves of a 16-lane row, ds_swizzle in bit-mask mode xors the lane id within 32 lanes,
+// and the permlane16/32 swaps exchange 16-lane rows / 32-lane halves.
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, uint32_t m, uint32_t lane) {
+  switch (m) {
+    case 1: return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);
+    case 4: return __builtin_amdgcn_ds_swizzle(v, 0x1F | (4 << 10));
+    case 8: return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xF, 0xF, false);
+    case 16: {
+      const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (lane & 16u) ? p[0] : p[1];
+    }
+    default: {
+      const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (lane & 32u) ? p[0] : p[1];
+    }
+  }
 }
 
-__device__ __forceinline__ uint32_t wave_or(uint32_t v, uint32_t lane) {
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, uint32_t m, uint32_t lane) {
+  const uint32_t lo = xor_lane(static_cast<uint32_t>(v), m, lane);
+  const uint32_t hi = xor_lane(static_cast<uint32_t>(v >> 32), m, lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v, uint32_t lane) {
 #pragma unroll
-  for (uint32_t o = 32; o > 0; o >>= 1) v |= shfl(v, lane ^ o);
+  for (uint32_t m = 1; m < 64; m <<= 1) {
+    const uint64_t o = xor_lane64(v, m, lane);
+    v = o > v ? o : v;
+  }
   return v;
 }
 
-__device__ __forceinline__ uint32_t wave_and(uint32_t v, uint32_t lane) {
+__device__ __forceinline__ uint64_t wave_min64(uint64_t v, uint32_t lane) {
 #pragma unroll
-  for (uint32_t o = 32; o > 0; o >>= 1) v &= shfl(v, lane ^ o);
+  for (uint32_t m = 1; m < 64; m <<= 1) {
+    const uint64_t o = xor_lane64(v, m, lane);
+    v = o < v ? o : v;
+  }
   return v;
+}
+
+// Inclusive prefix sum over the 64 lanes (row shifts within 16-lane rows, then the row
+// broadcasts of lanes 15 and 31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, uint32_t l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), l);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // --------------------------------------------------------------------------- keys
@@ -153,14 +200,18 @@ struct BlockOrder {
 
 // --------------------------------------------------------------------------- shared state
 constexpr int kMaxWaves = 16;
+constexpr uint32_t kBins = 512;      // histogram bins of one radix pass
+constexpr uint32_t kListCap = 64;    // pivot-bin entries resolved by one wave
 
 struct Scalars {
-  uint32_t app_count;              // entries appended since the last compaction
-  uint32_t outpos;                 // scatter cursor of the running compaction
-  uint32_t slot[2][kMaxWaves];     // per-wave end of its reservation, by block parity
-  uint32_t red[kMaxWaves][4];      // OR/AND reductions of the compaction
-  uint32_t mred[kMaxWaves][2];     // min-composite reduction of the compaction
-  unsigned long long reads;        // counters (stats runs only)
+  uint32_t app_count;               // entries appended since the last compaction
+  uint32_t outpos;                  // scatter cursor of the running compaction
+  uint32_t listpos;                 // pivot-list cursor of the running compaction
+  uint32_t pad0;
+  uint32_t slot[2][kMaxWaves];      // per-wave end of its reservation, by block parity
+  uint64_t red[kMaxWaves][2];       // per-wave min / max composites
+  uint2 list[kListCap];             // entries of the pivot bin
+  unsigned long long reads;         // counters (stats runs only)
   unsigned long long index_sum;
 };
 
@@ -168,252 +219,354 @@ struct Thr {
   uint32_t key, idx;
 };
 
-// Every wave scans the same 256-bin histogram (bins in descending digit order) and finds the
-// bin holding the `need`-th best entry: `above` entries lie in higher bins, `cnt` in it.
+__device__ __forceinline__ uint64_t comp_of(uint2 e) {
+  return (static_cast<uint64_t>(e.x) << 32) | static_cast<uint32_t>(~e.y);
+}
+
+__device__ __forceinline__ uint2 entry_of(uint64_t c) {
+  return make_uint2(static_cast<uint32_t>(c >> 32), ~static_cast<uint32_t>(c));
+}
+
+__device__ __forceinline__ uint32_t bitlen64(uint64_t v) { return v ? 64u - static_cast<uint32_t>(__builtin_clzll(v)) : 0u; }
+
+// Every wave scans the same kBins-bin histogram from the top bin down and finds the bin that
+// holds the `need`-th best entry: `above` entries lie in higher bins, `cnt` in that bin.
 __device__ __forceinline__ void scan_select(const uint32_t* h, uint32_t need, uint32_t lane, uint32_t& bin,
                                             uint32_t& above, uint32_t& cnt) {
-  const uint32_t top = 255u - 4u * lane;  // this lane holds bins top, top-1, top-2, top-3
-  const uint4 q = *reinterpret_cast<const uint4*>(h + top - 3);
-  const uint32_t c0 = q.w, c1 = q.z, c2 = q.y, c3 = q.x;
-  const uint32_t s = c0 + c1 + c2 + c3;
-  uint32_t incl = s;
+  constexpr uint32_t PER = kBins / 64;  // 8 bins per lane, lane 0 holds the highest
+  const uint32_t top = kBins - 1u - PER * lane;
+  const uint4 qa = *reinterpret_cast<const uint4*>(h + top - 7);
+  const uint4 qb = *reinterpret_cast<const uint4*>(h + top - 3);
+  const uint32_t c[PER] = {qb.w, qb.z, qb.y, qb.x, qa.w, qa.z, qa.y, qa.x};  // bins top, top-1, ...
+  uint32_t s = 0;
 #pragma unroll
-  for (uint32_t d = 1; d < 64; d <<= 1) {
-    const uint32_t t = shfl(incl, lane >= d ? lane - d : lane);
-    if (lane >= d) incl += t;
-  }
+  for (uint32_t i = 0; i < PER; ++i) s += c[i];
+  const uint32_t incl = wave_incl_scan(s);
   const uint64_t ge = ballot(incl >= need);
   const uint32_t src = ge ? static_cast<uint32_t>(__builtin_ctzll(ge)) : 63u;
-  const uint32_t excl = incl - s;
-  uint32_t b, a, c;
-  if (excl + c0 >= need) {
-    b = top; a = excl; c = c0;
-  } else if (excl + c0 + c1 >= need) {
-    b = top - 1; a = excl + c0; c = c1;
-  } else if (excl + c0 + c1 + c2 >= need) {
-    b = top - 2; a = excl + c0 + c1; c = c2;
-  } else {
-    b = top - 3; a = excl + c0 + c1 + c2; c = c3;
+  uint32_t acc = incl - s, b = top - (PER - 1), a = acc, n = c[PER - 1];
+  bool found = false;
+#pragma unroll
+  for (uint32_t i = 0; i < PER; ++i) {
+    if (!found && acc + c[i] >= need) {
+      found = true;
+      b = top - i;
+      a = acc;
+      n = c[i];
+    }
+    acc += c[i];
   }
   bin = __builtin_amdgcn_readlane(b, src);
   above = __builtin_amdgcn_readlane(a, src);
-  cnt = __builtin_amdgcn_readlane(c, src);
+  cnt = __builtin_amdgcn_readlane(n, src);
 }
 
-// Radix-select compaction: reduce the nsurv survivors in `sin` plus the napp appended entries
-// in `app` to the k best under the composite order, written (unordered) to `sout`, and
-// return the smallest of them (the new threshold). When the input holds at most k entries
-// everything is kept and `sout` is padded with sentinels up to k. RAW: appended entries hold
-// raw element bits (bf16: in the high half) and are turned into keys here.
+// Radix-select compaction.
+//
+// Reduces the nsurv survivors in `sin` plus the napp appended entries in `app` to the k best
+// under the composite order and writes them (unordered) to `sout`. Returns the smallest kept
+// composite (the new threshold) in `thr` and the largest in `maxc`.
+//
+// The search runs on the 64-bit composite c = (key << 32) | ~index over a window
+// [lo, hi] that holds every entry: a kBins-bin histogram of (c - lo) >> shift (entries
+// above hi fall in the top bin) locates the bin of the k-th best; while that bin holds more
+// than kListCap entries the window shrinks to it and the histogram repeats; then the
+// entries above the bin are scattered to `sout`, the bin's entries are gathered in a short
+// list, and every wave ranks that list to pick the rest and the threshold.
+// First call (nsurv == 0): one extra pass turns the raw entries into keys and measures the
+// window. Later calls: the window is [previous threshold, previous maximum] and the raw ->
+// key step is folded into the first histogram pass.
+// RAW: appended entries hold raw element bits (bf16: in the high half).
 template <int DT, int WAVES, bool RAW>
-__device__ Thr compact(const uint2* sin, uint32_t nsurv, uint2* app, uint32_t napp, uint2* sout, uint32_t k,
-                       Scalars& sc, uint32_t* hist3, uint32_t& hctr) {
+__device__ void compact(const uint2* sin, uint32_t nsurv, uint2* app, uint32_t napp, uint2* sout, uint32_t k,
+                        Scalars& sc, uint32_t* hist3, uint32_t& hctr, uint64_t& thr, uint64_t& maxc) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t n = nsurv + napp;
 
-  // 1. keys for the new entries; OR / AND of keys and of inverted indices over the buffer
-  uint32_t ok = 0, ak = ~0u, oi = 0, ai = ~0u;
-  for (uint32_t i = tid; i < n; i += NT) {
-    uint2 e;
-    if (i < nsurv) {
-      e = sin[i];
-    } else {
-      e = app[i - nsurv];
+  if (n <= k) {  // keep everything (only the final call can get here)
+    for (uint32_t i = tid; i < k; i += NT) {
+      uint2 e = make_uint2(0, kSentinelIdx);
+      if (i < nsurv) {
+        e = sin[i];
+      } else if (i < n) {
+        e = app[i - nsurv];
+        if constexpr (RAW) e.x = key_of_raw<DT>(DT == DS_BF16 ? (e.x >> 16) : e.x);
+      }
+      sout[i] = e;
+    }
+    lds_sync();
+    return;
+  }
+
+  uint64_t lo, hi;
+  bool raw_pending = RAW;
+  if (nsurv == 0) {
+    uint64_t mn = ~0ull, mx = 0;
+    for (uint32_t i = tid; i < n; i += NT) {
+      uint2 e = app[i];
       if constexpr (RAW) {
         e.x = key_of_raw<DT>(DT == DS_BF16 ? (e.x >> 16) : e.x);
-        app[i - nsurv].x = e.x;
+        app[i].x = e.x;
       }
+      const uint64_t c = comp_of(e);
+      mn = c < mn ? c : mn;
+      mx = c > mx ? c : mx;
     }
-    ok |= e.x;
-    ak &= e.x;
-    oi |= ~e.y;
-    ai &= ~e.y;
-  }
-  ok = wave_or(ok, lane);
-  ak = wave_and(ak, lane);
-  oi = wave_or(oi, lane);
-  ai = wave_and(ai, lane);
-  if (lane == 0) {
-    sc.red[wave][0] = ok;
-    sc.red[wave][1] = ak;
-    sc.red[wave][2] = oi;
-    sc.red[wave][3] = ai;
-  }
-  if (tid == 0) {
-    sc.outpos = 0;
-    sc.app_count = 0;
-  }
-  lds_sync();
-  ok = 0;
-  ak = ~0u;
-  oi = 0;
-  ai = ~0u;
+    mn = wave_min64(mn, lane);
+    mx = wave_max64(mx, lane);
+    if (lane == 0) {
+      sc.red[wave][0] = mn;
+      sc.red[wave][1] = mx;
+    }
+    if (tid == 0) {
+      sc.app_count = 0;
+      sc.outpos = 0;
+      sc.listpos = 0;
+    }
+    lds_sync();
+    lo = ~0ull;
+    hi = 0;
 #pragma unroll
-  for (int w = 0; w < WAVES; ++w) {
-    ok |= sc.red[w][0];
-    ak &= sc.red[w][1];
-    oi |= sc.red[w][2];
-    ai &= sc.red[w][3];
-  }
-
-  // 2. radix select of the k-th best composite: first over key bits, then over ~index bits
-  const bool all = n <= k;
-  uint32_t need = k, pk = 0, pi = 0;
-  if (!all) {
-    bool done = false;
-    const uint32_t dk = ok ^ ak;
-    if (dk == 0) {
-      pk = ak;  // every key equal: only the index decides
-    } else {
-      int hb = 31 - __builtin_clz(dk);
-      uint32_t mk = hb == 31 ? 0u : (~0u << (hb + 1));
-      pk = ak & mk;
-      int lo = hb > 7 ? hb - 7 : 0;
-      for (;;) {
-        const uint32_t dmask = (1u << (hb - lo + 1)) - 1u;
-        uint32_t* h = hist3 + 256u * (hctr % 3u);
-        uint32_t* hn = hist3 + 256u * ((hctr + 1u) % 3u);
-        for (uint32_t b = tid; b < 256u; b += NT) hn[b] = 0;
-        for (uint32_t i = tid; i < n; i += NT) {
-          const uint32_t key = (i < nsurv ? sin[i] : app[i - nsurv]).x;
-          if ((key & mk) == pk) atomicAdd(&h[(key >> lo) & dmask], 1u);
-        }
-        lds_sync();
-        ++hctr;
-        uint32_t bin, above, cnt;
-        scan_select(h, need, lane, bin, above, cnt);
-        need -= above;
-        pk |= bin << lo;
-        mk |= dmask << lo;
-        if (cnt == need) {
-          done = true;
-          break;
-        }
-        if (lo == 0) break;
-        hb = lo - 1;
-        lo = hb > 7 ? hb - 7 : 0;
-      }
+    for (int w = 0; w < WAVES; ++w) {
+      lo = sc.red[w][0] < lo ? sc.red[w][0] : lo;
+      hi = sc.red[w][1] > hi ? sc.red[w][1] : hi;
     }
-    if (!done) {
-      // `need` more entries among those whose key equals pk: the smallest indices win
-      const uint32_t di = oi ^ ai;
-      int hb = di ? 31 - __builtin_clz(di) : 0;
-      uint32_t mi = hb == 31 ? 0u : (~0u << (hb + 1));
-      pi = ai & mi;
-      int lo = hb > 7 ? hb - 7 : 0;
-      for (;;) {
-        const uint32_t dmask = (1u << (hb - lo + 1)) - 1u;
-        uint32_t* h = hist3 + 256u * (hctr % 3u);
-        uint32_t* hn = hist3 + 256u * ((hctr + 1u) % 3u);
-        for (uint32_t b = tid; b < 256u; b += NT) hn[b] = 0;
-        for (uint32_t i = tid; i < n; i += NT) {
-          const uint2 e = i < nsurv ? sin[i] : app[i - nsurv];
-          const uint32_t ni = ~e.y;
-          if (e.x == pk && (ni & mi) == pi) atomicAdd(&h[(ni >> lo) & dmask], 1u);
-        }
-        lds_sync();
-        ++hctr;
-        uint32_t bin, above, cnt;
-        scan_select(h, need, lane, bin, above, cnt);
-        need -= above;
-        pi |= bin << lo;
-        mi |= dmask << lo;
-        if (cnt == need || lo == 0) break;
-        hb = lo - 1;
-        lo = hb > 7 ? hb - 7 : 0;
-      }
+    raw_pending = false;
+  } else {
+    lo = thr;
+    hi = maxc;
+    if (tid == 0) {  // every wave passed the block barrier after its appends
+      sc.app_count = 0;
+      sc.outpos = 0;
+      sc.listpos = 0;
     }
   }
 
-  // 3. scatter the selected entries (composite >= (pk, pi)) and find the smallest of them
-  uint32_t min_key = ~0u, min_ni = ~0u;
+  // histogram passes, shrinking [lo, hi] to the bin of the k-th best
+  uint32_t need = k, above_total = 0, cnt = 0;
+  uint64_t plo = lo, phi = hi;  // current pivot window
+  bool top_open = nsurv != 0;   // entries above hi may exist (they fall in the top bin)
+  uint64_t seen_max = 0;
+  for (;;) {
+    const uint32_t shift = bitlen64(phi - plo) > 9 ? bitlen64(phi - plo) - 9 : 0;
+    uint32_t* h = hist3 + kBins * (hctr % 3u);
+    uint32_t* hn = hist3 + kBins * ((hctr + 1u) % 3u);
+    for (uint32_t b = tid; b < kBins; b += NT) hn[b] = 0;
+    uint64_t mx = 0;
+    for (uint32_t i = tid; i < n; i += NT) {
+      uint2 e;
+      if (i < nsurv) {
+        e = sin[i];
+      } else {
+        e = app[i - nsurv];
+        if (raw_pending) {
+          e.x = key_of_raw<DT>(DT == DS_BF16 ? (e.x >> 16) : e.x);
+          app[i - nsurv].x = e.x;
+        }
+      }
+      const uint64_t c = comp_of(e);
+      mx = c > mx ? c : mx;
+      if (c >= plo && (c <= phi || top_open)) {
+        const uint64_t d = (c > phi ? phi : c) - plo;
+        atomicAdd(&h[static_cast<uint32_t>(d >> shift)], 1u);
+      }
+    }
+    raw_pending = false;
+    mx = wave_max64(mx, lane);
+    if (lane == 0) sc.red[wave][1] = mx;
+    lds_sync();
+    ++hctr;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) seen_max = sc.red[w][1] > seen_max ? sc.red[w][1] : seen_max;
+    uint32_t bin, above;
+    scan_select(h, need, lane, bin, above, cnt);
+    need -= above;
+    above_total += above;
+    const uint64_t nlo = plo + (static_cast<uint64_t>(bin) << shift);
+    const bool open_bin = top_open && (bin == kBins - 1u || ((phi - plo) >> shift) == bin);
+    uint64_t nhi = plo + ((static_cast<uint64_t>(bin) + 1u) << shift) - 1u;
+    if (nhi > phi || nhi < nlo) nhi = phi;
+    plo = nlo;
+    phi = open_bin ? seen_max : nhi;
+    top_open = false;
+    // A chosen open bin widens the window to the true maximum, so it is refined again even
+    // when this pass had single-composite bins.
+    if (cnt <= kListCap || (shift == 0 && !open_bin)) break;
+  }
+
+  // scatter: everything above the pivot window is kept; the window's entries go to the list
+  // (cnt > kListCap only if composites repeat, which real entries never do; the list then
+  // keeps its first kListCap entries and the call still ends)
+  cnt = cnt < kListCap ? cnt : kListCap;
   const uint32_t iters = (n + NT - 1) / NT;
   for (uint32_t it = 0; it < iters; ++it) {
     const uint32_t i = it * NT + tid;
-    bool sel = false;
-    uint2 e = make_uint2(0, 0);
+    uint2 e = make_uint2(0, kSentinelIdx);
+    uint64_t c = 0;
     if (i < n) {
       e = i < nsurv ? sin[i] : app[i - nsurv];
-      sel = all || e.x > pk || (e.x == pk && ~e.y >= pi);
+      c = comp_of(e);
     }
-    const uint64_t bm = ballot(sel);
-    if (bm) {
-      uint32_t b0 = 0;
-      if (lane == 0) b0 = atomicAdd(&sc.outpos, popc(bm));
+    const bool up = i < n && c > phi;
+    const bool mid = i < n && c >= plo && c <= phi;
+    const uint64_t bu = ballot(up), bm = ballot(mid);
+    if (bu | bm) {
+      uint32_t b0 = 0, b1 = 0;
+      if (lane == 0) {
+        if (bu) b0 = atomicAdd(&sc.outpos, popc(bu));
+        if (bm) b1 = atomicAdd(&sc.listpos, popc(bm));
+      }
       b0 = uni(b0);
-      if (sel) {
-        sout[mbcnt(bm, b0)] = e;
-        if (e.x < min_key || (e.x == min_key && ~e.y < min_ni)) {
-          min_key = e.x;
-          min_ni = ~e.y;
-        }
+      b1 = uni(b1);
+      if (up) {
+        const uint32_t q = mbcnt(bu, b0);
+        if (q < k) sout[q] = e;
+      }
+      if (mid) {
+        const uint32_t q = mbcnt(bm, b1);
+        if (q < kListCap) sc.list[q] = e;
       }
     }
   }
-  if (all) {
-    for (uint32_t i = n + tid; i < k; i += NT) sout[i] = make_uint2(0, kSentinelIdx);
-  }
-#pragma unroll
-  for (uint32_t o = 32; o > 0; o >>= 1) {
-    const uint32_t ok2 = shfl(min_key, lane ^ o), on2 = shfl(min_ni, lane ^ o);
-    if (ok2 < min_key || (ok2 == min_key && on2 < min_ni)) {
-      min_key = ok2;
-      min_ni = on2;
-    }
-  }
-  if (lane == 0) {
-    sc.mred[wave][0] = min_key;
-    sc.mred[wave][1] = min_ni;
-  }
   lds_sync();
-  min_key = ~0u;
-  min_ni = ~0u;
-#pragma unroll
-  for (int w = 0; w < WAVES; ++w) {
-    const uint32_t a = sc.mred[w][0], b = sc.mred[w][1];
-    if (a < min_key || (a == min_key && b < min_ni)) {
-      min_key = a;
-      min_ni = b;
-    }
-  }
-  return Thr{min_key, ~min_ni};
+
+  // every wave ranks the short list: the `need` best of its cnt entries are kept
+  const uint64_t mine = lane < cnt ? comp_of(sc.list[lane]) : 0ull;
+  uint32_t rank = 0;
+  for (uint32_t m = 0; m < cnt; ++m) rank += readlane64(mine, m) > mine ? 1u : 0u;
+  const bool keep = lane < cnt && rank < need;
+  if (wave == 0 && keep) sout[above_total + rank] = entry_of(mine);
+  const uint64_t piv = ballot(lane < cnt && rank == need - 1u);
+  thr = readlane64(mine, piv ? static_cast<uint32_t>(__builtin_ctzll(piv)) : 0u);
+  maxc = seen_max;
 }
 
-// Bitonic sort of cap (a power of two) entries, best first, then store the first k.
+// One compare-exchange stage (SIZE, STRIDE) of a bitonic sort of NT*E 64-bit keys, best first,
+// held E per thread in registers (element t*E + j in thread t). Partners closer than E are in
+// the same thread, closer than 64*E in the same wave (lane exchanges); farther partners go
+// through `xbuf` (NT*E slots of LDS) between two barriers. Recurses through all later stages.
+template <int WAVES, int E, uint32_t SIZE, uint32_t STRIDE>
+__device__ __forceinline__ void bitonic_stages(uint64_t (&v)[E], uint64_t* xbuf, uint32_t tid, uint32_t lane) {
+  constexpr uint32_t TOTAL = WAVES * 64 * E;
+  if constexpr (STRIDE < static_cast<uint32_t>(E)) {
+#pragma unroll
+    for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
+      if ((j & STRIDE) == 0) {
+        const bool desc = ((tid * E + j) & SIZE) == 0;
+        const uint64_t a = v[j], b = v[j | STRIDE];
+        const bool sw = desc ? b > a : a > b;
+        v[j] = sw ? b : a;
+        v[j | STRIDE] = sw ? a : b;
+      }
+    }
+  } else if constexpr (STRIDE < 64u * E) {
+    constexpr uint32_t M = STRIDE / E;
+#pragma unroll
+    for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
+      const uint32_t e = tid * E + j;
+      const bool take_max = ((e & STRIDE) == 0) == ((e & SIZE) == 0);
+      const uint64_t o = xor_lane64(v[j], M, lane);
+      v[j] = take_max ? (o > v[j] ? o : v[j]) : (o < v[j] ? o : v[j]);
+    }
+  } else {
+#pragma unroll
+    for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) xbuf[tid * E + j] = v[j];
+    lds_sync();
+#pragma unroll
+    for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
+      const uint32_t e = tid * E + j;
+      const bool take_max = ((e & STRIDE) == 0) == ((e & SIZE) == 0);
+      const uint64_t o = xbuf[e ^ STRIDE];
+      v[j] = take_max ? (o > v[j] ? o : v[j]) : (o < v[j] ? o : v[j]);
+    }
+    lds_sync();
+  }
+  if constexpr (STRIDE > 1)
+    bitonic_stages<WAVES, E, SIZE, STRIDE / 2>(v, xbuf, tid, lane);
+  else if constexpr (SIZE < TOTAL)
+    bitonic_stages<WAVES, E, SIZE * 2, SIZE>(v, xbuf, tid, lane);
+}
+
+// Sort the k entries of `fin` (padded with sentinels to NT*E) best first and store the first k.
+template <int DT, int WAVES, int E>
+__device__ void sort_store_e(const uint2* fin, uint64_t* xbuf, uint32_t k, void* out_vals, int32_t* out_idx,
+                             uint64_t row) {
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
+  uint64_t v[E];
+#pragma unroll
+  for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
+    const uint32_t e = tid * E + j;
+    v[j] = e < k ? comp_of(fin[e]) : 0ull;
+  }
+  bitonic_stages<WAVES, E, 2, 1>(v, xbuf, tid, lane);
+#pragma unroll
+  for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
+    const uint32_t e = tid * E + j;
+    if (e < k) {
+      const uint2 en = entry_of(v[j]);
+      if (out_vals) {
+        if constexpr (DT == DS_BF16)
+          static_cast<uint16_t*>(out_vals)[row * k + e] = static_cast<uint16_t>(raw_of_key<DT>(en.x));
+        else
+          static_cast<uint32_t*>(out_vals)[row * k + e] = raw_of_key<DT>(en.x);
+      }
+      if (out_idx) out_idx[row * k + e] = static_cast<int32_t>(en.y);
+    }
+  }
+}
+
+// Bitonic sort in LDS (one barrier per stage), for k above four entries per thread: sorts cap
+// (a power of two >= k) composites in `xbuf`, best first, and stores the first k.
 template <int DT, int WAVES>
-__device__ void sort_and_store(uint2* sb, const uint2* fin, uint32_t k, uint32_t cap, void* out_vals,
-                               int32_t* out_idx, uint64_t row) {
+__device__ void sort_store_lds(const uint2* fin, uint64_t* xbuf, uint32_t k, void* out_vals, int32_t* out_idx,
+                               uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x;
-  for (uint32_t i = tid; i < cap; i += NT) sb[i] = i < k ? fin[i] : make_uint2(0, kSentinelIdx);
+  uint32_t cap = 1;
+  while (cap < k) cap <<= 1;
+  for (uint32_t i = tid; i < cap; i += NT) xbuf[i] = i < k ? comp_of(fin[i]) : 0ull;
   lds_sync();
   for (uint32_t size = 2; size <= cap; size <<= 1) {
     for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
       for (uint32_t q = tid; q < cap / 2; q += NT) {
         const uint32_t i = ((q & ~(stride - 1)) << 1) | (q & (stride - 1));
         const uint32_t j = i + stride;
-        const uint2 a = sb[i], b = sb[j];
+        const uint64_t a = xbuf[i], b = xbuf[j];
         const bool desc = (i & size) == 0;
-        const bool b_first = b.x > a.x || (b.x == a.x && b.y < a.y);
-        if (b_first == desc) {
-          sb[i] = b;
-          sb[j] = a;
+        if (desc ? b > a : a > b) {
+          xbuf[i] = b;
+          xbuf[j] = a;
         }
       }
       lds_sync();
     }
   }
   for (uint32_t i = tid; i < k; i += NT) {
-    const uint2 e = sb[i];
+    const uint2 en = entry_of(xbuf[i]);
     if (out_vals) {
       if constexpr (DT == DS_BF16)
-        static_cast<uint16_t*>(out_vals)[row * k + i] = static_cast<uint16_t>(raw_of_key<DT>(e.x));
+        static_cast<uint16_t*>(out_vals)[row * k + i] = static_cast<uint16_t>(raw_of_key<DT>(en.x));
       else
-        static_cast<uint32_t*>(out_vals)[row * k + i] = raw_of_key<DT>(e.x);
+        static_cast<uint32_t*>(out_vals)[row * k + i] = raw_of_key<DT>(en.x);
     }
-    if (out_idx) out_idx[row * k + i] = static_cast<int32_t>(e.y);
+    if (out_idx) out_idx[row * k + i] = static_cast<int32_t>(en.y);
   }
+}
+
+// `xbuf` needs max(NT, pow2 >= k) 64-bit slots; `fin` must be visible to every thread.
+template <int DT, int WAVES>
+__device__ void sort_and_store(uint64_t* xbuf, const uint2* fin, uint32_t k, void* out_vals, int32_t* out_idx,
+                               uint64_t row) {
+  constexpr uint32_t NT = WAVES * 64;
+  if (k <= NT)
+    sort_store_e<DT, WAVES, 1>(fin, xbuf, k, out_vals, out_idx, row);
+  else if (k <= 2 * NT)
+    sort_store_e<DT, WAVES, 2>(fin, xbuf, k, out_vals, out_idx, row);
+  else if (k <= 4 * NT)
+    sort_store_e<DT, WAVES, 4>(fin, xbuf, k, out_vals, out_idx, row);
+  else
+    sort_store_lds<DT, WAVES>(fin, xbuf, k, out_vals, out_idx, row);
 }
 
 // Integer compare values for the streaming filter, from the threshold pair (key, idx).
@@ -474,7 +627,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   uint2* const app_main = lds + 2 * k;
   uint32_t* const hist3 = reinterpret_cast<uint32_t*>(lds + ((2 * k + B2 + B + 1u) & ~1u));  // 16-byte aligned
 
-  for (uint32_t i = tid; i < 768u; i += NT) hist3[i] = 0;
+  for (uint32_t i = tid; i < 3u * kBins; i += NT) hist3[i] = 0;
   if (tid == 0) {
     sc.app_count = 0;
     sc.outpos = 0;
@@ -483,14 +636,17 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   }
 
   const uint8_t* base = p.x + static_cast<uint64_t>(row) * p.row_stride_bytes + static_cast<uint64_t>(slice_lo) * EB;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, static_cast<int>(len * EB), kRsrcWord3);
+  // Range = the slice rounded up to whole 16-byte chunks: the hardware checks whole dwords, so
+  // an exact byte count would zero the dword that holds a bf16 row's odd last element. Row
+  // starts are 16-byte aligned, so the rounded range never leaves the row's last chunk.
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(base), 0, static_cast<int>((len * EB + 15u) & ~15u), kRsrcWord3);
   BlockOrder ord;
   ord.init(p.seed, row, slice, m);
 
   // threshold state (uniform across the workgroup)
   uint32_t mode = 0, thr_s = 0, thr_n = 0, t_idx = 0;
-  Thr prev_t{0, kSentinelIdx};
+  uint64_t thr_c = 0, maxc = 0;
   uint32_t nsurv = 0, cur = 0, napp = 0, hctr = 0;
   // counters (thread-uniform; used when stats are requested)
   uint64_t st_a = 0, st_r = 0, st_w = 0, st_max = 0, st_mono = 1, my_reads = 0, my_jsum = 0;
@@ -603,18 +759,18 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
       if (nsurv + napp >= k + B2) {
         uint2* const sout = nsurv ? (cur ? surv0 : surv1) : surv0;
         const uint2* const sin = cur ? surv1 : surv0;
-        const Thr t = compact<DT, WAVES, true>(sin, nsurv, nsurv ? app_main : app_warm, napp, sout, k, sc, hist3,
-                                               hctr);
+        const uint64_t prev_c = thr_c;
+        compact<DT, WAVES, true>(sin, nsurv, nsurv ? app_main : app_warm, napp, sout, k, sc, hist3, hctr, thr_c,
+                                 maxc);
         st_a += napp;
         st_w += nsurv + napp;
         st_r += 1;
-        if (t.key < prev_t.key || (t.key == prev_t.key && t.idx > prev_t.idx)) st_mono = 0;
-        prev_t = t;
+        if (thr_c < prev_c) st_mono = 0;
         cur = nsurv ? (cur ^ 1u) : 0u;
         nsurv = k;
         napp = 0;
-        t_idx = t.idx;
-        filter_thresholds<DT>(t, mode, thr_s, thr_n);
+        t_idx = ~static_cast<uint32_t>(thr_c);
+        filter_thresholds<DT>(Thr{static_cast<uint32_t>(thr_c >> 32), t_idx}, mode, thr_s, thr_n);
       }
     }
   }
@@ -623,10 +779,11 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   uint2* const fin = nsurv ? (cur ? surv0 : surv1) : surv0;
   {
     const uint2* const sin = cur ? surv1 : surv0;
-    compact<DT, WAVES, true>(sin, nsurv, nsurv ? app_main : app_warm, napp, fin, k, sc, hist3, hctr);
+    compact<DT, WAVES, true>(sin, nsurv, nsurv ? app_main : app_warm, napp, fin, k, sc, hist3, hctr, thr_c, maxc);
     st_a += napp;
     st_w += nsurv + napp;
   }
+  lds_sync();
 
   if (stats) {
     for (uint32_t o = 32; o > 0; o >>= 1) {
@@ -656,9 +813,9 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   }
 
   if (p.slices == 1) {
-    sort_and_store<DT, WAVES>(app_main, fin, k, static_cast<uint32_t>(p.sort_cap), p.out_vals, p.out_idx, row);
+    sort_and_store<DT, WAVES>(reinterpret_cast<uint64_t*>(app_main), fin, k, p.out_vals, p.out_idx, row);
   } else {
-    uint2* const dst = p.ws + static_cast<uint64_t>(blockIdx.x) * k;
+    uint2* const dst = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + static_cast<uint64_t>(slice) * k;
     for (uint32_t i = tid; i < k; i += NT) dst[i] = fin[i];
   }
 }
@@ -688,18 +845,19 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   uint2* const app_main = lds + 2 * k;
   uint32_t* const hist3 = reinterpret_cast<uint32_t*>(lds + ((2 * k + B2 + B + 1u) & ~1u));  // 16-byte aligned
 
-  for (uint32_t i = tid; i < 768u; i += NT) hist3[i] = 0;
+  for (uint32_t i = tid; i < 3u * kBins; i += NT) hist3[i] = 0;
   if (tid == 0) {
     sc.app_count = 0;
     sc.outpos = 0;
   }
-  const uint2* base = p.ws + static_cast<uint64_t>(row) * len;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint2*>(base), 0, static_cast<int>(len * 8u), kRsrcWord3);
+  const uint2* base = p.ws + static_cast<uint64_t>(row) * p.row_entries;  // rows padded to 16 bytes
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint2*>(base), 0, static_cast<int>((len * 8u + 15u) & ~15u), kRsrcWord3);
   BlockOrder ord;
   ord.init(p.seed, row, 0x7FFFFFFFu, m);
 
   bool accept_all = true;
+  uint64_t thr_c = 0, maxc = 0;
   Thr thr{0, 0};
   uint32_t nsurv = 0, cur = 0, napp = 0, hctr = 0;
 
@@ -774,7 +932,9 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
       if (nsurv + napp >= k + B2) {
         uint2* const sout = nsurv ? (cur ? surv0 : surv1) : surv0;
         const uint2* const sin = cur ? surv1 : surv0;
-        thr = compact<DT, WAVES, false>(sin, nsurv, nsurv ? app_main : app_warm, napp, sout, k, sc, hist3, hctr);
+        compact<DT, WAVES, false>(sin, nsurv, nsurv ? app_main : app_warm, napp, sout, k, sc, hist3, hctr, thr_c,
+                                  maxc);
+        thr = Thr{static_cast<uint32_t>(thr_c >> 32), ~static_cast<uint32_t>(thr_c)};
         accept_all = false;
         cur = nsurv ? (cur ^ 1u) : 0u;
         nsurv = k;
@@ -785,9 +945,10 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   uint2* const fin = nsurv ? (cur ? surv0 : surv1) : surv0;
   {
     const uint2* const sin = cur ? surv1 : surv0;
-    compact<DT, WAVES, false>(sin, nsurv, nsurv ? app_main : app_warm, napp, fin, k, sc, hist3, hctr);
+    compact<DT, WAVES, false>(sin, nsurv, nsurv ? app_main : app_warm, napp, fin, k, sc, hist3, hctr, thr_c, maxc);
   }
-  sort_and_store<DT, WAVES>(app_main, fin, k, static_cast<uint32_t>(p.sort_cap), p.out_vals, p.out_idx, row);
+  lds_sync();
+  sort_and_store<DT, WAVES>(reinterpret_cast<uint64_t*>(app_main), fin, k, p.out_vals, p.out_idx, row);
 }
 
 // --------------------------------------------------------------------------- probes
@@ -884,7 +1045,7 @@ hipError_t launch_merge_dt(const MergeParams& p, int64_t rows, size_t lds, hipSt
 
 size_t select_lds_bytes(int k, int block, int slack, int waves) {
   (void)waves;
-  return (static_cast<size_t>(2) * k + slack + block + 1) * 8 + 768 * 4 + sizeof(Scalars);
+  return (static_cast<size_t>(2) * k + slack + block + 1) * 8 + 3 * kBins * 4 + sizeof(Scalars);
 }
 
 hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,
