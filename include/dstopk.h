@@ -83,6 +83,10 @@ typedef struct ds_stats {
   uint64_t slice_len;   /* elements in the slice */
   uint64_t block;       /* B used */
   uint64_t slack;       /* B2 used */
+  uint64_t t_total_ns;  /* workgroup wall time (device real-time clock, 10 ns ticks) */
+  uint64_t t_compact_ns; /* time in in-loop compactions */
+  uint64_t t_sync_ns;   /* time in the per-block barrier */
+  uint64_t t_final_ns;  /* time in the final compaction and output */
   uint64_t reserved;
 } ds_stats;
 

@@ -43,7 +43,7 @@ class ds_config(ctypes.Structure):
 
 
 STATS_FIELDS = ["appended", "compactions", "work", "max_len", "reads", "index_sum", "monotone", "slice_lo",
-                "slice_len", "block", "slack", "reserved"]
+                "slice_len", "block", "slack", "t_total_ns", "t_compact_ns", "t_sync_ns", "t_final_ns", "reserved"]
 STATS_DTYPE = np.dtype([(f, np.uint64) for f in STATS_FIELDS])
 
 _lock = threading.Lock()
@@ -182,7 +182,7 @@ def ds_topk(x, k: int, seed: int = 0, values: bool = True, indices: bool = True,
 def ds_topk_ex(x, k: int, seed: int = 0, workspace=None, cfg: Optional[Dict[str, int]] = None, stats=None,
                values: bool = True, indices: bool = True, out_vals=None, out_idx=None, stream=None):
     """ds_topk with a caller workspace (a device tensor), forced config and optional stats
-    (a device uint8 tensor of rows*slices*96 bytes). Allocates nothing itself."""
+    (a device uint8 tensor of rows*slices*128 bytes). Allocates nothing itself."""
     rows, n, rs, dt, out_vals, out_idx = _prep(x, k, values, indices, out_vals, out_idx)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())

@@ -176,14 +176,15 @@ int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t r
   return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }
 
-int run_merge(const Plan& pl, int64_t rows, int k, uint64_t seed, void* out_vals, int32_t* out_idx, void* ws,
-              hipStream_t stream) {
+int run_merge(const Plan& pl, int64_t rows, int64_t n, int k, uint64_t seed, void* out_vals, int32_t* out_idx,
+              void* ws, hipStream_t stream) {
   if (pl.slices <= 1) return DS_OK;
   (void)hipGetLastError();
   ds::MergeParams mp{};
   mp.ws = static_cast<const uint2*>(ws);
   mp.entries = static_cast<int64_t>(pl.slices) * k;
   mp.row_entries = (mp.entries + 1) & ~int64_t(1);
+  mp.n = n;
   mp.k = k;
   mp.slack = pl.mslack;
   mp.sort_cap = pl.sort_cap;
@@ -197,7 +198,7 @@ int run(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t row_stri
         void* out_vals, int32_t* out_idx, void* ws, ds_stats* stats, hipStream_t stream) {
   int st = run_select(pl, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, stats, stream);
   if (st != DS_OK) return st;
-  return run_merge(pl, rows, k, seed, out_vals, out_idx, ws, stream);
+  return run_merge(pl, rows, n, k, seed, out_vals, out_idx, ws, stream);
 }
 
 // Plan a call that brings its own workspace; validates the workspace against the plan.
@@ -322,7 +323,7 @@ int ds_topk_merge(int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void
   Plan p;
   st = plan_with_workspace(rows, n, k, dtype, cfg, workspace, ws_bytes, &p);
   if (st != DS_OK) return st;
-  return run_merge(p, rows, k, seed, out_vals, out_idx, workspace, static_cast<hipStream_t>(stream));
+  return run_merge(p, rows, n, k, seed, out_vals, out_idx, workspace, static_cast<hipStream_t>(stream));
 }
 
 int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,

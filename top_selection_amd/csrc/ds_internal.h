@@ -34,6 +34,7 @@ struct MergeParams {
   const uint2* ws;     // row r's entries at ws + r*row_entries
   int64_t entries;     // slices * k
   int64_t row_entries; // entries rounded up to even
+  int64_t n;           // row length (indices lie in [0, n))
   int32_t k;
   int32_t slack;
   int32_t sort_cap;
@@ -50,7 +51,7 @@ struct Shape {
 
 // Select-kernel shapes built for each element type. The block size is
 // waves * cpw * 64 lanes * (16 / elem_bytes) elements.
-constexpr Shape kSelectShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}, {8, 2}, {4, 4}, {8, 4}};
+constexpr Shape kSelectShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}, {8, 2}, {4, 4}, {8, 4}, {16, 1}, {16, 2}};
 constexpr int kNumSelectShapes = sizeof(kSelectShapes) / sizeof(kSelectShapes[0]);
 constexpr Shape kMergeShape = {4, 4};  // 4 waves x 4 chunks x 128 entries = 2048 entries per block
 

@@ -86,24 +86,6 @@ __device__ __forceinline__ uint64_t xor_lane64(uint64_t v, uint32_t m, uint32_t 
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t wave_max64(uint64_t v, uint32_t lane) {
-#pragma unroll
-  for (uint32_t m = 1; m < 64; m <<= 1) {
-    const uint64_t o = xor_lane64(v, m, lane);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ uint64_t wave_min64(uint64_t v, uint32_t lane) {
-#pragma unroll
-  for (uint32_t m = 1; m < 64; m <<= 1) {
-    const uint64_t o = xor_lane64(v, m, lane);
-    v = o < v ? o : v;
-  }
-  return v;
-}
-
 // Inclusive prefix sum over the 64 lanes (row shifts within 16-lane rows, then the row
 // broadcasts of lanes 15 and 31).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
@@ -209,28 +191,53 @@ struct Scalars {
   uint32_t listpos;                 // pivot-list cursor of the running compaction
   uint32_t pad0;
   uint32_t slot[2][kMaxWaves];      // per-wave end of its reservation, by block parity
-  uint64_t red[kMaxWaves][2];       // per-wave min / max composites
-  uint2 list[kListCap];             // entries of the pivot bin
+  uint32_t red[kMaxWaves][2];       // per-wave min / max keys
+  uint32_t scan[4];                 // bin scan result published by wave 0
+  uint32_t lkey[kListCap];          // pivot-bin entries
+  uint32_t lidx[kListCap];
   unsigned long long reads;         // counters (stats runs only)
   unsigned long long index_sum;
+};
+
+// Candidate buffer in LDS, keys and indices in separate arrays (16-byte aligned, capacity a
+// multiple of 4). Entries [0, nsurv) are survivors (keys), [nsurv, n) were appended since the
+// last compaction (raw element bits in the select kernel; bf16 in the high half). tkey/tidx
+// (k entries) receive the scattered survivors of a compaction.
+struct Cand {
+  uint32_t* key;
+  uint32_t* idx;
+  uint32_t* tkey;
+  uint32_t* tidx;
 };
 
 struct Thr {
   uint32_t key, idx;
 };
 
-__device__ __forceinline__ uint64_t comp_of(uint2 e) {
-  return (static_cast<uint64_t>(e.x) << 32) | static_cast<uint32_t>(~e.y);
+__device__ __forceinline__ uint64_t comp_of(uint32_t key, uint32_t idx) {
+  return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~idx);
 }
 
-__device__ __forceinline__ uint2 entry_of(uint64_t c) {
-  return make_uint2(static_cast<uint32_t>(c >> 32), ~static_cast<uint32_t>(c));
+__device__ __forceinline__ uint32_t bitlen32(uint32_t v) { return v ? 32u - static_cast<uint32_t>(__builtin_clz(v)) : 0u; }
+
+__device__ __forceinline__ uint32_t wave_max32(uint32_t v, uint32_t lane) {
+#pragma unroll
+  for (uint32_t m = 1; m < 64; m <<= 1) v = max(v, xor_lane(v, m, lane));
+  return v;
 }
 
-__device__ __forceinline__ uint32_t bitlen64(uint64_t v) { return v ? 64u - static_cast<uint32_t>(__builtin_clzll(v)) : 0u; }
+__device__ __forceinline__ uint32_t wave_min32(uint32_t v, uint32_t lane) {
+#pragma unroll
+  for (uint32_t m = 1; m < 64; m <<= 1) v = min(v, xor_lane(v, m, lane));
+  return v;
+}
 
-// Every wave scans the same kBins-bin histogram from the top bin down and finds the bin that
-// holds the `need`-th best entry: `above` entries lie in higher bins, `cnt` in that bin.
+__device__ __forceinline__ uint32_t u4get(const uint4& v, uint32_t q) {
+  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
+
+// One wave scans a kBins-bin histogram from the top bin down and finds the bin that holds the
+// `need`-th best entry: `above` entries lie in higher bins, `cnt` in that bin.
 __device__ __forceinline__ void scan_select(const uint32_t* h, uint32_t need, uint32_t lane, uint32_t& bin,
                                             uint32_t& above, uint32_t& cnt) {
   constexpr uint32_t PER = kBins / 64;  // 8 bins per lane, lane 0 holds the highest
@@ -263,58 +270,70 @@ __device__ __forceinline__ void scan_select(const uint32_t* h, uint32_t need, ui
 
 // Radix-select compaction.
 //
-// Reduces the nsurv survivors in `sin` plus the napp appended entries in `app` to the k best
-// under the composite order and writes them (unordered) to `sout`. Returns the smallest kept
-// composite (the new threshold) in `thr` and the largest in `maxc`.
+// Reduces the n entries of the candidate buffer to the k best under the composite order
+// (key descending, then index ascending). In-loop calls (fin == false) leave the survivors in
+// entries [0, k) of the buffer and return the smallest of them as the new threshold
+// (tkey, tidx) and the largest key in maxkey; the final call (fin == true) leaves them in
+// tkey/tidx (padded with sentinels when n < k).
 //
-// The search runs on the 64-bit composite c = (key << 32) | ~index over a window
-// [lo, hi] that holds every entry: a kBins-bin histogram of (c - lo) >> shift (entries
-// above hi fall in the top bin) locates the bin of the k-th best; while that bin holds more
-// than kListCap entries the window shrinks to it and the histogram repeats; then the
-// entries above the bin are scattered to `sout`, the bin's entries are gathered in a short
-// list, and every wave ranks that list to pick the rest and the threshold.
-// First call (nsurv == 0): one extra pass turns the raw entries into keys and measures the
-// window. Later calls: the window is [previous threshold, previous maximum] and the raw ->
-// key step is folded into the first histogram pass.
-// RAW: appended entries hold raw element bits (bf16: in the high half).
+// Search: a kBins-bin histogram of (key - lo) >> shift over a key window [lo, hi] that holds
+// every entry locates the bin of the k-th best; while that bin holds more than kListCap
+// entries the window shrinks to it and the histogram repeats; a bin that is a single key
+// (ties) continues on the indices in [ilo, ihi] (smaller index first). Then the entries
+// above the pivot bin are scattered out, the bin's entries are gathered in a short list, and
+// the list is ranked to pick the rest and the threshold.
+// First call (nsurv == 0): one pass turns raw entries into keys and measures the window.
+// Later calls: the window is [threshold key, previous maximum key]; new entries above it fall
+// into the top bin ("open" bin, refined over [bin start, true maximum]); the raw -> key step
+// is folded into the first histogram pass.
 template <int DT, int WAVES, bool RAW>
-__device__ void compact(const uint2* sin, uint32_t nsurv, uint2* app, uint32_t napp, uint2* sout, uint32_t k,
-                        Scalars& sc, uint32_t* hist3, uint32_t& hctr, uint64_t& thr, uint64_t& maxc) {
+__device__ void compact(const Cand& c, uint32_t n, uint32_t nsurv, uint32_t k, bool fin, uint32_t ilo,
+                        uint32_t ihi, Scalars& sc, uint32_t* hist3, uint32_t& hctr, uint32_t& tkey,
+                        uint32_t& tidx, uint32_t& maxkey) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-  const uint32_t n = nsurv + napp;
+  const uint32_t groups = (n + 3u) / 4u;  // entries are visited four at a time
+  auto conv = [](uint32_t raw) { return key_of_raw<DT>(DT == DS_BF16 ? (raw >> 16) : raw); };
 
   if (n <= k) {  // keep everything (only the final call can get here)
     for (uint32_t i = tid; i < k; i += NT) {
-      uint2 e = make_uint2(0, kSentinelIdx);
-      if (i < nsurv) {
-        e = sin[i];
-      } else if (i < n) {
-        e = app[i - nsurv];
-        if constexpr (RAW) e.x = key_of_raw<DT>(DT == DS_BF16 ? (e.x >> 16) : e.x);
+      uint32_t key = 0, id = kSentinelIdx;
+      if (i < n) {
+        key = c.key[i];
+        if (RAW && i >= nsurv) key = conv(key);
+        id = c.idx[i];
       }
-      sout[i] = e;
+      c.tkey[i] = key;
+      c.tidx[i] = id;
     }
     lds_sync();
     return;
   }
 
-  uint64_t lo, hi;
   bool raw_pending = RAW;
+  uint32_t lo, hi;
+  bool top_open;
   if (nsurv == 0) {
-    uint64_t mn = ~0ull, mx = 0;
-    for (uint32_t i = tid; i < n; i += NT) {
-      uint2 e = app[i];
+    uint32_t mn = ~0u, mx = 0;
+    for (uint32_t g = tid; g < groups; g += NT) {
+      uint4 kk = *reinterpret_cast<const uint4*>(c.key + 4 * g);
       if constexpr (RAW) {
-        e.x = key_of_raw<DT>(DT == DS_BF16 ? (e.x >> 16) : e.x);
-        app[i].x = e.x;
+        kk.x = conv(kk.x);
+        kk.y = conv(kk.y);
+        kk.z = conv(kk.z);
+        kk.w = conv(kk.w);
+        *reinterpret_cast<uint4*>(c.key + 4 * g) = kk;
       }
-      const uint64_t c = comp_of(e);
-      mn = c < mn ? c : mn;
-      mx = c > mx ? c : mx;
+#pragma unroll
+      for (uint32_t q = 0; q < 4; ++q) {
+        if (4 * g + q < n) {
+          mn = min(mn, u4get(kk, q));
+          mx = max(mx, u4get(kk, q));
+        }
+      }
     }
-    mn = wave_min64(mn, lane);
-    mx = wave_max64(mx, lane);
+    mn = wave_min32(mn, lane);
+    mx = wave_max32(mx, lane);
     if (lane == 0) {
       sc.red[wave][0] = mn;
       sc.red[wave][1] = mx;
@@ -325,17 +344,19 @@ __device__ void compact(const uint2* sin, uint32_t nsurv, uint2* app, uint32_t n
       sc.listpos = 0;
     }
     lds_sync();
-    lo = ~0ull;
+    lo = ~0u;
     hi = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
-      lo = sc.red[w][0] < lo ? sc.red[w][0] : lo;
-      hi = sc.red[w][1] > hi ? sc.red[w][1] : hi;
+      lo = min(lo, sc.red[w][0]);
+      hi = max(hi, sc.red[w][1]);
     }
+    top_open = false;
     raw_pending = false;
   } else {
-    lo = thr;
-    hi = maxc;
+    lo = tkey;  // every entry ranks at or above the threshold
+    hi = maxkey;
+    top_open = true;
     if (tid == 0) {  // every wave passed the block barrier after its appends
       sc.app_count = 0;
       sc.outpos = 0;
@@ -343,103 +364,184 @@ __device__ void compact(const uint2* sin, uint32_t nsurv, uint2* app, uint32_t n
     }
   }
 
-  // histogram passes, shrinking [lo, hi] to the bin of the k-th best
-  uint32_t need = k, above_total = 0, cnt = 0;
-  uint64_t plo = lo, phi = hi;  // current pivot window
-  bool top_open = nsurv != 0;   // entries above hi may exist (they fall in the top bin)
-  uint64_t seen_max = 0;
+  // histogram passes
+  uint32_t need = k, above_total = 0, cnt = 0, seen_max = 0;
+  uint32_t plo = lo, phi = hi;  // key window of the pivot
+  bool tie = false;             // pivot window is a single key: continue on indices
+  uint32_t pkey = 0, iplo = ilo, iphi = ihi;
   for (;;) {
-    const uint32_t shift = bitlen64(phi - plo) > 9 ? bitlen64(phi - plo) - 9 : 0;
+    const uint32_t range = tie ? iphi - iplo : phi - plo;
+    const uint32_t shift = bitlen32(range) > 9 ? bitlen32(range) - 9 : 0;
     uint32_t* h = hist3 + kBins * (hctr % 3u);
     uint32_t* hn = hist3 + kBins * ((hctr + 1u) % 3u);
     for (uint32_t b = tid; b < kBins; b += NT) hn[b] = 0;
-    uint64_t mx = 0;
-    for (uint32_t i = tid; i < n; i += NT) {
-      uint2 e;
-      if (i < nsurv) {
-        e = sin[i];
-      } else {
-        e = app[i - nsurv];
-        if (raw_pending) {
-          e.x = key_of_raw<DT>(DT == DS_BF16 ? (e.x >> 16) : e.x);
-          app[i - nsurv].x = e.x;
-        }
+    uint32_t mx = 0;
+    for (uint32_t g = tid; g < groups; g += NT) {
+      uint4 kk = *reinterpret_cast<const uint4*>(c.key + 4 * g);
+      if (raw_pending && 4 * g + 3 >= nsurv) {
+        if (4 * g + 0 >= nsurv) kk.x = conv(kk.x);
+        if (4 * g + 1 >= nsurv) kk.y = conv(kk.y);
+        if (4 * g + 2 >= nsurv) kk.z = conv(kk.z);
+        kk.w = conv(kk.w);
+        *reinterpret_cast<uint4*>(c.key + 4 * g) = kk;
       }
-      const uint64_t c = comp_of(e);
-      mx = c > mx ? c : mx;
-      if (c >= plo && (c <= phi || top_open)) {
-        const uint64_t d = (c > phi ? phi : c) - plo;
-        atomicAdd(&h[static_cast<uint32_t>(d >> shift)], 1u);
+      if (!tie) {
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+          const uint32_t key = u4get(kk, q);
+          if (4 * g + q < n) {
+            mx = max(mx, key);
+            if (key >= plo && (key <= phi || top_open)) atomicAdd(&h[(min(key, phi) - plo) >> shift], 1u);
+          }
+        }
+      } else {
+        const uint4 ii = *reinterpret_cast<const uint4*>(c.idx + 4 * g);
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+          const uint32_t key = u4get(kk, q), id = u4get(ii, q);
+          if (4 * g + q < n) {
+            mx = max(mx, key);
+            if (key == pkey && id >= iplo && id <= iphi) atomicAdd(&h[kBins - 1u - ((id - iplo) >> shift)], 1u);
+          }
+        }
       }
     }
     raw_pending = false;
-    mx = wave_max64(mx, lane);
+    mx = wave_max32(mx, lane);
     if (lane == 0) sc.red[wave][1] = mx;
     lds_sync();
     ++hctr;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) seen_max = sc.red[w][1] > seen_max ? sc.red[w][1] : seen_max;
+    for (int w = 0; w < WAVES; ++w) seen_max = max(seen_max, sc.red[w][1]);
     uint32_t bin, above;
-    scan_select(h, need, lane, bin, above, cnt);
+    if constexpr (WAVES > 4) {  // one wave scans and publishes the result
+      if (wave == 0) {
+        scan_select(h, need, lane, bin, above, cnt);
+        if (lane == 0) {
+          sc.scan[0] = bin;
+          sc.scan[1] = above;
+          sc.scan[2] = cnt;
+        }
+      }
+      lds_sync();
+      bin = sc.scan[0];
+      above = sc.scan[1];
+      cnt = sc.scan[2];
+    } else {
+      scan_select(h, need, lane, bin, above, cnt);
+    }
     need -= above;
     above_total += above;
-    const uint64_t nlo = plo + (static_cast<uint64_t>(bin) << shift);
-    const bool open_bin = top_open && (bin == kBins - 1u || ((phi - plo) >> shift) == bin);
-    uint64_t nhi = plo + ((static_cast<uint64_t>(bin) + 1u) << shift) - 1u;
-    if (nhi > phi || nhi < nlo) nhi = phi;
-    plo = nlo;
-    phi = open_bin ? seen_max : nhi;
-    top_open = false;
-    // A chosen open bin widens the window to the true maximum, so it is refined again even
-    // when this pass had single-composite bins.
-    if (cnt <= kListCap || (shift == 0 && !open_bin)) break;
-  }
-
-  // scatter: everything above the pivot window is kept; the window's entries go to the list
-  // (cnt > kListCap only if composites repeat, which real entries never do; the list then
-  // keeps its first kListCap entries and the call still ends)
-  cnt = cnt < kListCap ? cnt : kListCap;
-  const uint32_t iters = (n + NT - 1) / NT;
-  for (uint32_t it = 0; it < iters; ++it) {
-    const uint32_t i = it * NT + tid;
-    uint2 e = make_uint2(0, kSentinelIdx);
-    uint64_t c = 0;
-    if (i < n) {
-      e = i < nsurv ? sin[i] : app[i - nsurv];
-      c = comp_of(e);
+    if (!tie) {
+      const uint32_t nlo = plo + (bin << shift);
+      const bool open_bin = top_open && bin == ((phi - plo) >> shift);
+      const uint64_t nhi64 = static_cast<uint64_t>(plo) + ((static_cast<uint64_t>(bin) + 1u) << shift) - 1u;
+      const uint32_t nhi = nhi64 > phi ? phi : static_cast<uint32_t>(nhi64);
+      plo = nlo;
+      phi = open_bin ? seen_max : nhi;
+      top_open = false;
+      if (cnt <= kListCap) break;
+      if (shift == 0 && !open_bin) {  // one key holds more than kListCap entries
+        tie = true;
+        pkey = plo;
+      }
+    } else {
+      const uint32_t nlo = iplo + ((kBins - 1u - bin) << shift);
+      const uint64_t nhi64 = static_cast<uint64_t>(nlo) + (1ull << shift) - 1u;
+      iphi = nhi64 > iphi ? iphi : static_cast<uint32_t>(nhi64);
+      iplo = nlo;
+      if (cnt <= kListCap || shift == 0) break;
     }
-    const bool up = i < n && c > phi;
-    const bool mid = i < n && c >= plo && c <= phi;
-    const uint64_t bu = ballot(up), bm = ballot(mid);
-    if (bu | bm) {
+  }
+  cnt = cnt < kListCap ? cnt : kListCap;  // more only if (key, index) pairs repeat
+
+  // scatter: entries above the pivot window go out, the window's entries to the list
+  const uint32_t iters = (groups + NT - 1) / NT;
+  for (uint32_t it = 0; it < iters; ++it) {
+    const uint32_t g = it * NT + tid;
+    uint4 kk = make_uint4(0, 0, 0, 0), ii = make_uint4(0, 0, 0, 0);
+    if (g < groups) {
+      kk = *reinterpret_cast<const uint4*>(c.key + 4 * g);
+      ii = *reinterpret_cast<const uint4*>(c.idx + 4 * g);
+    }
+    bool up[4], mid[4];
+    uint64_t bu[4], bm[4];
+    uint32_t nu = 0, nm = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+      const uint32_t key = u4get(kk, q), id = u4get(ii, q);
+      const bool valid = g < groups && 4 * g + q < n;
+      if (!tie) {
+        up[q] = valid && key > phi;
+        mid[q] = valid && key >= plo && key <= phi;
+      } else {
+        up[q] = valid && (key > pkey || (key == pkey && id < iplo));
+        mid[q] = valid && key == pkey && id >= iplo && id <= iphi;
+      }
+      bu[q] = ballot(up[q]);
+      bm[q] = ballot(mid[q]);
+      nu += popc(bu[q]);
+      nm += popc(bm[q]);
+    }
+    if (nu | nm) {
       uint32_t b0 = 0, b1 = 0;
       if (lane == 0) {
-        if (bu) b0 = atomicAdd(&sc.outpos, popc(bu));
-        if (bm) b1 = atomicAdd(&sc.listpos, popc(bm));
+        if (nu) b0 = atomicAdd(&sc.outpos, nu);
+        if (nm) b1 = atomicAdd(&sc.listpos, nm);
       }
       b0 = uni(b0);
       b1 = uni(b1);
-      if (up) {
-        const uint32_t q = mbcnt(bu, b0);
-        if (q < k) sout[q] = e;
-      }
-      if (mid) {
-        const uint32_t q = mbcnt(bm, b1);
-        if (q < kListCap) sc.list[q] = e;
+#pragma unroll
+      for (uint32_t q = 0; q < 4; ++q) {
+        if (up[q]) {
+          const uint32_t at = mbcnt(bu[q], b0);
+          if (at < k) {
+            c.tkey[at] = u4get(kk, q);
+            c.tidx[at] = u4get(ii, q);
+          }
+        }
+        if (mid[q]) {
+          const uint32_t at = mbcnt(bm[q], b1);
+          if (at < kListCap) {
+            sc.lkey[at] = u4get(kk, q);
+            sc.lidx[at] = u4get(ii, q);
+          }
+        }
+        b0 += popc(bu[q]);
+        b1 += popc(bm[q]);
       }
     }
   }
   lds_sync();
 
   // every wave ranks the short list: the `need` best of its cnt entries are kept
-  const uint64_t mine = lane < cnt ? comp_of(sc.list[lane]) : 0ull;
+  const bool have = lane < cnt;
+  const uint32_t lk = have ? sc.lkey[lane] : 0u, li = have ? sc.lidx[lane] : kSentinelIdx;
+  const uint64_t mine = comp_of(lk, li);
   uint32_t rank = 0;
   for (uint32_t m = 0; m < cnt; ++m) rank += readlane64(mine, m) > mine ? 1u : 0u;
-  const bool keep = lane < cnt && rank < need;
-  if (wave == 0 && keep) sout[above_total + rank] = entry_of(mine);
-  const uint64_t piv = ballot(lane < cnt && rank == need - 1u);
-  thr = readlane64(mine, piv ? static_cast<uint32_t>(__builtin_ctzll(piv)) : 0u);
-  maxc = seen_max;
+  const bool keep = have && rank < need;
+  const uint64_t piv = ballot(have && rank == need - 1u);
+  const uint32_t pl = piv ? static_cast<uint32_t>(__builtin_ctzll(piv)) : 0u;
+  tkey = __builtin_amdgcn_readlane(lk, pl);
+  tidx = __builtin_amdgcn_readlane(li, pl);
+  maxkey = seen_max;
+  if (!fin) {
+    for (uint32_t i = tid; i < above_total && i < k; i += NT) {
+      c.key[i] = c.tkey[i];
+      c.idx[i] = c.tidx[i];
+    }
+    if (wave == 0 && keep) {
+      c.key[above_total + rank] = lk;
+      c.idx[above_total + rank] = li;
+    }
+  } else {
+    if (wave == 0 && keep) {
+      c.tkey[above_total + rank] = lk;
+      c.tidx[above_total + rank] = li;
+    }
+    lds_sync();
+  }
 }
 
 // One compare-exchange stage (SIZE, STRIDE) of a bitonic sort of NT*E 64-bit keys, best first,
@@ -488,45 +590,64 @@ __device__ __forceinline__ void bitonic_stages(uint64_t (&v)[E], uint64_t* xbuf,
     bitonic_stages<WAVES, E, SIZE * 2, SIZE>(v, xbuf, tid, lane);
 }
 
-// Sort the k entries of `fin` (padded with sentinels to NT*E) best first and store the first k.
+template <int DT>
+__device__ __forceinline__ void store_out(void* out_vals, int32_t* out_idx, uint64_t at, uint64_t c) {
+  const uint32_t key = static_cast<uint32_t>(c >> 32), id = ~static_cast<uint32_t>(c);
+  if (out_vals) {
+    if constexpr (DT == DS_BF16)
+      static_cast<uint16_t*>(out_vals)[at] = static_cast<uint16_t>(raw_of_key<DT>(key));
+    else
+      static_cast<uint32_t*>(out_vals)[at] = raw_of_key<DT>(key);
+  }
+  if (out_idx) out_idx[at] = static_cast<int32_t>(id);
+}
+
+// Sort the k entries of (fkey, fidx) (padded with sentinels to NT*E) best first and store the
+// first k of them.
 template <int DT, int WAVES, int E>
-__device__ void sort_store_e(const uint2* fin, uint64_t* xbuf, uint32_t k, void* out_vals, int32_t* out_idx,
-                             uint64_t row) {
+__device__ void sort_store_e(const uint32_t* fkey, const uint32_t* fidx, uint64_t* xbuf, uint32_t k,
+                             void* out_vals, int32_t* out_idx, uint64_t row) {
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   uint64_t v[E];
 #pragma unroll
   for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
     const uint32_t e = tid * E + j;
-    v[j] = e < k ? comp_of(fin[e]) : 0ull;
+    v[j] = e < k ? comp_of(fkey[e], fidx[e]) : 0ull;
   }
+  lds_sync();  // xbuf may overlap memory other threads are still reading above
   bitonic_stages<WAVES, E, 2, 1>(v, xbuf, tid, lane);
 #pragma unroll
   for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
     const uint32_t e = tid * E + j;
-    if (e < k) {
-      const uint2 en = entry_of(v[j]);
-      if (out_vals) {
-        if constexpr (DT == DS_BF16)
-          static_cast<uint16_t*>(out_vals)[row * k + e] = static_cast<uint16_t>(raw_of_key<DT>(en.x));
-        else
-          static_cast<uint32_t*>(out_vals)[row * k + e] = raw_of_key<DT>(en.x);
-      }
-      if (out_idx) out_idx[row * k + e] = static_cast<int32_t>(en.y);
-    }
+    if (e < k) store_out<DT>(out_vals, out_idx, row * k + e, v[j]);
   }
 }
 
-// Bitonic sort in LDS (one barrier per stage), for k above four entries per thread: sorts cap
+// Bitonic sort in LDS (one barrier per stage) for k above four entries per thread: sorts cap
 // (a power of two >= k) composites in `xbuf`, best first, and stores the first k.
 template <int DT, int WAVES>
-__device__ void sort_store_lds(const uint2* fin, uint64_t* xbuf, uint32_t k, void* out_vals, int32_t* out_idx,
-                               uint64_t row) {
+__device__ void sort_store_lds(const uint32_t* fkey, const uint32_t* fidx, uint64_t* xbuf, uint32_t k,
+                               void* out_vals, int32_t* out_idx, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x;
   uint32_t cap = 1;
   while (cap < k) cap <<= 1;
-  for (uint32_t i = tid; i < cap; i += NT) xbuf[i] = i < k ? comp_of(fin[i]) : 0ull;
-  lds_sync();
+  // xbuf may overlap (fkey, fidx): read everything into registers first, in two halves
+  for (uint32_t base = 0; base < cap; base += NT * 8) {
+    uint64_t tmp[8];
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j) {
+      const uint32_t i = base + j * NT + tid;
+      tmp[j] = i < k ? comp_of(fkey[i], fidx[i]) : 0ull;
+    }
+    lds_sync();
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j) {
+      const uint32_t i = base + j * NT + tid;
+      if (i < cap) xbuf[i] = tmp[j];
+    }
+    lds_sync();
+  }
   for (uint32_t size = 2; size <= cap; size <<= 1) {
     for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
       for (uint32_t q = tid; q < cap / 2; q += NT) {
@@ -542,31 +663,22 @@ __device__ void sort_store_lds(const uint2* fin, uint64_t* xbuf, uint32_t k, voi
       lds_sync();
     }
   }
-  for (uint32_t i = tid; i < k; i += NT) {
-    const uint2 en = entry_of(xbuf[i]);
-    if (out_vals) {
-      if constexpr (DT == DS_BF16)
-        static_cast<uint16_t*>(out_vals)[row * k + i] = static_cast<uint16_t>(raw_of_key<DT>(en.x));
-      else
-        static_cast<uint32_t*>(out_vals)[row * k + i] = raw_of_key<DT>(en.x);
-    }
-    if (out_idx) out_idx[row * k + i] = static_cast<int32_t>(en.y);
-  }
+  for (uint32_t i = tid; i < k; i += NT) store_out<DT>(out_vals, out_idx, row * k + i, xbuf[i]);
 }
 
-// `xbuf` needs max(NT, pow2 >= k) 64-bit slots; `fin` must be visible to every thread.
+// `xbuf` needs max(NT, pow2 >= k) 64-bit slots; (fkey, fidx) must be visible to every thread.
 template <int DT, int WAVES>
-__device__ void sort_and_store(uint64_t* xbuf, const uint2* fin, uint32_t k, void* out_vals, int32_t* out_idx,
-                               uint64_t row) {
+__device__ void sort_and_store(uint64_t* xbuf, const uint32_t* fkey, const uint32_t* fidx, uint32_t k,
+                               void* out_vals, int32_t* out_idx, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
   if (k <= NT)
-    sort_store_e<DT, WAVES, 1>(fin, xbuf, k, out_vals, out_idx, row);
+    sort_store_e<DT, WAVES, 1>(fkey, fidx, xbuf, k, out_vals, out_idx, row);
   else if (k <= 2 * NT)
-    sort_store_e<DT, WAVES, 2>(fin, xbuf, k, out_vals, out_idx, row);
+    sort_store_e<DT, WAVES, 2>(fkey, fidx, xbuf, k, out_vals, out_idx, row);
   else if (k <= 4 * NT)
-    sort_store_e<DT, WAVES, 4>(fin, xbuf, k, out_vals, out_idx, row);
+    sort_store_e<DT, WAVES, 4>(fkey, fidx, xbuf, k, out_vals, out_idx, row);
   else
-    sort_store_lds<DT, WAVES>(fin, xbuf, k, out_vals, out_idx, row);
+    sort_store_lds<DT, WAVES>(fkey, fidx, xbuf, k, out_vals, out_idx, row);
 }
 
 // Integer compare values for the streaming filter, from the threshold pair (key, idx).
@@ -599,7 +711,25 @@ __device__ __forceinline__ void filter_thresholds(Thr t, uint32_t& mode, uint32_
   }
 }
 
+// LDS layout shared by both kernels (32-bit words): key[cap] idx[cap] tkey[k4] tidx[k4]
+// hist[3*kBins], with cap = k + B2 + B and k4 = k, both rounded up to multiples of 4.
+__host__ __device__ constexpr uint32_t round4(uint32_t v) { return (v + 3u) & ~3u; }
+
+__device__ __forceinline__ Cand cand_layout(uint32_t* lds, uint32_t k, uint32_t B2, uint32_t B, uint32_t*& hist3) {
+  const uint32_t cap = round4(k + B2 + B), k4 = round4(k);
+  Cand c;
+  c.key = lds;
+  c.idx = lds + cap;
+  c.tkey = lds + 2 * cap;
+  c.tidx = lds + 2 * cap + k4;
+  hist3 = lds + 2 * cap + 2 * k4;
+  return c;
+}
+
 // --------------------------------------------------------------------------- select kernel
+// Byte offset past every buffer range: a load there returns zeros and reads no memory.
+constexpr uint32_t kNoLoad = 0x7FFFFFF0u;
+
 template <int DT, int WAVES, int CPW, int PD>
 __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   constexpr uint32_t NT = WAVES * 64;
@@ -608,7 +738,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   constexpr uint32_t CHUNK = 64 * VEC;
   constexpr uint32_t B = WAVES * CPW * CHUNK;
 
-  extern __shared__ __attribute__((aligned(16))) uint2 lds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   __shared__ Scalars sc;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
@@ -621,16 +751,14 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   const uint32_t B2 = static_cast<uint32_t>(p.slack);
   const bool stats = p.stats != nullptr;
 
-  uint2* const surv0 = lds;
-  uint2* const surv1 = lds + k;
-  uint2* const app_warm = lds + k;
-  uint2* const app_main = lds + 2 * k;
-  uint32_t* const hist3 = reinterpret_cast<uint32_t*>(lds + ((2 * k + B2 + B + 1u) & ~1u));  // 16-byte aligned
+  uint32_t* hist3;
+  const Cand c = cand_layout(lds, k, B2, B, hist3);
 
   for (uint32_t i = tid; i < 3u * kBins; i += NT) hist3[i] = 0;
   if (tid == 0) {
     sc.app_count = 0;
     sc.outpos = 0;
+    sc.listpos = 0;
     sc.reads = 0;
     sc.index_sum = 0;
   }
@@ -645,145 +773,150 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   ord.init(p.seed, row, slice, m);
 
   // threshold state (uniform across the workgroup)
-  uint32_t mode = 0, thr_s = 0, thr_n = 0, t_idx = 0;
-  uint64_t thr_c = 0, maxc = 0;
-  uint32_t nsurv = 0, cur = 0, napp = 0, hctr = 0;
+  uint32_t mode = 0, thr_s = 0, thr_n = 0;
+  uint32_t t_key = 0, t_idx = 0, maxkey = 0;
+  uint32_t nsurv = 0, napp = 0, hctr = 0;
   // counters (thread-uniform; used when stats are requested)
   uint64_t st_a = 0, st_r = 0, st_w = 0, st_max = 0, st_mono = 1, my_reads = 0, my_jsum = 0;
+  uint64_t t_start = stats ? wall_clock64() : 0, t_compact = 0, t_sync = 0, t_mark = 0;
 
-  u32x4 ring[PD][CPW];
-  uint32_t bids[PD];
+  // Two-stage pipeline: at the top of block i the wave takes block i's chunks (loaded during
+  // block i-1) and at once issues the loads of block i+1, which stay in flight through the
+  // filter, the barrier and any compaction. Past the last block the loads go to kNoLoad.
+  u32x4 next[CPW];
+  uint32_t next_bid = ord.at(0);
 #pragma unroll
-  for (uint32_t d = 0; d < PD; ++d) {
-    if (d < m) {
-      const uint32_t b = ord.at(d);
-      bids[d] = b;
+  for (uint32_t t = 0; t < CPW; ++t) next[t] = load16(rs, (next_bid * B + (wave + t * WAVES) * CHUNK + lane * VEC) * EB);
+  lds_sync();
+
+  for (uint32_t i = 0; i < m; ++i) {
+    u32x4 cur[CPW];
+#pragma unroll
+    for (uint32_t t = 0; t < CPW; ++t) cur[t] = next[t];
+    const uint32_t bid = next_bid;
+    {
+      const bool live = i + 1 < m;
+      next_bid = live ? ord.at(i + 1) : 0u;
 #pragma unroll
       for (uint32_t t = 0; t < CPW; ++t)
-        ring[d][t] = load16(rs, (b * B + (wave + t * WAVES) * CHUNK + lane * VEC) * EB);
+        next[t] = load16(rs, live ? (next_bid * B + (wave + t * WAVES) * CHUNK + lane * VEC) * EB : kNoLoad);
     }
-  }
-  lds_sync();
+    const uint32_t blk_lo = bid * B;
+    const bool strict = slice_lo + blk_lo > t_idx;
+    const uint32_t thr = strict ? thr_s : thr_n;
 
-  for (uint32_t i0 = 0; i0 < m; i0 += PD) {
+    // ---- filter: scores (bf16 elements in the high half) and hit masks
+    uint32_t s[CPW][VEC];
+    bool h[CPW][VEC];
 #pragma unroll
-    for (uint32_t d = 0; d < PD; ++d) {
-      const uint32_t i = i0 + d;
-      if (i >= m) break;
-      const uint32_t bid = bids[d];
-      u32x4 v[CPW];
+    for (uint32_t t = 0; t < CPW; ++t) {
+      if constexpr (DT == DS_BF16) {
 #pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t) v[t] = ring[d][t];
-      if (i + PD < m) {
-        const uint32_t nb = ord.at(i + PD);
-        bids[d] = nb;
+        for (uint32_t q = 0; q < 4; ++q) {
+          s[t][2 * q] = cur[t][q] << 16;
+          s[t][2 * q + 1] = cur[t][q];
+        }
+      } else {
 #pragma unroll
-        for (uint32_t t = 0; t < CPW; ++t)
-          ring[d][t] = load16(rs, (nb * B + (wave + t * WAVES) * CHUNK + lane * VEC) * EB);
+        for (uint32_t q = 0; q < 4; ++q) s[t][q] = cur[t][q];
       }
+    }
+    if (mode == 1) {
+#pragma unroll
+      for (uint32_t t = 0; t < CPW; ++t)
+#pragma unroll
+        for (uint32_t e = 0; e < VEC; ++e) h[t][e] = static_cast<int32_t>(s[t][e]) > static_cast<int32_t>(thr);
+    } else if (mode == 2) {
+#pragma unroll
+      for (uint32_t t = 0; t < CPW; ++t)
+#pragma unroll
+        for (uint32_t e = 0; e < VEC; ++e) h[t][e] = s[t][e] < thr;
+    } else {
+#pragma unroll
+      for (uint32_t t = 0; t < CPW; ++t)
+#pragma unroll
+        for (uint32_t e = 0; e < VEC; ++e) h[t][e] = true;
+    }
+    uint64_t mk[CPW][VEC];
+    uint32_t tot = 0;
+#pragma unroll
+    for (uint32_t t = 0; t < CPW; ++t) {
+      const uint32_t off = blk_lo + (wave + t * WAVES) * CHUNK;
+      uint32_t nval = VEC;
+      if (off + CHUNK > len) {  // the slice's tail chunk: only [0, len) is valid
+        const uint32_t first = off + lane * VEC;
+        nval = first >= len ? 0u : min(VEC, len - first);
+#pragma unroll
+        for (uint32_t e = 0; e < VEC; ++e) h[t][e] = h[t][e] && e < nval;
+      }
+      if (stats) {
+        const uint64_t j0 = slice_lo + off + lane * VEC;
+        my_reads += nval;
+        my_jsum += nval * j0 + (static_cast<uint64_t>(nval) * (nval - 1)) / 2;
+      }
+#pragma unroll
+      for (uint32_t e = 0; e < VEC; ++e) {
+        mk[t][e] = ballot(h[t][e]);
+        tot += popc(mk[t][e]);
+      }
+    }
 
-      // ---- filter: hit masks for every element slot of every chunk of this wave
-      const uint32_t blk_lo = bid * B;
-      const bool strict = slice_lo + blk_lo > t_idx;
-      const uint32_t thr = strict ? thr_s : thr_n;
-      uint32_t s[CPW][VEC];
-      bool h[CPW][VEC];
-      uint64_t mk[CPW][VEC];
-      uint32_t tot = 0;
+    // ---- append: one reservation per wave per block
+    uint32_t pos = 0;
+    if (lane == 0) pos = atomicAdd(&sc.app_count, tot);
+    pos = uni(pos);
+    if (lane == 0) sc.slot[i & 1u][wave] = pos + tot;
+    if (tot) {
+      pos += nsurv;
 #pragma unroll
       for (uint32_t t = 0; t < CPW; ++t) {
-        const uint32_t off = blk_lo + (wave + t * WAVES) * CHUNK;
-        if constexpr (DT == DS_BF16) {
-#pragma unroll
-          for (uint32_t q = 0; q < 4; ++q) {
-            s[t][2 * q] = v[t][q] << 16;
-            s[t][2 * q + 1] = v[t][q];
-          }
-        } else {
-#pragma unroll
-          for (uint32_t q = 0; q < 4; ++q) s[t][q] = v[t][q];
-        }
+        const uint32_t jl = slice_lo + blk_lo + (wave + t * WAVES) * CHUNK + lane * VEC;
 #pragma unroll
         for (uint32_t e = 0; e < VEC; ++e) {
-          h[t][e] = mode == 0 ? true
-                    : mode == 1 ? static_cast<int32_t>(s[t][e]) > static_cast<int32_t>(thr)
-                                : s[t][e] < thr;
-        }
-        uint32_t nval = VEC;
-        if (off + CHUNK > len) {  // the slice's tail chunk: only [0, len) is valid
-          const uint32_t first = off + lane * VEC;
-          nval = first >= len ? 0u : min(VEC, len - first);
-#pragma unroll
-          for (uint32_t e = 0; e < VEC; ++e) h[t][e] = h[t][e] && e < nval;
-        }
-        if (stats) {
-          const uint64_t j0 = slice_lo + off + lane * VEC;
-          my_reads += nval;
-          my_jsum += nval * j0 + (static_cast<uint64_t>(nval) * (nval - 1)) / 2;
-        }
-#pragma unroll
-        for (uint32_t e = 0; e < VEC; ++e) {
-          mk[t][e] = ballot(h[t][e]);
-          tot += popc(mk[t][e]);
-        }
-      }
-
-      // ---- append: one reservation per wave per block
-      uint32_t pos = 0;
-      if (lane == 0) pos = atomicAdd(&sc.app_count, tot);
-      pos = uni(pos);
-      if (lane == 0) sc.slot[i & 1u][wave] = pos + tot;
-      if (tot) {
-        uint2* const app = nsurv ? app_main : app_warm;
-#pragma unroll
-        for (uint32_t t = 0; t < CPW; ++t) {
-          const uint32_t jl = slice_lo + blk_lo + (wave + t * WAVES) * CHUNK + lane * VEC;
-#pragma unroll
-          for (uint32_t e = 0; e < VEC; ++e) {
-            if (mk[t][e]) {
-              const uint32_t q = mbcnt(mk[t][e], pos);
-              if (h[t][e]) app[q] = make_uint2(s[t][e], jl + e);
-              pos += popc(mk[t][e]);
+          if (mk[t][e]) {
+            const uint32_t q = mbcnt(mk[t][e], pos);
+            if (h[t][e]) {
+              c.key[q] = s[t][e];
+              c.idx[q] = jl + e;
             }
+            pos += popc(mk[t][e]);
           }
         }
       }
-      lds_sync();
+    }
+    if (stats) t_mark = wall_clock64();
+    lds_sync();
+    if (stats) t_sync += wall_clock64() - t_mark;
 
-      // ---- compaction test after the whole block
-      uint32_t cnt = 0;
+    // ---- compaction test after the whole block
+    uint32_t cnt = 0;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) cnt = max(cnt, sc.slot[i & 1u][w]);
-      napp = cnt;
-      st_max = max(st_max, static_cast<uint64_t>(nsurv + napp));
-      if (nsurv + napp >= k + B2) {
-        uint2* const sout = nsurv ? (cur ? surv0 : surv1) : surv0;
-        const uint2* const sin = cur ? surv1 : surv0;
-        const uint64_t prev_c = thr_c;
-        compact<DT, WAVES, true>(sin, nsurv, nsurv ? app_main : app_warm, napp, sout, k, sc, hist3, hctr, thr_c,
-                                 maxc);
-        st_a += napp;
-        st_w += nsurv + napp;
-        st_r += 1;
-        if (thr_c < prev_c) st_mono = 0;
-        cur = nsurv ? (cur ^ 1u) : 0u;
-        nsurv = k;
-        napp = 0;
-        t_idx = ~static_cast<uint32_t>(thr_c);
-        filter_thresholds<DT>(Thr{static_cast<uint32_t>(thr_c >> 32), t_idx}, mode, thr_s, thr_n);
-      }
+    for (int w = 0; w < WAVES; ++w) cnt = max(cnt, sc.slot[i & 1u][w]);
+    napp = cnt;
+    st_max = max(st_max, static_cast<uint64_t>(nsurv + napp));
+    if (nsurv + napp >= k + B2) {
+      const uint64_t prev_c = comp_of(t_key, t_idx);
+      const bool first = nsurv == 0;
+      if (stats) t_mark = wall_clock64();
+      compact<DT, WAVES, true>(c, nsurv + napp, nsurv, k, false, slice_lo, slice_lo + len - 1u, sc, hist3, hctr,
+                               t_key, t_idx, maxkey);
+      if (stats) t_compact += wall_clock64() - t_mark;
+      st_a += napp;
+      st_w += nsurv + napp;
+      st_r += 1;
+      if (!first && comp_of(t_key, t_idx) < prev_c) st_mono = 0;
+      nsurv = k;
+      napp = 0;
+      filter_thresholds<DT>(Thr{t_key, t_idx}, mode, thr_s, thr_n);
     }
   }
 
-  // ---- final compaction
-  uint2* const fin = nsurv ? (cur ? surv0 : surv1) : surv0;
-  {
-    const uint2* const sin = cur ? surv1 : surv0;
-    compact<DT, WAVES, true>(sin, nsurv, nsurv ? app_main : app_warm, napp, fin, k, sc, hist3, hctr, thr_c, maxc);
-    st_a += napp;
-    st_w += nsurv + napp;
-  }
-  lds_sync();
+  // ---- final compaction: survivors to (tkey, tidx)
+  const uint64_t t_final0 = stats ? wall_clock64() : 0;
+  compact<DT, WAVES, true>(c, nsurv + napp, nsurv, k, true, slice_lo, slice_lo + len - 1u, sc, hist3, hctr, t_key,
+                           t_idx, maxkey);
+  st_a += napp;
+  st_w += nsurv + napp;
 
   if (stats) {
     for (uint32_t o = 32; o > 0; o >>= 1) {
@@ -808,15 +941,22 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
       o->slice_len = len;
       o->block = B;
       o->slack = B2;
+      o->t_compact_ns = t_compact * 10;
+      o->t_sync_ns = t_sync * 10;
       o->reserved = 0;
     }
   }
 
   if (p.slices == 1) {
-    sort_and_store<DT, WAVES>(reinterpret_cast<uint64_t*>(app_main), fin, k, p.out_vals, p.out_idx, row);
+    sort_and_store<DT, WAVES>(reinterpret_cast<uint64_t*>(c.key), c.tkey, c.tidx, k, p.out_vals, p.out_idx, row);
   } else {
     uint2* const dst = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + static_cast<uint64_t>(slice) * k;
-    for (uint32_t i = tid; i < k; i += NT) dst[i] = fin[i];
+    for (uint32_t i = tid; i < k; i += NT) dst[i] = make_uint2(c.tkey[i], c.tidx[i]);
+  }
+  if (stats && tid == 0) {
+    const uint64_t t_end = wall_clock64();
+    p.stats[blockIdx.x].t_total_ns = (t_end - t_start) * 10;
+    p.stats[blockIdx.x].t_final_ns = (t_end - t_final0) * 10;
   }
 }
 
@@ -829,7 +969,7 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   constexpr uint32_t CHUNK = 128;  // entries per wave load
   constexpr uint32_t B = WAVES * CPW * CHUNK;
 
-  extern __shared__ __attribute__((aligned(16))) uint2 lds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   __shared__ Scalars sc;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
@@ -839,16 +979,13 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   const uint32_t k = static_cast<uint32_t>(p.k);
   const uint32_t B2 = static_cast<uint32_t>(p.slack);
 
-  uint2* const surv0 = lds;
-  uint2* const surv1 = lds + k;
-  uint2* const app_warm = lds + k;
-  uint2* const app_main = lds + 2 * k;
-  uint32_t* const hist3 = reinterpret_cast<uint32_t*>(lds + ((2 * k + B2 + B + 1u) & ~1u));  // 16-byte aligned
-
+  uint32_t* hist3;
+  const Cand c = cand_layout(lds, k, B2, B, hist3);
   for (uint32_t i = tid; i < 3u * kBins; i += NT) hist3[i] = 0;
   if (tid == 0) {
     sc.app_count = 0;
     sc.outpos = 0;
+    sc.listpos = 0;
   }
   const uint2* base = p.ws + static_cast<uint64_t>(row) * p.row_entries;  // rows padded to 16 bytes
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -857,98 +994,80 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   ord.init(p.seed, row, 0x7FFFFFFFu, m);
 
   bool accept_all = true;
-  uint64_t thr_c = 0, maxc = 0;
-  Thr thr{0, 0};
-  uint32_t nsurv = 0, cur = 0, napp = 0, hctr = 0;
+  uint32_t t_key = 0, t_idx = 0, maxkey = 0;
+  uint32_t nsurv = 0, napp = 0, hctr = 0;
 
-  u32x4 ring[PD][CPW];
-  uint32_t bids[PD];
+  u32x4 next[CPW];
+  uint32_t next_bid = ord.at(0);
 #pragma unroll
-  for (uint32_t d = 0; d < PD; ++d) {
-    if (d < m) {
-      const uint32_t b = ord.at(d);
-      bids[d] = b;
-#pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t) ring[d][t] = load16(rs, (b * B + (wave + t * WAVES) * CHUNK + lane * 2) * 8u);
-    }
-  }
+  for (uint32_t t = 0; t < CPW; ++t) next[t] = load16(rs, (next_bid * B + (wave + t * WAVES) * CHUNK + lane * 2) * 8u);
   lds_sync();
 
-  for (uint32_t i0 = 0; i0 < m; i0 += PD) {
+  for (uint32_t i = 0; i < m; ++i) {
+    u32x4 v[CPW];
 #pragma unroll
-    for (uint32_t d = 0; d < PD; ++d) {
-      const uint32_t i = i0 + d;
-      if (i >= m) break;
-      const uint32_t bid = bids[d];
-      u32x4 v[CPW];
+    for (uint32_t t = 0; t < CPW; ++t) v[t] = next[t];
+    const uint32_t bid = next_bid;
+    {
+      const bool live = i + 1 < m;
+      next_bid = live ? ord.at(i + 1) : 0u;
 #pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t) v[t] = ring[d][t];
-      if (i + PD < m) {
-        const uint32_t nb = ord.at(i + PD);
-        bids[d] = nb;
+      for (uint32_t t = 0; t < CPW; ++t)
+        next[t] = load16(rs, live ? (next_bid * B + (wave + t * WAVES) * CHUNK + lane * 2) * 8u : kNoLoad);
+    }
+    const uint32_t blk_lo = bid * B;
+    bool h[CPW][2];
+    uint64_t mk[CPW][2];
+    uint32_t tot = 0;
 #pragma unroll
-        for (uint32_t t = 0; t < CPW; ++t)
-          ring[d][t] = load16(rs, (nb * B + (wave + t * WAVES) * CHUNK + lane * 2) * 8u);
+    for (uint32_t t = 0; t < CPW; ++t) {
+      const uint32_t first = blk_lo + (wave + t * WAVES) * CHUNK + lane * 2;
+#pragma unroll
+      for (uint32_t e = 0; e < 2; ++e) {
+        const uint32_t key = v[t][2 * e], idx = v[t][2 * e + 1];
+        const bool beats = accept_all || key > t_key || (key == t_key && idx < t_idx);
+        h[t][e] = beats && first + e < len;
+        mk[t][e] = ballot(h[t][e]);
+        tot += popc(mk[t][e]);
       }
-      const uint32_t blk_lo = bid * B;
-      bool h[CPW][2];
-      uint64_t mk[CPW][2];
-      uint32_t tot = 0;
+    }
+    uint32_t pos = 0;
+    if (lane == 0) pos = atomicAdd(&sc.app_count, tot);
+    pos = uni(pos);
+    if (lane == 0) sc.slot[i & 1u][wave] = pos + tot;
+    if (tot) {
+      pos += nsurv;
 #pragma unroll
       for (uint32_t t = 0; t < CPW; ++t) {
-        const uint32_t first = blk_lo + (wave + t * WAVES) * CHUNK + lane * 2;
 #pragma unroll
         for (uint32_t e = 0; e < 2; ++e) {
-          const uint32_t key = v[t][2 * e], idx = v[t][2 * e + 1];
-          const bool beats = accept_all || key > thr.key || (key == thr.key && idx < thr.idx);
-          h[t][e] = beats && first + e < len;
-          mk[t][e] = ballot(h[t][e]);
-          tot += popc(mk[t][e]);
-        }
-      }
-      uint32_t pos = 0;
-      if (lane == 0) pos = atomicAdd(&sc.app_count, tot);
-      pos = uni(pos);
-      if (lane == 0) sc.slot[i & 1u][wave] = pos + tot;
-      if (tot) {
-        uint2* const app = nsurv ? app_main : app_warm;
-#pragma unroll
-        for (uint32_t t = 0; t < CPW; ++t) {
-#pragma unroll
-          for (uint32_t e = 0; e < 2; ++e) {
-            if (mk[t][e]) {
-              const uint32_t q = mbcnt(mk[t][e], pos);
-              if (h[t][e]) app[q] = make_uint2(v[t][2 * e], v[t][2 * e + 1]);
-              pos += popc(mk[t][e]);
+          if (mk[t][e]) {
+            const uint32_t q = mbcnt(mk[t][e], pos);
+            if (h[t][e]) {
+              c.key[q] = v[t][2 * e];
+              c.idx[q] = v[t][2 * e + 1];
             }
+            pos += popc(mk[t][e]);
           }
         }
       }
-      lds_sync();
-      uint32_t cnt = 0;
+    }
+    lds_sync();
+    uint32_t cnt = 0;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) cnt = max(cnt, sc.slot[i & 1u][w]);
-      napp = cnt;
-      if (nsurv + napp >= k + B2) {
-        uint2* const sout = nsurv ? (cur ? surv0 : surv1) : surv0;
-        const uint2* const sin = cur ? surv1 : surv0;
-        compact<DT, WAVES, false>(sin, nsurv, nsurv ? app_main : app_warm, napp, sout, k, sc, hist3, hctr, thr_c,
-                                  maxc);
-        thr = Thr{static_cast<uint32_t>(thr_c >> 32), ~static_cast<uint32_t>(thr_c)};
-        accept_all = false;
-        cur = nsurv ? (cur ^ 1u) : 0u;
-        nsurv = k;
-        napp = 0;
-      }
+    for (int w = 0; w < WAVES; ++w) cnt = max(cnt, sc.slot[i & 1u][w]);
+    napp = cnt;
+    if (nsurv + napp >= k + B2) {
+      compact<DT, WAVES, false>(c, nsurv + napp, nsurv, k, false, 0u, static_cast<uint32_t>(p.n - 1), sc, hist3,
+                                hctr, t_key, t_idx, maxkey);
+      accept_all = false;
+      nsurv = k;
+      napp = 0;
     }
   }
-  uint2* const fin = nsurv ? (cur ? surv0 : surv1) : surv0;
-  {
-    const uint2* const sin = cur ? surv1 : surv0;
-    compact<DT, WAVES, false>(sin, nsurv, nsurv ? app_main : app_warm, napp, fin, k, sc, hist3, hctr, thr_c, maxc);
-  }
-  lds_sync();
-  sort_and_store<DT, WAVES>(reinterpret_cast<uint64_t*>(app_main), fin, k, p.out_vals, p.out_idx, row);
+  compact<DT, WAVES, false>(c, nsurv + napp, nsurv, k, true, 0u, static_cast<uint32_t>(p.n - 1), sc, hist3, hctr,
+                            t_key, t_idx, maxkey);
+  sort_and_store<DT, WAVES>(reinterpret_cast<uint64_t*>(c.key), c.tkey, c.tidx, k, p.out_vals, p.out_idx, row);
 }
 
 // --------------------------------------------------------------------------- probes
@@ -1000,7 +1119,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(u32x4* dst, c
 }
 
 // prefetch ring depth: about eight 1 KiB wave chunks in flight per wave
-constexpr int ring_depth(int cpw) { return cpw >= 4 ? 2 : (cpw == 2 ? 4 : 8); }
+constexpr int ring_depth(int cpw) { return cpw > 0 ? 1 : 1; }  // one block in flight per wave (two-stage pipeline)
 
 template <int DT, int W, int C>
 hipError_t launch_select_shape(const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream) {
@@ -1024,6 +1143,8 @@ hipError_t launch_select_dt(int shape, const SelectParams& p, int64_t rows, size
     case 4: return launch_select_shape<DT, 8, 2>(p, rows, lds, s);
     case 5: return launch_select_shape<DT, 4, 4>(p, rows, lds, s);
     case 6: return launch_select_shape<DT, 8, 4>(p, rows, lds, s);
+    case 7: return launch_select_shape<DT, 16, 1>(p, rows, lds, s);
+    case 8: return launch_select_shape<DT, 16, 2>(p, rows, lds, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1045,7 +1166,8 @@ hipError_t launch_merge_dt(const MergeParams& p, int64_t rows, size_t lds, hipSt
 
 size_t select_lds_bytes(int k, int block, int slack, int waves) {
   (void)waves;
-  return (static_cast<size_t>(2) * k + slack + block + 1) * 8 + 3 * kBins * 4 + sizeof(Scalars);
+  const size_t cap = round4(static_cast<uint32_t>(k + slack + block)), k4 = round4(static_cast<uint32_t>(k));
+  return (2 * cap + 2 * k4 + 3 * kBins) * 4 + sizeof(Scalars);
 }
 
 hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,
