@@ -16,6 +16,11 @@ constexpr int64_t kMaxLdsBytes = 160 * 1024;    // LDS per workgroup on gfx950
 constexpr int64_t kMaxSliceBytes = 0x7FFFFF00;  // buffer offsets are 31-bit
 constexpr int kChunkBf16 = 512, kChunkFp32 = 256;
 constexpr int kMergeBlock = ds::kMergeShape.waves * ds::kMergeShape.cpw * 128;
+constexpr int kDefaultSlack = 2048;  // B2 when not forced (at least k)
+// default select shapes (indices into kSelectShapes), best first
+constexpr int kDefaultFp32[] = {8, 7, 2, 1};  // 16x2 (B=8192), 16x1 (4096), 4x2 (2048), 4x1 (1024)
+constexpr int kDefaultBf16[] = {7, 3, 1, 0};  // 16x1 (B=8192), 8x1 (4096), 4x1 (2048), 2x1 (1024)
+constexpr int kNumDefaults = 4;
 
 int elem_bytes(int dtype) { return dtype == DS_BF16 ? 2 : 4; }
 int chunk_elems(int dtype) { return dtype == DS_BF16 ? kChunkBf16 : kChunkFp32; }
@@ -73,33 +78,62 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   const int chunk = chunk_elems(dtype);
   const int eb = elem_bytes(dtype);
 
-  // kernel shape: the forced block/waves, else the default per element type
-  int shape = -1;
+  // kernel shape: the forced block/waves, else the default per element type (16 waves and
+  // B = 8192, measured best on MI355X for k = 512), stepping down to smaller blocks when the
+  // candidate buffer would not fit in LDS
+  const int sort_cap = pow2_at_least(k);
+  int shape = -1, block = 0, slack = 0;
+  size_t lds = 0;
+  auto fit = [&](int s) -> bool {
+    const int b = kSelectShapes[s].waves * kSelectShapes[s].cpw * chunk;
+    int sl = c.slack ? c.slack : std::max(k, kDefaultSlack);
+    if (sl + b < sort_cap) {
+      if (c.slack) return false;  // the final sort runs in the append region
+      sl = sort_cap - b;
+    }
+    const size_t l = ds::select_lds_bytes(k, b, sl, kSelectShapes[s].waves);
+    if (static_cast<int64_t>(l) > kMaxLdsBytes) return false;
+    shape = s;
+    block = b;
+    slack = sl;
+    lds = l;
+    return true;
+  };
   if (c.block || c.waves) {
-    for (int s = 0; s < kNumSelectShapes; ++s) {
+    for (int s = 0; s < kNumSelectShapes && shape < 0; ++s) {
       const int b = kSelectShapes[s].waves * kSelectShapes[s].cpw * chunk;
       if (c.block && b != c.block) continue;
       if (c.waves && kSelectShapes[s].waves != c.waves) continue;
-      if (shape < 0 || (!c.waves && kSelectShapes[s].waves == 4)) shape = s;
+      if (!c.waves && kSelectShapes[s].waves != 4) continue;  // a forced block alone prefers 4 waves
+      fit(s);
+    }
+    for (int s = 0; s < kNumSelectShapes && shape < 0; ++s) {
+      const int b = kSelectShapes[s].waves * kSelectShapes[s].cpw * chunk;
+      if (c.block && b != c.block) continue;
+      if (c.waves && kSelectShapes[s].waves != c.waves) continue;
+      fit(s);
     }
     if (shape < 0) return DS_ERR_UNSUPPORTED;
   } else {
-    shape = dtype == DS_BF16 ? 1 : 2;  // bf16: 4 waves x 1 chunk (B=2048); fp32: 4 x 2 (B=2048)
-  }
-  const int block = kSelectShapes[shape].waves * kSelectShapes[shape].cpw * chunk;
-  const int sort_cap = pow2_at_least(k);
-  int slack = c.slack ? c.slack : (k > block ? k : block);
-  if (slack + block < sort_cap) {
-    if (c.slack) return DS_ERR_UNSUPPORTED;  // the final sort runs in the append region
-    slack = sort_cap - block;
+    // the largest default block that is not longer than a slice (the whole row when the
+    // slice count is automatic), else the smallest that fits
+    const int* order = dtype == DS_BF16 ? kDefaultBf16 : kDefaultFp32;
+    const int64_t cap = c.slices ? (n + c.slices - 1) / c.slices : n;
+    for (int i = 0; i < kNumDefaults && shape < 0; ++i) {
+      const int s = order[i];
+      if (kSelectShapes[s].waves * kSelectShapes[s].cpw * chunk <= cap) fit(s);
+    }
+    for (int i = kNumDefaults - 1; i >= 0 && shape < 0; --i) fit(order[i]);
+    if (shape < 0) return DS_ERR_UNSUPPORTED;
   }
 
-  // slices: enough workgroups to fill the device twice, each slice at least 4 blocks and 8k
+  // slices: about one workgroup per compute unit, each slice at least 4 blocks and 8k
   int64_t slices;
   if (c.slices) {
     slices = c.slices;
   } else {
-    const int64_t want = cus > 0 ? (2 * static_cast<int64_t>(cus) + (rows > 0 ? rows : 1) - 1) / (rows > 0 ? rows : 1) : 1;
+    const int64_t r = rows > 0 ? rows : 1;
+    const int64_t want = cus > 0 ? (static_cast<int64_t>(cus) + r - 1) / r : 1;
     const int64_t min_len = std::max<int64_t>(4 * static_cast<int64_t>(block), 8 * static_cast<int64_t>(k));
     const int64_t most = std::max<int64_t>(1, n / min_len);
     slices = std::max<int64_t>(1, std::min(want, most));
@@ -115,9 +149,6 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   slices = (n + slice_len - 1) / slice_len;
   if (c.slices && slices != c.slices) return DS_ERR_UNSUPPORTED;  // forced count leaves an empty slice
   if (rows * slices > INT32_MAX) return DS_ERR_UNSUPPORTED;
-
-  const size_t lds = ds::select_lds_bytes(k, block, slack, kSelectShapes[shape].waves);
-  if (static_cast<int64_t>(lds) > kMaxLdsBytes) return DS_ERR_UNSUPPORTED;
 
   Plan p{};
   p.dtype = dtype;

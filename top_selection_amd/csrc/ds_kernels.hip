@@ -14,19 +14,23 @@
 // composite (key << 32) | ~index, so every comparison is an integer comparison.
 //
 // MI355X mapping:
-//  * one workgroup (2-8 waves) per (row, slice); every lane streams 16-byte raw buffer
-//    loads, one wave covers 1 KiB per chunk, and each wave keeps a ring of chunks in
-//    flight that runs ahead across block boundaries and across compactions;
-//  * the filter compares raw bit patterns against a per-block integer threshold (no
-//    key transform and no float compare on the streaming path); the per-element hit
-//    masks become 64-lane SGPR masks, positions come from mbcnt, and one LDS atomic per
-//    wave per block reserves buffer space;
+//  * one workgroup (2-16 waves) per (row, slice); every lane streams 16-byte raw buffer
+//    loads (1 KiB per wave per chunk). Each wave keeps D blocks in flight (D buffers of
+//    registers): block i+D is loaded into the registers of block i as soon as block i has
+//    been filtered, so loads stay in flight through the block barrier and any compaction.
+//    The block order is a table in LDS, computed once per workgroup;
+//  * the filter compares raw bit patterns against a per-block integer threshold; hit masks
+//    are 64-lane SGPR masks, positions come from mbcnt, and one LDS atomic per wave and chunk
+//    reserves buffer space. Hits are stored raw; the compaction's first pass turns them
+//    into keys;
 //  * barriers are LDS-only (s_barrier with workgroup/local fences), so in-flight global
 //    loads are never drained by a barrier;
-//  * the compaction is an LDS radix select over the composite with 8-bit digits placed
-//    below the common prefix of the buffer (found by a wave OR/AND reduction), a
-//    triple-buffered histogram, and a per-wave redundant bin scan, so one barrier is
-//    needed per digit; survivors ping-pong between two k-entry segments.
+//  * the compaction is an LDS radix select with 2048-bin histograms over an adaptive key
+//    window [T, previous maximum]: all waves count (survivors from the last thread down,
+//    appended entries from the first up), one wave scans the bins and publishes the pivot
+//    bin, and in the usual case one or two passes leave at most 64 pivot-bin entries, which
+//    one wave ranks with lane reads. Survivors alternate between two k-entry sets, so
+//    nothing is copied back; appends always go to the region after the survivor set A.
 #include "ds_internal.h"
 
 namespace ds {
@@ -60,14 +64,18 @@ __device__ __forceinline__ uint32_t popc(uint64_t m) { return static_cast<uint32
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Value held by lane (lane ^ m), m a power of two below 64. Lane mappings (checked on
-// gfx950): quad_perm 0xB1 / 0x4E swap neighbours at distance 1 / 2, row_ror:8 swaps the
-// halves of a 16-lane row, ds_swizzle in bit-mask mode xors the lane id within 32 lanes,
-// and the permlane16/32 swaps exchange 16-lane rows / 32-lane halves.
+// gfx950): quad_perm 0xB1 / 0x4E swap neighbours at distance 1 / 2, row_shl:4 / row_shr:4
+// bring the lane four above / below within a 16-lane row, row_ror:8 swaps the halves of a
+// row, and the permlane16/32 swaps exchange 16-lane rows / 32-lane halves.
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v, uint32_t m, uint32_t lane) {
   switch (m) {
     case 1: return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);
     case 2: return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);
-    case 4: return __builtin_amdgcn_ds_swizzle(v, 0x1F | (4 << 10));
+    case 4: {
+      const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, 0x104, 0xF, 0xF, false);
+      const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);
+      return (lane & 4u) ? dn : up;
+    }
     case 8: return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xF, 0xF, false);
     case 16: {
       const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
@@ -104,6 +112,25 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, uint32_t l) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Maximum over the 64 lanes (the same row shifts and broadcasts as the scan, then lane 63).
+__device__ __forceinline__ uint32_t wave_max32(uint32_t x) {
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false)));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+__device__ __forceinline__ uint32_t u4get(const uint4& v, uint32_t q) {
+  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ uint32_t bitlen32(uint32_t v) {
+  return v ? 32u - static_cast<uint32_t>(__builtin_clz(v)) : 0u;
+}
+
 // --------------------------------------------------------------------------- keys
 // Order-preserving key of a raw element (bf16: the 16 bits in the low half).
 template <int DT>
@@ -117,6 +144,18 @@ __device__ __forceinline__ uint32_t key_of_raw(uint32_t raw) {
   }
 }
 
+// Order-preserving key of a streamed score without branches (bf16: the element in bits 16-31,
+// as the filter holds it).
+template <int DT>
+__device__ __forceinline__ uint32_t key_of_score(uint32_t s) {
+  if constexpr (DT == DS_BF16) {
+    const uint32_t r = s >> 16;
+    return (r ^ (static_cast<uint32_t>(static_cast<int32_t>(s) >> 31) | 0x8000u)) & 0xFFFFu;
+  } else {
+    return s ^ (static_cast<uint32_t>(static_cast<int32_t>(s) >> 31) | 0x80000000u);
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ uint32_t raw_of_key(uint32_t key) {
   if constexpr (DT == DS_BF16) {
@@ -124,6 +163,10 @@ __device__ __forceinline__ uint32_t raw_of_key(uint32_t key) {
   } else {
     return key ^ ((key & 0x80000000u) ? 0x80000000u : 0xFFFFFFFFu);
   }
+}
+
+__device__ __forceinline__ uint64_t comp_of(uint32_t key, uint32_t idx) {
+  return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~idx);
 }
 
 // --------------------------------------------------------------------------- block order
@@ -182,287 +225,205 @@ struct BlockOrder {
 
 // --------------------------------------------------------------------------- shared state
 constexpr int kMaxWaves = 16;
-constexpr uint32_t kBins = 512;      // histogram bins of one radix pass
-constexpr uint32_t kListCap = 64;    // pivot-bin entries resolved by one wave
+constexpr uint32_t kLogBins = 11;
+constexpr uint32_t kBins = 1u << kLogBins;  // histogram bins of one radix pass
+constexpr uint32_t kPer = kBins / 64;       // bins per lane in the bin scan
+constexpr uint32_t kListCap = 64;           // pivot-bin entries ranked with lane reads
+constexpr uint32_t kOrdCap = 1024;          // block-order table entries (longer streams compute it)
 
 struct Scalars {
-  uint32_t app_count;               // entries appended since the last compaction
-  uint32_t outpos;                  // scatter cursor of the running compaction
-  uint32_t listpos;                 // pivot-list cursor of the running compaction
-  uint32_t pad0;
-  uint32_t slot[2][kMaxWaves];      // per-wave end of its reservation, by block parity
-  uint32_t red[kMaxWaves][2];       // per-wave min / max keys
-  uint32_t scan[4];                 // bin scan result published by wave 0
-  uint32_t lkey[kListCap];          // pivot-bin entries
+  uint32_t blk[3];             // entries appended by block i, at blk[i % 3]
+  uint32_t outpos;             // scatter cursor of the running compaction
+  uint32_t listpos;            // pivot-list cursor of the running compaction
+  uint32_t pub[4];             // bin scan result: bin, entries above it, entries in it, max key
+  uint32_t red[kMaxWaves];     // per-wave maximum keys
+  uint32_t lkey[kListCap];     // pivot-bin entries
   uint32_t lidx[kListCap];
-  unsigned long long reads;         // counters (stats runs only)
-  unsigned long long index_sum;
+  // counters (stats runs only; thread 0 keeps them): appended A, compactions R, work W,
+  // largest buffer, threshold monotone, compaction time, block barrier time, start of the
+  // final compaction, elements read and the sum of their indices
+  unsigned long long st_a, st_r, st_w, st_max, st_mono, st_tc, st_ts, st_tf, reads, index_sum;
 };
 
-// Candidate buffer in LDS, keys and indices in separate arrays (16-byte aligned, capacity a
-// multiple of 4). Entries [0, nsurv) are survivors (keys), [nsurv, n) were appended since the
-// last compaction (raw element bits in the select kernel; bf16 in the high half). tkey/tidx
-// (k entries) receive the scattered survivors of a compaction.
-struct Cand {
-  uint32_t* key;
-  uint32_t* idx;
-  uint32_t* tkey;
-  uint32_t* tidx;
+__host__ __device__ constexpr uint32_t round4(uint32_t v) { return (v + 3u) & ~3u; }
+
+// Candidate buffer in LDS (32-bit words, every array 16-byte aligned), k4 = round4(k),
+// pc = round4(B2 + B):
+//   ck[k4 + pc], ci[k4 + pc]  keys / indices: survivor set A in [0, k4), appended entries
+//                             from k4 on (before the first compaction appends start at 0,
+//                             so k + B2 + B entries fit)
+//   bk[k4], bi[k4]            survivor set B
+//   hist[2 * kBins]           two histograms, used alternately
+//   ordt[kOrdCap]             the block order (block id of the i-th block read)
+// After the final compaction the append region (ck + k4, ci + k4: pc >= pow2(k) words
+// each) is the sort's exchange buffer.
+struct Lay {
+  uint32_t *ck, *ci, *bk, *bi, *hist, *ordt;
+  uint32_t k4, pc;
 };
 
-struct Thr {
-  uint32_t key, idx;
+__device__ __forceinline__ Lay lay_of(uint32_t* lds, uint32_t k, uint32_t B2, uint32_t B) {
+  Lay l;
+  l.k4 = round4(k);
+  l.pc = round4(B2 + B);
+  l.ck = lds;
+  l.ci = lds + (l.k4 + l.pc);
+  l.bk = lds + 2u * (l.k4 + l.pc);
+  l.bi = l.bk + l.k4;
+  l.hist = l.bi + l.k4;
+  l.ordt = l.hist + 2u * kBins;
+  return l;
+}
+
+// The entries of one compaction: survivors (n0, possibly none) and appended entries (n1),
+// each visited in groups of four (the slots up to a multiple of four exist; padding is skipped).
+struct Segs {
+  uint32_t *k0, *i0, *k1, *i1;
+  uint32_t n0, n1;
 };
 
-__device__ __forceinline__ uint64_t comp_of(uint32_t key, uint32_t idx) {
-  return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~idx);
+__device__ __forceinline__ Segs make_segs(uint32_t* k0, uint32_t* i0, uint32_t n0, uint32_t* k1, uint32_t* i1,
+                                          uint32_t n1) {
+  Segs s;
+  s.k0 = k0;
+  s.i0 = i0;
+  s.k1 = k1;
+  s.i1 = i1;
+  s.n0 = n0;
+  s.n1 = n1;
+  return s;
 }
 
-__device__ __forceinline__ uint32_t bitlen32(uint32_t v) { return v ? 32u - static_cast<uint32_t>(__builtin_clz(v)) : 0u; }
+// Word of histogram bin b: bits 2-4 of the index are xored with bits 5-7. Neighbouring bins
+// stay in neighbouring words (the counting atomics), and the 16-byte reads of the bin scan
+// (lane l reads the four-bin groups of bins [32*(63-l), 32*(64-l))) hit eight different bank
+// groups instead of one.
+__device__ __forceinline__ uint32_t hslot(uint32_t b) { return b ^ (((b >> 5) & 7u) << 2); }
 
-__device__ __forceinline__ uint32_t wave_max32(uint32_t v, uint32_t lane) {
-#pragma unroll
-  for (uint32_t m = 1; m < 64; m <<= 1) v = max(v, xor_lane(v, m, lane));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_min32(uint32_t v, uint32_t lane) {
-#pragma unroll
-  for (uint32_t m = 1; m < 64; m <<= 1) v = min(v, xor_lane(v, m, lane));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t u4get(const uint4& v, uint32_t q) {
-  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
-}
-
-// One wave scans a kBins-bin histogram from the top bin down and finds the bin that holds the
-// `need`-th best entry: `above` entries lie in higher bins, `cnt` in that bin.
+// One wave finds the bin of a kBins histogram (higher bin = better entries) that holds the
+// `need`-th best entry: `above` entries lie in higher bins and `cnt` in that bin. Lane l sums
+// the 32 bins of block 63 - l in groups of four; a wave scan finds the lane, the lane's group
+// sums find the group, and one broadcast read finds the bin. Counting the prefix sums below
+// `need` replaces searching, so the wave never diverges.
 __device__ __forceinline__ void scan_select(const uint32_t* h, uint32_t need, uint32_t lane, uint32_t& bin,
                                             uint32_t& above, uint32_t& cnt) {
-  constexpr uint32_t PER = kBins / 64;  // 8 bins per lane, lane 0 holds the highest
-  const uint32_t top = kBins - 1u - PER * lane;
-  const uint4 qa = *reinterpret_cast<const uint4*>(h + top - 7);
-  const uint4 qb = *reinterpret_cast<const uint4*>(h + top - 3);
-  const uint32_t c[PER] = {qb.w, qb.z, qb.y, qb.x, qa.w, qa.z, qa.y, qa.x};  // bins top, top-1, ...
+  constexpr uint32_t Q = kPer / 4;
+  const uint32_t hb = 63u - lane, sw = hb & 7u;
+  uint32_t gs[Q];  // gs[0]: the lane's highest four bins
   uint32_t s = 0;
 #pragma unroll
-  for (uint32_t i = 0; i < PER; ++i) s += c[i];
+  for (uint32_t j = 0; j < Q; ++j) {
+    const uint4 q = *reinterpret_cast<const uint4*>(h + 32u * hb + 4u * ((Q - 1u - j) ^ sw));
+    gs[j] = q.x + q.y + q.z + q.w;
+    s += gs[j];
+  }
   const uint32_t incl = wave_incl_scan(s);
   const uint64_t ge = ballot(incl >= need);
   const uint32_t src = ge ? static_cast<uint32_t>(__builtin_ctzll(ge)) : 63u;
-  uint32_t acc = incl - s, b = top - (PER - 1), a = acc, n = c[PER - 1];
-  bool found = false;
+  uint32_t acc = incl - s, gj = 0, gacc = incl - s;
 #pragma unroll
-  for (uint32_t i = 0; i < PER; ++i) {
-    if (!found && acc + c[i] >= need) {
-      found = true;
-      b = top - i;
-      a = acc;
-      n = c[i];
-    }
-    acc += c[i];
+  for (uint32_t j = 0; j < Q; ++j) {  // groups whose running total stays below need are passed
+    acc += gs[j];
+    const bool below = acc < need;
+    gj += below ? 1u : 0u;
+    gacc = below ? acc : gacc;
   }
-  bin = __builtin_amdgcn_readlane(b, src);
-  above = __builtin_amdgcn_readlane(a, src);
-  cnt = __builtin_amdgcn_readlane(n, src);
+  gj = __builtin_amdgcn_readlane(gj, src);
+  gacc = __builtin_amdgcn_readlane(gacc, src);
+  gj = gj < Q ? gj : Q - 1u;
+  const uint32_t hs = 63u - src;
+  const uint4 q = *reinterpret_cast<const uint4*>(h + 32u * hs + 4u * ((Q - 1u - gj) ^ (hs & 7u)));
+  const uint32_t c[4] = {q.w, q.z, q.y, q.x};  // the group's bins, highest first
+  uint32_t a = gacc, bi = 0, ab = gacc;
+#pragma unroll
+  for (uint32_t i = 0; i < 3; ++i) {
+    a += c[i];
+    const bool below = a < need;
+    bi += below ? 1u : 0u;
+    ab = below ? a : ab;
+  }
+  bin = 32u * hs + 4u * (Q - 1u - gj) + 3u - bi;
+  above = ab;
+  cnt = bi == 0 ? c[0] : bi == 1 ? c[1] : bi == 2 ? c[2] : c[3];
 }
 
 // Radix-select compaction.
 //
-// Reduces the n entries of the candidate buffer to the k best under the composite order
-// (key descending, then index ascending). In-loop calls (fin == false) leave the survivors in
-// entries [0, k) of the buffer and return the smallest of them as the new threshold
-// (tkey, tidx) and the largest key in maxkey; the final call (fin == true) leaves them in
-// tkey/tidx (padded with sentinels when n < k).
+// Reduces the entries of `sg` to the k best under the composite order (key descending, then
+// index ascending) and writes them, unordered, to (dk, di); when fewer than k entries exist
+// all of them are written followed by sentinels (key 0, index ~0) up to round4(k). In-loop
+// calls return the smallest survivor as the new threshold (tkey, tidx) and the largest key
+// seen in maxkey.
 //
-// Search: a kBins-bin histogram of (key - lo) >> shift over a key window [lo, hi] that holds
-// every entry locates the bin of the k-th best; while that bin holds more than kListCap
-// entries the window shrinks to it and the histogram repeats; a bin that is a single key
-// (ties) continues on the indices in [ilo, ihi] (smaller index first). Then the entries
-// above the pivot bin are scattered out, the bin's entries are gathered in a short list, and
-// the list is ranked to pick the rest and the threshold.
-// First call (nsurv == 0): one pass turns raw entries into keys and measures the window.
-// Later calls: the window is [threshold key, previous maximum key]; new entries above it fall
-// into the top bin ("open" bin, refined over [bin start, true maximum]); the raw -> key step
-// is folded into the first histogram pass.
-template <int DT, int WAVES, bool RAW>
-__device__ void compact(const Cand& c, uint32_t n, uint32_t nsurv, uint32_t k, bool fin, uint32_t ilo,
-                        uint32_t ihi, Scalars& sc, uint32_t* hist3, uint32_t& hctr, uint32_t& tkey,
-                        uint32_t& tidx, uint32_t& maxkey) {
-  constexpr uint32_t NT = WAVES * 64;
-  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-  const uint32_t groups = (n + 3u) / 4u;  // entries are visited four at a time
-  auto conv = [](uint32_t raw) { return key_of_raw<DT>(DT == DS_BF16 ? (raw >> 16) : raw); };
+// Search: a kBins-bin histogram of (min(key, hi) - lo) >> shift over a key window [lo, hi]
+// that holds every entry locates the bin of the k-th best; while that bin holds more than
+// kListCap entries the window shrinks to it and the histogram repeats; a bin that is a single
+// key (ties) continues on the indices in [ilo, ihi] (smaller index = higher bin). Then the
+// entries above the pivot window are scattered to the destination, the window's entries are
+// gathered in a short list, and the list is ranked to place the rest and find the threshold.
+// The first window is the whole key space [0, key_hi]; later ones are [T.key, previous
+// maximum], with keys above the previous maximum counted in the top bin ("open" bin, refined
+// over [bin start, new maximum] when it is chosen).
+//
+// Barriers: two per histogram pass (after the counts; after the scan result is published),
+// one after the scatter and one after the list is ranked.
 
-  if (n <= k) {  // keep everything (only the final call can get here)
-    for (uint32_t i = tid; i < k; i += NT) {
-      uint32_t key = 0, id = kSentinelIdx;
-      if (i < n) {
-        key = c.key[i];
-        if (RAW && i >= nsurv) key = conv(key);
-        id = c.idx[i];
-      }
-      c.tkey[i] = key;
-      c.tidx[i] = id;
+// Histogram of one segment's keys (n entries from kp) over the window. With conv the segment
+// holds raw scores, which are replaced by their keys on the way.
+template <int DT>
+__device__ __forceinline__ uint32_t hist_keys(uint32_t* kp, uint32_t n, uint32_t tid, uint32_t nt, uint32_t plo,
+                                              uint32_t phi, bool open, uint32_t shift, uint32_t* h, bool conv) {
+  uint32_t mx = 0;
+  for (uint32_t g = tid; 4u * g < n; g += nt) {
+    uint4 kk = *reinterpret_cast<const uint4*>(kp + 4u * g);
+    if (conv) {
+      kk = make_uint4(key_of_score<DT>(kk.x), key_of_score<DT>(kk.y), key_of_score<DT>(kk.z), key_of_score<DT>(kk.w));
+      *reinterpret_cast<uint4*>(kp + 4u * g) = kk;
     }
-    lds_sync();
-    return;
-  }
-
-  bool raw_pending = RAW;
-  uint32_t lo, hi;
-  bool top_open;
-  if (nsurv == 0) {
-    uint32_t mn = ~0u, mx = 0;
-    for (uint32_t g = tid; g < groups; g += NT) {
-      uint4 kk = *reinterpret_cast<const uint4*>(c.key + 4 * g);
-      if constexpr (RAW) {
-        kk.x = conv(kk.x);
-        kk.y = conv(kk.y);
-        kk.z = conv(kk.z);
-        kk.w = conv(kk.w);
-        *reinterpret_cast<uint4*>(c.key + 4 * g) = kk;
-      }
 #pragma unroll
-      for (uint32_t q = 0; q < 4; ++q) {
-        if (4 * g + q < n) {
-          mn = min(mn, u4get(kk, q));
-          mx = max(mx, u4get(kk, q));
-        }
+    for (uint32_t q = 0; q < 4; ++q) {
+      const uint32_t key = u4get(kk, q);
+      if (4u * g + q < n) {
+        mx = max(mx, key);
+        if (key >= plo && (key <= phi || open)) atomicAdd(&h[hslot((min(key, phi) - plo) >> shift)], 1u);
       }
-    }
-    mn = wave_min32(mn, lane);
-    mx = wave_max32(mx, lane);
-    if (lane == 0) {
-      sc.red[wave][0] = mn;
-      sc.red[wave][1] = mx;
-    }
-    if (tid == 0) {
-      sc.app_count = 0;
-      sc.outpos = 0;
-      sc.listpos = 0;
-    }
-    lds_sync();
-    lo = ~0u;
-    hi = 0;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      lo = min(lo, sc.red[w][0]);
-      hi = max(hi, sc.red[w][1]);
-    }
-    top_open = false;
-    raw_pending = false;
-  } else {
-    lo = tkey;  // every entry ranks at or above the threshold
-    hi = maxkey;
-    top_open = true;
-    if (tid == 0) {  // every wave passed the block barrier after its appends
-      sc.app_count = 0;
-      sc.outpos = 0;
-      sc.listpos = 0;
     }
   }
+  return mx;
+}
 
-  // histogram passes
-  uint32_t need = k, above_total = 0, cnt = 0, seen_max = 0;
-  uint32_t plo = lo, phi = hi;  // key window of the pivot
-  bool tie = false;             // pivot window is a single key: continue on indices
-  uint32_t pkey = 0, iplo = ilo, iphi = ihi;
-  for (;;) {
-    const uint32_t range = tie ? iphi - iplo : phi - plo;
-    const uint32_t shift = bitlen32(range) > 9 ? bitlen32(range) - 9 : 0;
-    uint32_t* h = hist3 + kBins * (hctr % 3u);
-    uint32_t* hn = hist3 + kBins * ((hctr + 1u) % 3u);
-    for (uint32_t b = tid; b < kBins; b += NT) hn[b] = 0;
-    uint32_t mx = 0;
-    for (uint32_t g = tid; g < groups; g += NT) {
-      uint4 kk = *reinterpret_cast<const uint4*>(c.key + 4 * g);
-      if (raw_pending && 4 * g + 3 >= nsurv) {
-        if (4 * g + 0 >= nsurv) kk.x = conv(kk.x);
-        if (4 * g + 1 >= nsurv) kk.y = conv(kk.y);
-        if (4 * g + 2 >= nsurv) kk.z = conv(kk.z);
-        kk.w = conv(kk.w);
-        *reinterpret_cast<uint4*>(c.key + 4 * g) = kk;
-      }
-      if (!tie) {
+// Histogram of the indices of one segment's entries whose key is pkey.
+__device__ __forceinline__ void hist_ties(const uint32_t* kp, const uint32_t* ip, uint32_t n, uint32_t tid, uint32_t nt,
+                                          uint32_t pkey, uint32_t iplo, uint32_t iphi, uint32_t shift, uint32_t* h) {
+  for (uint32_t g = tid; 4u * g < n; g += nt) {
+    const uint4 kk = *reinterpret_cast<const uint4*>(kp + 4u * g);
+    const uint4 ii = *reinterpret_cast<const uint4*>(ip + 4u * g);
 #pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) {
-          const uint32_t key = u4get(kk, q);
-          if (4 * g + q < n) {
-            mx = max(mx, key);
-            if (key >= plo && (key <= phi || top_open)) atomicAdd(&h[(min(key, phi) - plo) >> shift], 1u);
-          }
-        }
-      } else {
-        const uint4 ii = *reinterpret_cast<const uint4*>(c.idx + 4 * g);
-#pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) {
-          const uint32_t key = u4get(kk, q), id = u4get(ii, q);
-          if (4 * g + q < n) {
-            mx = max(mx, key);
-            if (key == pkey && id >= iplo && id <= iphi) atomicAdd(&h[kBins - 1u - ((id - iplo) >> shift)], 1u);
-          }
-        }
-      }
-    }
-    raw_pending = false;
-    mx = wave_max32(mx, lane);
-    if (lane == 0) sc.red[wave][1] = mx;
-    lds_sync();
-    ++hctr;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) seen_max = max(seen_max, sc.red[w][1]);
-    uint32_t bin, above;
-    if constexpr (WAVES > 4) {  // one wave scans and publishes the result
-      if (wave == 0) {
-        scan_select(h, need, lane, bin, above, cnt);
-        if (lane == 0) {
-          sc.scan[0] = bin;
-          sc.scan[1] = above;
-          sc.scan[2] = cnt;
-        }
-      }
-      lds_sync();
-      bin = sc.scan[0];
-      above = sc.scan[1];
-      cnt = sc.scan[2];
-    } else {
-      scan_select(h, need, lane, bin, above, cnt);
-    }
-    need -= above;
-    above_total += above;
-    if (!tie) {
-      const uint32_t nlo = plo + (bin << shift);
-      const bool open_bin = top_open && bin == ((phi - plo) >> shift);
-      const uint64_t nhi64 = static_cast<uint64_t>(plo) + ((static_cast<uint64_t>(bin) + 1u) << shift) - 1u;
-      const uint32_t nhi = nhi64 > phi ? phi : static_cast<uint32_t>(nhi64);
-      plo = nlo;
-      phi = open_bin ? seen_max : nhi;
-      top_open = false;
-      if (cnt <= kListCap) break;
-      if (shift == 0 && !open_bin) {  // one key holds more than kListCap entries
-        tie = true;
-        pkey = plo;
-      }
-    } else {
-      const uint32_t nlo = iplo + ((kBins - 1u - bin) << shift);
-      const uint64_t nhi64 = static_cast<uint64_t>(nlo) + (1ull << shift) - 1u;
-      iphi = nhi64 > iphi ? iphi : static_cast<uint32_t>(nhi64);
-      iplo = nlo;
-      if (cnt <= kListCap || shift == 0) break;
+    for (uint32_t q = 0; q < 4; ++q) {
+      const uint32_t key = u4get(kk, q), id = u4get(ii, q);
+      if (4u * g + q < n && key == pkey && id >= iplo && id <= iphi)
+        atomicAdd(&h[hslot(kBins - 1u - ((id - iplo) >> shift))], 1u);
     }
   }
-  cnt = cnt < kListCap ? cnt : kListCap;  // more only if (key, index) pairs repeat
+}
 
-  // scatter: entries above the pivot window go out, the window's entries to the list
-  const uint32_t iters = (groups + NT - 1) / NT;
+// Where the compaction sends one segment's entries: above the pivot window to (dk, di), inside
+// it to the list.
+struct Pivot {
+  uint32_t plo, phi, pkey, iplo, iphi, k;
+  bool tie;
+};
+
+__device__ __forceinline__ void scatter_seg(const uint32_t* kp, const uint32_t* ip, uint32_t n, uint32_t tid,
+                                            uint32_t nt, uint32_t lane, const Pivot& pv, uint32_t* dk, uint32_t* di,
+                                            Scalars& sc) {
+  const uint32_t iters = (n + 4u * nt - 1u) / (4u * nt);
   for (uint32_t it = 0; it < iters; ++it) {
-    const uint32_t g = it * NT + tid;
+    const uint32_t g = it * nt + tid;
     uint4 kk = make_uint4(0, 0, 0, 0), ii = make_uint4(0, 0, 0, 0);
-    if (g < groups) {
-      kk = *reinterpret_cast<const uint4*>(c.key + 4 * g);
-      ii = *reinterpret_cast<const uint4*>(c.idx + 4 * g);
+    if (4u * g < n) {
+      kk = *reinterpret_cast<const uint4*>(kp + 4u * g);
+      ii = *reinterpret_cast<const uint4*>(ip + 4u * g);
     }
     bool up[4], mid[4];
     uint64_t bu[4], bm[4];
@@ -470,13 +431,13 @@ __device__ void compact(const Cand& c, uint32_t n, uint32_t nsurv, uint32_t k, b
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
       const uint32_t key = u4get(kk, q), id = u4get(ii, q);
-      const bool valid = g < groups && 4 * g + q < n;
-      if (!tie) {
-        up[q] = valid && key > phi;
-        mid[q] = valid && key >= plo && key <= phi;
+      const bool valid = 4u * g + q < n;
+      if (!pv.tie) {
+        up[q] = valid && key > pv.phi;
+        mid[q] = valid && key >= pv.plo && key <= pv.phi;
       } else {
-        up[q] = valid && (key > pkey || (key == pkey && id < iplo));
-        mid[q] = valid && key == pkey && id >= iplo && id <= iphi;
+        up[q] = valid && (key > pv.pkey || (key == pv.pkey && id < pv.iplo));
+        mid[q] = valid && key == pv.pkey && id >= pv.iplo && id <= pv.iphi;
       }
       bu[q] = ballot(up[q]);
       bm[q] = ballot(mid[q]);
@@ -486,8 +447,8 @@ __device__ void compact(const Cand& c, uint32_t n, uint32_t nsurv, uint32_t k, b
     if (nu | nm) {
       uint32_t b0 = 0, b1 = 0;
       if (lane == 0) {
-        if (nu) b0 = atomicAdd(&sc.outpos, nu);
-        if (nm) b1 = atomicAdd(&sc.listpos, nm);
+        b0 = atomicAdd(&sc.outpos, nu);
+        b1 = atomicAdd(&sc.listpos, nm);
       }
       b0 = uni(b0);
       b1 = uni(b1);
@@ -495,9 +456,9 @@ __device__ void compact(const Cand& c, uint32_t n, uint32_t nsurv, uint32_t k, b
       for (uint32_t q = 0; q < 4; ++q) {
         if (up[q]) {
           const uint32_t at = mbcnt(bu[q], b0);
-          if (at < k) {
-            c.tkey[at] = u4get(kk, q);
-            c.tidx[at] = u4get(ii, q);
+          if (at < pv.k) {
+            dk[at] = u4get(kk, q);
+            di[at] = u4get(ii, q);
           }
         }
         if (mid[q]) {
@@ -512,50 +473,161 @@ __device__ void compact(const Cand& c, uint32_t n, uint32_t nsurv, uint32_t k, b
       }
     }
   }
-  lds_sync();
-
-  // every wave ranks the short list: the `need` best of its cnt entries are kept
-  const bool have = lane < cnt;
-  const uint32_t lk = have ? sc.lkey[lane] : 0u, li = have ? sc.lidx[lane] : kSentinelIdx;
-  const uint64_t mine = comp_of(lk, li);
-  uint32_t rank = 0;
-  for (uint32_t m = 0; m < cnt; ++m) rank += readlane64(mine, m) > mine ? 1u : 0u;
-  const bool keep = have && rank < need;
-  const uint64_t piv = ballot(have && rank == need - 1u);
-  const uint32_t pl = piv ? static_cast<uint32_t>(__builtin_ctzll(piv)) : 0u;
-  tkey = __builtin_amdgcn_readlane(lk, pl);
-  tidx = __builtin_amdgcn_readlane(li, pl);
-  maxkey = seen_max;
-  if (!fin) {
-    for (uint32_t i = tid; i < above_total && i < k; i += NT) {
-      c.key[i] = c.tkey[i];
-      c.idx[i] = c.tidx[i];
-    }
-    if (wave == 0 && keep) {
-      c.key[above_total + rank] = lk;
-      c.idx[above_total + rank] = li;
-    }
-  } else {
-    if (wave == 0 && keep) {
-      c.tkey[above_total + rank] = lk;
-      c.tidx[above_total + rank] = li;
-    }
-    lds_sync();
-  }
 }
 
-// One compare-exchange stage (SIZE, STRIDE) of a bitonic sort of NT*E 64-bit keys, best first,
-// held E per thread in registers (element t*E + j in thread t). Partners closer than E are in
-// the same thread, closer than 64*E in the same wave (lane exchanges); farther partners go
-// through `xbuf` (NT*E slots of LDS) between two barriers. Recurses through all later stages.
-template <int WAVES, int E, uint32_t SIZE, uint32_t STRIDE>
-__device__ __forceinline__ void bitonic_stages(uint64_t (&v)[E], uint64_t* xbuf, uint32_t tid, uint32_t lane) {
-  constexpr uint32_t TOTAL = WAVES * 64 * E;
+// RAW: the appended segment holds raw scores (the select kernel); they become keys in the first
+// histogram pass (or in the copy when everything is kept).
+template <int WAVES, int DT, bool RAW>
+__device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, bool fin, bool have_t,
+                        uint32_t key_hi, uint32_t ilo, uint32_t ihi, Scalars& sc, uint32_t* hist2, uint32_t& hpar,
+                        uint32_t& tkey, uint32_t& tidx, uint32_t& maxkey) {
+  constexpr uint32_t NT = WAVES * 64;
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t n = sg.n0 + sg.n1;
+
+  if (n <= k) {  // keep everything (only the final call can get here)
+    const uint32_t k4 = round4(k);
+    for (uint32_t i = tid; i < k4; i += NT) {
+      uint32_t key = 0, id = kSentinelIdx;
+      if (i < sg.n0) {
+        key = sg.k0[i];
+        id = sg.i0[i];
+      } else if (i < n) {
+        key = sg.k1[i - sg.n0];
+        if (RAW) key = key_of_score<DT>(key);
+        id = sg.i1[i - sg.n0];
+      }
+      dk[i] = key;
+      di[i] = id;
+    }
+    lds_sync();
+    return;
+  }
+  if (tid == 0) {  // last used by the previous compaction's scatter, several barriers ago
+    sc.outpos = 0;
+    sc.listpos = 0;
+  }
+
+  Pivot pv;
+  pv.plo = have_t ? tkey : 0u;
+  pv.phi = have_t ? maxkey : key_hi;
+  pv.tie = false;
+  pv.pkey = 0;
+  pv.iplo = ilo;
+  pv.iphi = ihi;
+  pv.k = k;
+  bool open = have_t, first = true;
+  uint32_t need = k, above_total = 0, cnt = 0, seen_max = 0;
+  for (;;) {
+    const uint32_t bl = bitlen32(pv.tie ? pv.iphi - pv.iplo : pv.phi - pv.plo);
+    const uint32_t shift = bl > kLogBins ? bl - kLogBins : 0u;
+    uint32_t* h = hist2 + kBins * (hpar & 1u);
+    uint32_t* hz = hist2 + kBins * ((hpar + 1u) & 1u);
+    // the other histogram was last read by the previous scan, before the last barrier
+    for (uint32_t b = 4u * tid; b < kBins; b += 4u * NT) *reinterpret_cast<uint4*>(hz + b) = make_uint4(0, 0, 0, 0);
+    if (!pv.tie) {
+      // survivors are counted from the last thread down, appended entries from the first up,
+      // so that the threads share the groups evenly
+      uint32_t mx = hist_keys<DT>(sg.k0, sg.n0, NT - 1u - tid, NT, pv.plo, pv.phi, open, shift, h, false);
+      mx = max(mx, hist_keys<DT>(sg.k1, sg.n1, tid, NT, pv.plo, pv.phi, open, shift, h, RAW && first));
+      if (first) {
+        mx = wave_max32(mx);
+        if (lane == 0) sc.red[wave] = mx;
+      }
+    } else {
+      hist_ties(sg.k0, sg.i0, sg.n0, NT - 1u - tid, NT, pv.pkey, pv.iplo, pv.iphi, shift, h);
+      hist_ties(sg.k1, sg.i1, sg.n1, tid, NT, pv.pkey, pv.iplo, pv.iphi, shift, h);
+    }
+    lds_sync();
+    ++hpar;
+    if (wave == 0) {
+      uint32_t smax = 0;
+      if (first) {
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) smax = max(smax, sc.red[w]);
+      }
+      uint32_t bin, above, c;
+      scan_select(h, need, lane, bin, above, c);
+      if (lane == 0) {
+        sc.pub[0] = bin;
+        sc.pub[1] = above;
+        sc.pub[2] = c;
+        sc.pub[3] = smax;
+      }
+    }
+    lds_sync();
+    const uint32_t bin = sc.pub[0], above = sc.pub[1];
+    cnt = sc.pub[2];
+    if (first) seen_max = sc.pub[3];
+    first = false;
+    need -= above;
+    above_total += above;
+    if (!pv.tie) {
+      const bool open_bin = open && bin == ((pv.phi - pv.plo) >> shift);
+      const uint32_t nlo = pv.plo + (bin << shift);
+      const uint64_t nhi64 = static_cast<uint64_t>(nlo) + (1ull << shift) - 1u;
+      pv.phi = open_bin ? seen_max : (nhi64 > pv.phi ? pv.phi : static_cast<uint32_t>(nhi64));
+      pv.plo = nlo;
+      open = false;
+      if (cnt <= kListCap) break;
+      if (pv.plo == pv.phi) {  // one key holds more than kListCap entries: continue on indices
+        pv.tie = true;
+        pv.pkey = pv.plo;
+      }
+    } else {
+      const uint32_t nlo = pv.iplo + ((kBins - 1u - bin) << shift);
+      const uint64_t nhi64 = static_cast<uint64_t>(nlo) + (1ull << shift) - 1u;
+      pv.iphi = nhi64 > pv.iphi ? pv.iphi : static_cast<uint32_t>(nhi64);
+      pv.iplo = nlo;
+      if (cnt <= kListCap || shift == 0) break;
+    }
+  }
+  cnt = cnt < kListCap ? cnt : kListCap;  // more only if (key, index) pairs repeat
+
+  // scatter: entries above the pivot window go to the destination, the window's to the list
+  scatter_seg(sg.k0, sg.i0, sg.n0, NT - 1u - tid, NT, lane, pv, dk, di, sc);
+  scatter_seg(sg.k1, sg.i1, sg.n1, tid, NT, lane, pv, dk, di, sc);
+  lds_sync();
+
+  // wave 0 ranks the short list, places the `need` best of it after the above_total entries
+  // and publishes the threshold
+  if (wave == 0) {
+    const bool have = lane < cnt;
+    const uint32_t lk = have ? sc.lkey[lane] : 0u, li = have ? sc.lidx[lane] : kSentinelIdx;
+    const uint64_t mine = comp_of(lk, li);
+    uint32_t rank = 0;
+    for (uint32_t m = 0; m < cnt; ++m) rank += readlane64(mine, m) > mine ? 1u : 0u;
+    if (have && rank < need) {
+      dk[above_total + rank] = lk;
+      di[above_total + rank] = li;
+    }
+    const uint64_t piv = ballot(have && rank == need - 1u);
+    const uint32_t pl = piv ? static_cast<uint32_t>(__builtin_ctzll(piv)) : 0u;
+    if (lane == 0) {
+      sc.pub[0] = __builtin_amdgcn_readlane(lk, pl);
+      sc.pub[1] = __builtin_amdgcn_readlane(li, pl);
+    }
+  }
+  lds_sync();
+  tkey = sc.pub[0];
+  tidx = sc.pub[1];
+  maxkey = seen_max;
+  (void)fin;
+}
+
+// --------------------------------------------------------------------------- final sort
+// Compare-exchange stages (SIZE, STRIDE) of a bitonic sort, best first, of TOTAL 64-bit keys
+// held E per thread in registers (element t*E + j in thread t). Partners closer than E are
+// in the same thread, closer than 64*E in the same wave (lane exchanges); farther partners
+// go through LDS (xk / xi take the high / low halves) between two barriers. Recurses
+// through all later stages.
+template <int E, uint32_t TOTAL, uint32_t SIZE, uint32_t STRIDE>
+__device__ __forceinline__ void bitonic(uint64_t (&v)[E], uint32_t* xk, uint32_t* xi, uint32_t t, uint32_t lane) {
   if constexpr (STRIDE < static_cast<uint32_t>(E)) {
 #pragma unroll
     for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
       if ((j & STRIDE) == 0) {
-        const bool desc = ((tid * E + j) & SIZE) == 0;
+        const bool desc = ((t * E + j) & SIZE) == 0;
         const uint64_t a = v[j], b = v[j | STRIDE];
         const bool sw = desc ? b > a : a > b;
         v[j] = sw ? b : a;
@@ -566,28 +638,41 @@ __device__ __forceinline__ void bitonic_stages(uint64_t (&v)[E], uint64_t* xbuf,
     constexpr uint32_t M = STRIDE / E;
 #pragma unroll
     for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
-      const uint32_t e = tid * E + j;
+      const uint32_t e = t * E + j;
       const bool take_max = ((e & STRIDE) == 0) == ((e & SIZE) == 0);
       const uint64_t o = xor_lane64(v[j], M, lane);
       v[j] = take_max ? (o > v[j] ? o : v[j]) : (o < v[j] ? o : v[j]);
     }
   } else {
 #pragma unroll
-    for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) xbuf[tid * E + j] = v[j];
+    for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
+      xk[t * E + j] = static_cast<uint32_t>(v[j] >> 32);
+      xi[t * E + j] = static_cast<uint32_t>(v[j]);
+    }
     lds_sync();
 #pragma unroll
     for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
-      const uint32_t e = tid * E + j;
+      const uint32_t e = t * E + j;
       const bool take_max = ((e & STRIDE) == 0) == ((e & SIZE) == 0);
-      const uint64_t o = xbuf[e ^ STRIDE];
+      const uint64_t o = (static_cast<uint64_t>(xk[e ^ STRIDE]) << 32) | xi[e ^ STRIDE];
       v[j] = take_max ? (o > v[j] ? o : v[j]) : (o < v[j] ? o : v[j]);
     }
     lds_sync();
   }
   if constexpr (STRIDE > 1)
-    bitonic_stages<WAVES, E, SIZE, STRIDE / 2>(v, xbuf, tid, lane);
+    bitonic<E, TOTAL, SIZE, STRIDE / 2>(v, xk, xi, t, lane);
   else if constexpr (SIZE < TOTAL)
-    bitonic_stages<WAVES, E, SIZE * 2, SIZE>(v, xbuf, tid, lane);
+    bitonic<E, TOTAL, SIZE * 2, SIZE>(v, xk, xi, t, lane);
+}
+
+// Number of barriers the network above executes.
+template <int E, uint32_t TOTAL>
+constexpr int bitonic_barriers() {
+  int c = 0;
+  for (uint32_t size = 2; size <= TOTAL; size <<= 1)
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1)
+      if (stride >= 64u * E) c += 2;
+  return c;
 }
 
 template <int DT>
@@ -602,83 +687,96 @@ __device__ __forceinline__ void store_out(void* out_vals, int32_t* out_idx, uint
   if (out_idx) out_idx[at] = static_cast<int32_t>(id);
 }
 
-// Sort the k entries of (fkey, fidx) (padded with sentinels to NT*E) best first and store the
-// first k of them.
-template <int DT, int WAVES, int E>
-__device__ void sort_store_e(const uint32_t* fkey, const uint32_t* fidx, uint64_t* xbuf, uint32_t k,
+// Sorts the k entries (fk, fi) (k <= 2^LOGT, padded with zeros) best first and stores them.
+// TH = min(2^LOGT, workgroup) threads hold E = 2^LOGT / TH entries each; the other waves only
+// take part in the barriers. (xk, xi) must not overlap
+// (fk, fi) and hold 2^LOGT words each.
+template <int DT, int WAVES, uint32_t LOGT>
+__device__ __forceinline__ void sort_store_t(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi, uint32_t k,
                              void* out_vals, int32_t* out_idx, uint64_t row) {
+  constexpr uint32_t NT = WAVES * 64, TOTAL = 1u << LOGT;
+  constexpr uint32_t TH = TOTAL > NT ? NT : TOTAL;
+  constexpr int E = static_cast<int>(TOTAL / TH);
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
-  uint64_t v[E];
+  if (tid < TH) {
+    uint64_t v[E];
 #pragma unroll
-  for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
-    const uint32_t e = tid * E + j;
-    v[j] = e < k ? comp_of(fkey[e], fidx[e]) : 0ull;
-  }
-  lds_sync();  // xbuf may overlap memory other threads are still reading above
-  bitonic_stages<WAVES, E, 2, 1>(v, xbuf, tid, lane);
+    for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
+      const uint32_t e = tid * E + j;
+      v[j] = e < k ? comp_of(fk[e], fi[e]) : 0ull;
+    }
+    bitonic<E, TOTAL, 2, 1>(v, xk, xi, tid, lane);
 #pragma unroll
-  for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
-    const uint32_t e = tid * E + j;
-    if (e < k) store_out<DT>(out_vals, out_idx, row * k + e, v[j]);
+    for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
+      const uint32_t e = tid * E + j;
+      if (e < k) store_out<DT>(out_vals, out_idx, row * k + e, v[j]);
+    }
+  } else {
+    constexpr int NB = bitonic_barriers<E, TOTAL>();
+    for (int s = 0; s < NB; ++s) lds_sync();
   }
 }
 
-// Bitonic sort in LDS (one barrier per stage) for k above four entries per thread: sorts cap
-// (a power of two >= k) composites in `xbuf`, best first, and stores the first k.
+// Bitonic sort in LDS with one barrier per stage, for large k in small workgroups: sorts cap
+// (a power of two >= k) composites held as (xk, xi) halves, best first, and stores the first k.
 template <int DT, int WAVES>
-__device__ void sort_store_lds(const uint32_t* fkey, const uint32_t* fidx, uint64_t* xbuf, uint32_t k,
-                               void* out_vals, int32_t* out_idx, uint64_t row) {
+__device__ __forceinline__ void sort_store_lds(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi, uint32_t k,
+                               uint32_t cap, void* out_vals, int32_t* out_idx, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x;
-  uint32_t cap = 1;
-  while (cap < k) cap <<= 1;
-  // xbuf may overlap (fkey, fidx): read everything into registers first, in two halves
-  for (uint32_t base = 0; base < cap; base += NT * 8) {
-    uint64_t tmp[8];
-#pragma unroll
-    for (uint32_t j = 0; j < 8; ++j) {
-      const uint32_t i = base + j * NT + tid;
-      tmp[j] = i < k ? comp_of(fkey[i], fidx[i]) : 0ull;
-    }
-    lds_sync();
-#pragma unroll
-    for (uint32_t j = 0; j < 8; ++j) {
-      const uint32_t i = base + j * NT + tid;
-      if (i < cap) xbuf[i] = tmp[j];
-    }
-    lds_sync();
+  for (uint32_t i = tid; i < cap; i += NT) {
+    xk[i] = i < k ? fk[i] : 0u;
+    xi[i] = i < k ? ~fi[i] : 0u;
   }
+  lds_sync();
   for (uint32_t size = 2; size <= cap; size <<= 1) {
     for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
       for (uint32_t q = tid; q < cap / 2; q += NT) {
         const uint32_t i = ((q & ~(stride - 1)) << 1) | (q & (stride - 1));
         const uint32_t j = i + stride;
-        const uint64_t a = xbuf[i], b = xbuf[j];
+        const uint64_t a = (static_cast<uint64_t>(xk[i]) << 32) | xi[i];
+        const uint64_t b = (static_cast<uint64_t>(xk[j]) << 32) | xi[j];
         const bool desc = (i & size) == 0;
         if (desc ? b > a : a > b) {
-          xbuf[i] = b;
-          xbuf[j] = a;
+          xk[i] = static_cast<uint32_t>(b >> 32);
+          xi[i] = static_cast<uint32_t>(b);
+          xk[j] = static_cast<uint32_t>(a >> 32);
+          xi[j] = static_cast<uint32_t>(a);
         }
       }
       lds_sync();
     }
   }
-  for (uint32_t i = tid; i < k; i += NT) store_out<DT>(out_vals, out_idx, row * k + i, xbuf[i]);
+  for (uint32_t i = tid; i < k; i += NT)
+    store_out<DT>(out_vals, out_idx, row * k + i, (static_cast<uint64_t>(xk[i]) << 32) | xi[i]);
 }
 
-// `xbuf` needs max(NT, pow2 >= k) 64-bit slots; (fkey, fidx) must be visible to every thread.
+// Register sort when at most eight entries per thread are needed, else the LDS sort.
 template <int DT, int WAVES>
-__device__ void sort_and_store(uint64_t* xbuf, const uint32_t* fkey, const uint32_t* fidx, uint32_t k,
+__device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi, uint32_t k,
                                void* out_vals, int32_t* out_idx, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
-  if (k <= NT)
-    sort_store_e<DT, WAVES, 1>(fkey, fidx, xbuf, k, out_vals, out_idx, row);
-  else if (k <= 2 * NT)
-    sort_store_e<DT, WAVES, 2>(fkey, fidx, xbuf, k, out_vals, out_idx, row);
-  else if (k <= 4 * NT)
-    sort_store_e<DT, WAVES, 4>(fkey, fidx, xbuf, k, out_vals, out_idx, row);
-  else
-    sort_store_lds<DT, WAVES>(fkey, fidx, xbuf, k, out_vals, out_idx, row);
+  uint32_t cap = 64;
+  while (cap < k) cap <<= 1;
+  if (cap > 8 * NT) {
+    sort_store_lds<DT, WAVES>(fk, fi, xk, xi, k, cap, out_vals, out_idx, row);
+    return;
+  }
+  switch (cap) {
+    case 64: sort_store_t<DT, WAVES, 6>(fk, fi, xk, xi, k, out_vals, out_idx, row); break;
+    case 128: sort_store_t<DT, WAVES, 7>(fk, fi, xk, xi, k, out_vals, out_idx, row); break;
+    case 256: sort_store_t<DT, WAVES, 8>(fk, fi, xk, xi, k, out_vals, out_idx, row); break;
+    case 512: sort_store_t<DT, WAVES, 9>(fk, fi, xk, xi, k, out_vals, out_idx, row); break;
+    case 1024:
+      if constexpr (1024 <= 8 * NT) sort_store_t<DT, WAVES, 10>(fk, fi, xk, xi, k, out_vals, out_idx, row);
+      break;
+    case 2048:
+      if constexpr (2048 <= 8 * NT) sort_store_t<DT, WAVES, 11>(fk, fi, xk, xi, k, out_vals, out_idx, row);
+      break;
+    default:
+      if constexpr (4096 <= 8 * NT) sort_store_t<DT, WAVES, 12>(fk, fi, xk, xi, k, out_vals, out_idx, row);
+      break;
+  }
 }
 
 // Integer compare values for the streaming filter, from the threshold pair (key, idx).
@@ -686,8 +784,8 @@ __device__ void sort_and_store(uint64_t* xbuf, const uint32_t* fkey, const uint3
 // blocks after the threshold's index, "non-strict" (ties win) for blocks before it.
 // bf16 scores carry the element in the high 16 bits.
 template <int DT>
-__device__ __forceinline__ void filter_thresholds(Thr t, uint32_t& mode, uint32_t& thr_s, uint32_t& thr_n) {
-  const uint32_t raw = raw_of_key<DT>(t.key);
+__device__ __forceinline__ void filter_thresholds(uint32_t tkey, uint32_t& mode, uint32_t& thr_s, uint32_t& thr_n) {
+  const uint32_t raw = raw_of_key<DT>(tkey);
   if constexpr (DT == DS_BF16) {
     if ((raw & 0x8000u) == 0) {
       mode = 1;
@@ -711,37 +809,290 @@ __device__ __forceinline__ void filter_thresholds(Thr t, uint32_t& mode, uint32_
   }
 }
 
-// LDS layout shared by both kernels (32-bit words): key[cap] idx[cap] tkey[k4] tidx[k4]
-// hist[3*kBins], with cap = k + B2 + B and k4 = k, both rounded up to multiples of 4.
-__host__ __device__ constexpr uint32_t round4(uint32_t v) { return (v + 3u) & ~3u; }
-
-__device__ __forceinline__ Cand cand_layout(uint32_t* lds, uint32_t k, uint32_t B2, uint32_t B, uint32_t*& hist3) {
-  const uint32_t cap = round4(k + B2 + B), k4 = round4(k);
-  Cand c;
-  c.key = lds;
-  c.idx = lds + cap;
-  c.tkey = lds + 2 * cap;
-  c.tidx = lds + 2 * cap + k4;
-  hist3 = lds + 2 * cap + 2 * k4;
-  return c;
-}
-
-// --------------------------------------------------------------------------- select kernel
+// --------------------------------------------------------------------------- DeepSelect body
 // Byte offset past every buffer range: a load there returns zeros and reads no memory.
 constexpr uint32_t kNoLoad = 0x7FFFFFF0u;
 
-template <int DT, int WAVES, int CPW, int PD>
+// One workgroup runs DeepSelect over `len` items of a 16-byte-aligned stream (rs).
+// MERGE == false: items are raw elements of type DT (the select kernel); MERGE == true:
+// items are (key, index) pairs of 8 bytes (the merge kernel). Ends with the k survivors,
+// unordered, in (*fk, *fi) (visible to every thread).
+struct BodyOut {
+  const uint32_t* fk;
+  const uint32_t* fi;
+  uint64_t reads, jsum;  // this thread's share of the elements read and of their indices
+};
+
+// D buffers of CPW chunks per wave are in flight: block i+D is loaded into the registers of
+// block i as soon as block i has been filtered. The loop body handles D blocks with D
+// separate buffers and has no exit, so the compiler sees which loads are the older ones and
+// waits only for those.
+template <int DT, int WAVES, int CPW, int D, bool MERGE>
+__device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amdgpu_buffer_rsrc_t rs, uint32_t len,
+                                                uint32_t idx_base, uint32_t k, uint32_t B2, const BlockOrder& ord,
+                                                uint32_t ilo, uint32_t ihi, bool stats, BodyOut& out) {
+  constexpr uint32_t NT = WAVES * 64;
+  constexpr uint32_t IB = MERGE ? 8 : (DT == DS_BF16 ? 2 : 4);  // bytes per item
+  constexpr uint32_t VEC = 16 / IB;                            // items per lane per chunk
+  constexpr uint32_t CHUNK = 64 * VEC;
+  constexpr uint32_t B = WAVES * CPW * CHUNK;
+  constexpr uint32_t key_hi = DT == DS_BF16 ? 0xFFFFu : 0xFFFFFFFFu;  // largest possible key
+  static_assert(D == 2 || D == 4, "two or four buffers");
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t m = (len + B - 1) / B;
+
+  // block order: a table for streams of up to kOrdCap blocks, computed on the fly beyond
+  const bool tab = m <= kOrdCap;
+  if (tab)
+    for (uint32_t i = tid; i < m; i += NT) L.ordt[i] = ord.at(i);
+  lds_sync();
+  auto bid_of = [&](uint32_t i) -> uint32_t { return i >= m ? m : (tab ? uni(L.ordt[i]) : ord.at(i)); };
+
+  // threshold state (uniform across the workgroup)
+  uint32_t mode = 0, thr_s = ~0u, thr_n = ~0u;  // mode 0: accept everything (no threshold yet)
+  uint32_t t_key = 0, t_idx = 0, maxkey = 0;
+  uint32_t nsurv = 0, napp = 0, hpar = 0, b3 = 0;
+  bool sur_a = false;  // survivors in set A (else set B)
+  const bool st0 = stats && tid == 0;  // the thread that keeps the counters in sc.st_*
+  uint64_t t_mark = 0;
+  uint64_t my_reads = 0, my_jsum = 0;
+
+  auto addr = [&](uint32_t bid, uint32_t t) -> uint32_t {
+    return bid < m ? (bid * B + (wave + t * WAVES) * CHUNK + lane * VEC) * IB : kNoLoad;
+  };
+
+  u32x4 buf[D][CPW];
+  uint32_t bids[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    bids[d] = bid_of(d);
+#pragma unroll
+    for (uint32_t t = 0; t < CPW; ++t) buf[d][t] = load16(rs, addr(bids[d], t));
+  }
+
+  auto compaction = [&](bool fin) {
+    const Segs sg = nsurv ? make_segs(sur_a ? L.ck : L.bk, sur_a ? L.ci : L.bi, nsurv, L.ck + L.k4, L.ci + L.k4, napp)
+                          : make_segs(nullptr, nullptr, 0u, L.ck, L.ci, napp);
+    const bool to_a = nsurv != 0 && !sur_a;  // first compaction: entries start in A, go to B
+    compact<WAVES, DT, !MERGE>(sg, to_a ? L.ck : L.bk, to_a ? L.ci : L.bi, k, fin, nsurv != 0, key_hi, ilo, ihi, sc,
+                               L.hist, hpar, t_key, t_idx, maxkey);
+    if (st0) {
+      sc.st_a += napp;
+      sc.st_w += nsurv + napp;
+    }
+    sur_a = to_a;
+  };
+
+  // Filter block `bid` (the i-th in the order) from `buf`, refill `buf` with block i+D, sync,
+  // and compact when the buffer is full.
+  auto process = [&](u32x4(&bf)[CPW], uint32_t& bid_ref, uint32_t i) {
+    const uint32_t bid = bid_ref;
+    const uint32_t blk_lo = bid * B;
+    const uint32_t abase = (nsurv ? L.k4 : 0u) + napp;  // append position of this block's first entry
+    const uint32_t nxt = (b3 == 2 ? 0u : b3 + 1u);
+    if constexpr (!MERGE) {
+      const bool strict = idx_base + blk_lo > t_idx;
+      const uint32_t thr = strict ? thr_s : thr_n;
+      uint32_t s[CPW][VEC];
+#pragma unroll
+      for (uint32_t t = 0; t < CPW; ++t) {
+        if constexpr (DT == DS_BF16) {
+#pragma unroll
+          for (uint32_t q = 0; q < 4; ++q) {
+            s[t][2 * q] = bf[t][q] << 16;
+            s[t][2 * q + 1] = bf[t][q];
+          }
+        } else {
+#pragma unroll
+          for (uint32_t q = 0; q < 4; ++q) s[t][q] = bf[t][q];
+        }
+      }
+      if (stats) {
+#pragma unroll
+        for (uint32_t t = 0; t < CPW; ++t) {
+          const uint32_t first = blk_lo + (wave + t * WAVES) * CHUNK + lane * VEC;
+          const uint32_t nval = first >= len ? 0u : min(VEC, len - first);
+          my_reads += nval;
+          my_jsum += nval * static_cast<uint64_t>(idx_base + first) + (static_cast<uint64_t>(nval) * (nval - 1)) / 2;
+        }
+      }
+      if (mode == 0 && blk_lo + B <= len) {
+        // accept everything: each wave stores its chunks (raw) contiguously
+        constexpr uint32_t tot = CPW * CHUNK;
+        uint32_t pos = 0;
+        if (lane == 0) pos = atomicAdd(&sc.blk[b3], tot);
+        pos = uni(pos) + abase;
+        if (tid == 0) sc.blk[nxt] = 0;
+        if (pos % 4u == 0) {
+#pragma unroll
+          for (uint32_t t = 0; t < CPW; ++t) {
+            const uint32_t at = pos + t * CHUNK + lane * VEC;
+            const uint32_t j0 = idx_base + blk_lo + (wave + t * WAVES) * CHUNK + lane * VEC;
+#pragma unroll
+            for (uint32_t q = 0; q < VEC; q += 4) {
+              *reinterpret_cast<uint4*>(L.ck + at + q) = make_uint4(s[t][q], s[t][q + 1], s[t][q + 2], s[t][q + 3]);
+              *reinterpret_cast<uint4*>(L.ci + at + q) = make_uint4(j0 + q, j0 + q + 1, j0 + q + 2, j0 + q + 3);
+            }
+          }
+        } else {
+#pragma unroll
+          for (uint32_t t = 0; t < CPW; ++t) {
+            const uint32_t at = pos + t * CHUNK + lane * VEC;
+            const uint32_t j0 = idx_base + blk_lo + (wave + t * WAVES) * CHUNK + lane * VEC;
+#pragma unroll
+            for (uint32_t q = 0; q < VEC; ++q) {
+              L.ck[at + q] = s[t][q];
+              L.ci[at + q] = j0 + q;
+            }
+          }
+        }
+      } else {
+        // one reservation per chunk: only that chunk's hit masks are live. Hits are stored raw.
+#pragma unroll
+        for (uint32_t t = 0; t < CPW; ++t) {
+          const uint32_t first = blk_lo + (wave + t * WAVES) * CHUNK + lane * VEC;
+          bool h[VEC];
+          if (mode == 1) {
+#pragma unroll
+            for (uint32_t e = 0; e < VEC; ++e) h[e] = static_cast<int32_t>(s[t][e]) > static_cast<int32_t>(thr);
+          } else {  // mode 2; without a threshold thr is ~0 and every (non-NaN) score passes
+#pragma unroll
+            for (uint32_t e = 0; e < VEC; ++e) h[e] = s[t][e] < thr;
+          }
+          if (blk_lo + (wave + t * WAVES) * CHUNK + CHUNK > len) {  // the stream's tail chunk
+            const uint32_t nval = first >= len ? 0u : min(VEC, len - first);
+#pragma unroll
+            for (uint32_t e = 0; e < VEC; ++e) h[e] = h[e] && e < nval;
+          }
+          uint64_t mk[VEC];
+          uint32_t tot = 0;
+#pragma unroll
+          for (uint32_t e = 0; e < VEC; ++e) {
+            mk[e] = ballot(h[e]);
+            tot += popc(mk[e]);
+          }
+          if (tot) {
+            uint32_t pos = 0;
+            if (lane == 0) pos = atomicAdd(&sc.blk[b3], tot);
+            pos = uni(pos) + abase;
+            const uint32_t j0 = idx_base + first;
+#pragma unroll
+            for (uint32_t e = 0; e < VEC; ++e) {
+              if (mk[e]) {
+                const uint32_t q = mbcnt(mk[e], pos);
+                if (h[e]) {
+                  L.ck[q] = s[t][e];
+                  L.ci[q] = j0 + e;
+                }
+                pos += popc(mk[e]);
+              }
+            }
+          }
+        }
+        if (tid == 0) sc.blk[nxt] = 0;
+      }
+    } else {
+      // merge: items are (key, index) pairs; a hit beats T in the composite order
+      bool h[CPW][2];
+      uint64_t mk[CPW][2];
+      uint32_t tot = 0;
+#pragma unroll
+      for (uint32_t t = 0; t < CPW; ++t) {
+        const uint32_t first = blk_lo + (wave + t * WAVES) * CHUNK + lane * 2;
+#pragma unroll
+        for (uint32_t e = 0; e < 2; ++e) {
+          const uint32_t key = bf[t][2 * e], id = bf[t][2 * e + 1];
+          const bool beats = mode == 0 || key > t_key || (key == t_key && id < t_idx);
+          h[t][e] = beats && first + e < len;
+          mk[t][e] = ballot(h[t][e]);
+          tot += popc(mk[t][e]);
+        }
+      }
+      uint32_t pos = 0;
+      if (lane == 0 && tot) pos = atomicAdd(&sc.blk[b3], tot);
+      pos = uni(pos) + abase;
+      if (tid == 0) sc.blk[nxt] = 0;
+      if (tot) {
+#pragma unroll
+        for (uint32_t t = 0; t < CPW; ++t) {
+#pragma unroll
+          for (uint32_t e = 0; e < 2; ++e) {
+            if (mk[t][e]) {
+              const uint32_t q = mbcnt(mk[t][e], pos);
+              if (h[t][e]) {
+                L.ck[q] = bf[t][2 * e];
+                L.ci[q] = bf[t][2 * e + 1];
+              }
+              pos += popc(mk[t][e]);
+            }
+          }
+        }
+      }
+    }
+
+    // refill this buffer with block i+D (blocks i+1 .. i+D-1 are already in flight)
+    bid_ref = bid_of(i + D);
+#pragma unroll
+    for (uint32_t t = 0; t < CPW; ++t) bf[t] = load16(rs, addr(bid_ref, t));
+
+    if (st0) t_mark = wall_clock64();
+    lds_sync();
+    if (st0) sc.st_ts += wall_clock64() - t_mark;
+    napp += sc.blk[b3];
+    b3 = nxt;
+    if (st0) sc.st_max = max(sc.st_max, static_cast<unsigned long long>(nsurv + napp));
+    if (nsurv + napp >= k + B2) {
+      const uint64_t prev_c = comp_of(t_key, t_idx);
+      const bool had_t = nsurv != 0;
+      if (st0) t_mark = wall_clock64();
+      compaction(false);
+      if (st0) {
+        sc.st_tc += wall_clock64() - t_mark;
+        sc.st_r += 1;
+        if (had_t && comp_of(t_key, t_idx) < prev_c) sc.st_mono = 0;
+      }
+      nsurv = k;
+      napp = 0;
+      if constexpr (!MERGE)
+        filter_thresholds<DT>(t_key, mode, thr_s, thr_n);
+      else
+        mode = 1;
+    }
+  };
+
+  // Steps past the last block use the empty block id m: no loads, no hits, no effect.
+  for (uint32_t i = 0; i < m; i += D) {
+    process(buf[0], bids[0], i);
+    process(buf[1], bids[1], i + 1);
+    if constexpr (D == 4) {
+      process(buf[2], bids[2], i + 2);
+      process(buf[3], bids[3], i + 3);
+    }
+  }
+
+  // final compaction
+  if (st0) sc.st_tf = wall_clock64();
+  compaction(true);
+  out.fk = sur_a ? L.ck : L.bk;
+  out.fi = sur_a ? L.ci : L.bi;
+  out.reads = my_reads;
+  out.jsum = my_jsum;
+}
+
+// Buffers in flight per wave: four when the workgroup is small enough to leave the registers.
+constexpr int depth_for(int waves) { return waves >= 16 ? 2 : 4; }
+
+// --------------------------------------------------------------------------- select kernel
+template <int DT, int WAVES, int CPW>
 __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t EB = DT == DS_BF16 ? 2 : 4;
-  constexpr uint32_t VEC = 16 / EB;
-  constexpr uint32_t CHUNK = 64 * VEC;
-  constexpr uint32_t B = WAVES * CPW * CHUNK;
+  constexpr uint32_t B = WAVES * CPW * 64 * (16 / EB);
 
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   __shared__ Scalars sc;
 
-  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t row = blockIdx.x / static_cast<uint32_t>(p.slices);
   const uint32_t slice = blockIdx.x % static_cast<uint32_t>(p.slices);
   const uint32_t slice_lo = slice * static_cast<uint32_t>(p.slice_len);
@@ -750,15 +1101,14 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   const uint32_t k = static_cast<uint32_t>(p.k);
   const uint32_t B2 = static_cast<uint32_t>(p.slack);
   const bool stats = p.stats != nullptr;
+  const uint64_t t_start = stats ? wall_clock64() : 0;
 
-  uint32_t* hist3;
-  const Cand c = cand_layout(lds, k, B2, B, hist3);
-
-  for (uint32_t i = tid; i < 3u * kBins; i += NT) hist3[i] = 0;
+  const Lay L = lay_of(lds, k, B2, B);
+  for (uint32_t i = 4u * tid; i < 2u * kBins; i += 4u * NT) *reinterpret_cast<uint4*>(L.hist + i) = make_uint4(0, 0, 0, 0);
   if (tid == 0) {
-    sc.app_count = 0;
-    sc.outpos = 0;
-    sc.listpos = 0;
+    sc.blk[0] = sc.blk[1] = sc.blk[2] = 0;
+    sc.st_a = sc.st_r = sc.st_w = sc.st_max = sc.st_tc = sc.st_ts = sc.st_tf = 0;
+    sc.st_mono = 1;
     sc.reads = 0;
     sc.index_sum = 0;
   }
@@ -772,153 +1122,12 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   BlockOrder ord;
   ord.init(p.seed, row, slice, m);
 
-  // threshold state (uniform across the workgroup)
-  uint32_t mode = 0, thr_s = 0, thr_n = 0;
-  uint32_t t_key = 0, t_idx = 0, maxkey = 0;
-  uint32_t nsurv = 0, napp = 0, hctr = 0;
-  // counters (thread-uniform; used when stats are requested)
-  uint64_t st_a = 0, st_r = 0, st_w = 0, st_max = 0, st_mono = 1, my_reads = 0, my_jsum = 0;
-  uint64_t t_start = stats ? wall_clock64() : 0, t_compact = 0, t_sync = 0, t_mark = 0;
-
-  // Two-stage pipeline: at the top of block i the wave takes block i's chunks (loaded during
-  // block i-1) and at once issues the loads of block i+1, which stay in flight through the
-  // filter, the barrier and any compaction. Past the last block the loads go to kNoLoad.
-  u32x4 next[CPW];
-  uint32_t next_bid = ord.at(0);
-#pragma unroll
-  for (uint32_t t = 0; t < CPW; ++t) next[t] = load16(rs, (next_bid * B + (wave + t * WAVES) * CHUNK + lane * VEC) * EB);
-  lds_sync();
-
-  for (uint32_t i = 0; i < m; ++i) {
-    u32x4 cur[CPW];
-#pragma unroll
-    for (uint32_t t = 0; t < CPW; ++t) cur[t] = next[t];
-    const uint32_t bid = next_bid;
-    {
-      const bool live = i + 1 < m;
-      next_bid = live ? ord.at(i + 1) : 0u;
-#pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t)
-        next[t] = load16(rs, live ? (next_bid * B + (wave + t * WAVES) * CHUNK + lane * VEC) * EB : kNoLoad);
-    }
-    const uint32_t blk_lo = bid * B;
-    const bool strict = slice_lo + blk_lo > t_idx;
-    const uint32_t thr = strict ? thr_s : thr_n;
-
-    // ---- filter: scores (bf16 elements in the high half) and hit masks
-    uint32_t s[CPW][VEC];
-    bool h[CPW][VEC];
-#pragma unroll
-    for (uint32_t t = 0; t < CPW; ++t) {
-      if constexpr (DT == DS_BF16) {
-#pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) {
-          s[t][2 * q] = cur[t][q] << 16;
-          s[t][2 * q + 1] = cur[t][q];
-        }
-      } else {
-#pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) s[t][q] = cur[t][q];
-      }
-    }
-    if (mode == 1) {
-#pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t)
-#pragma unroll
-        for (uint32_t e = 0; e < VEC; ++e) h[t][e] = static_cast<int32_t>(s[t][e]) > static_cast<int32_t>(thr);
-    } else if (mode == 2) {
-#pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t)
-#pragma unroll
-        for (uint32_t e = 0; e < VEC; ++e) h[t][e] = s[t][e] < thr;
-    } else {
-#pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t)
-#pragma unroll
-        for (uint32_t e = 0; e < VEC; ++e) h[t][e] = true;
-    }
-    uint64_t mk[CPW][VEC];
-    uint32_t tot = 0;
-#pragma unroll
-    for (uint32_t t = 0; t < CPW; ++t) {
-      const uint32_t off = blk_lo + (wave + t * WAVES) * CHUNK;
-      uint32_t nval = VEC;
-      if (off + CHUNK > len) {  // the slice's tail chunk: only [0, len) is valid
-        const uint32_t first = off + lane * VEC;
-        nval = first >= len ? 0u : min(VEC, len - first);
-#pragma unroll
-        for (uint32_t e = 0; e < VEC; ++e) h[t][e] = h[t][e] && e < nval;
-      }
-      if (stats) {
-        const uint64_t j0 = slice_lo + off + lane * VEC;
-        my_reads += nval;
-        my_jsum += nval * j0 + (static_cast<uint64_t>(nval) * (nval - 1)) / 2;
-      }
-#pragma unroll
-      for (uint32_t e = 0; e < VEC; ++e) {
-        mk[t][e] = ballot(h[t][e]);
-        tot += popc(mk[t][e]);
-      }
-    }
-
-    // ---- append: one reservation per wave per block
-    uint32_t pos = 0;
-    if (lane == 0) pos = atomicAdd(&sc.app_count, tot);
-    pos = uni(pos);
-    if (lane == 0) sc.slot[i & 1u][wave] = pos + tot;
-    if (tot) {
-      pos += nsurv;
-#pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t) {
-        const uint32_t jl = slice_lo + blk_lo + (wave + t * WAVES) * CHUNK + lane * VEC;
-#pragma unroll
-        for (uint32_t e = 0; e < VEC; ++e) {
-          if (mk[t][e]) {
-            const uint32_t q = mbcnt(mk[t][e], pos);
-            if (h[t][e]) {
-              c.key[q] = s[t][e];
-              c.idx[q] = jl + e;
-            }
-            pos += popc(mk[t][e]);
-          }
-        }
-      }
-    }
-    if (stats) t_mark = wall_clock64();
-    lds_sync();
-    if (stats) t_sync += wall_clock64() - t_mark;
-
-    // ---- compaction test after the whole block
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) cnt = max(cnt, sc.slot[i & 1u][w]);
-    napp = cnt;
-    st_max = max(st_max, static_cast<uint64_t>(nsurv + napp));
-    if (nsurv + napp >= k + B2) {
-      const uint64_t prev_c = comp_of(t_key, t_idx);
-      const bool first = nsurv == 0;
-      if (stats) t_mark = wall_clock64();
-      compact<DT, WAVES, true>(c, nsurv + napp, nsurv, k, false, slice_lo, slice_lo + len - 1u, sc, hist3, hctr,
-                               t_key, t_idx, maxkey);
-      if (stats) t_compact += wall_clock64() - t_mark;
-      st_a += napp;
-      st_w += nsurv + napp;
-      st_r += 1;
-      if (!first && comp_of(t_key, t_idx) < prev_c) st_mono = 0;
-      nsurv = k;
-      napp = 0;
-      filter_thresholds<DT>(Thr{t_key, t_idx}, mode, thr_s, thr_n);
-    }
-  }
-
-  // ---- final compaction: survivors to (tkey, tidx)
-  const uint64_t t_final0 = stats ? wall_clock64() : 0;
-  compact<DT, WAVES, true>(c, nsurv + napp, nsurv, k, true, slice_lo, slice_lo + len - 1u, sc, hist3, hctr, t_key,
-                           t_idx, maxkey);
-  st_a += napp;
-  st_w += nsurv + napp;
+  BodyOut bo;
+  deepselect_body<DT, WAVES, CPW, depth_for(WAVES), false>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
+                                                            slice_lo + len - 1u, stats, bo);
 
   if (stats) {
+    uint64_t my_reads = bo.reads, my_jsum = bo.jsum;
     for (uint32_t o = 32; o > 0; o >>= 1) {
       my_reads += __shfl_xor(my_reads, o);
       my_jsum += __shfl_xor(my_jsum, o);
@@ -930,144 +1139,66 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
     lds_sync();
     if (tid == 0) {
       ds_stats* o = p.stats + blockIdx.x;
-      o->appended = st_a;
-      o->compactions = st_r;
-      o->work = st_w;
-      o->max_len = st_max;
+      o->appended = sc.st_a;
+      o->compactions = sc.st_r;
+      o->work = sc.st_w;
+      o->max_len = sc.st_max;
       o->reads = sc.reads;
       o->index_sum = sc.index_sum;
-      o->monotone = st_mono;
+      o->monotone = sc.st_mono;
       o->slice_lo = slice_lo;
       o->slice_len = len;
       o->block = B;
       o->slack = B2;
-      o->t_compact_ns = t_compact * 10;
-      o->t_sync_ns = t_sync * 10;
+      o->t_compact_ns = sc.st_tc * 10;
+      o->t_sync_ns = sc.st_ts * 10;
       o->reserved = 0;
     }
   }
 
   if (p.slices == 1) {
-    sort_and_store<DT, WAVES>(reinterpret_cast<uint64_t*>(c.key), c.tkey, c.tidx, k, p.out_vals, p.out_idx, row);
+    sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, p.out_vals, p.out_idx, row);
   } else {
     uint2* const dst = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + static_cast<uint64_t>(slice) * k;
-    for (uint32_t i = tid; i < k; i += NT) dst[i] = make_uint2(c.tkey[i], c.tidx[i]);
+    for (uint32_t i = tid; i < k; i += NT) dst[i] = make_uint2(bo.fk[i], bo.fi[i]);
   }
   if (stats && tid == 0) {
     const uint64_t t_end = wall_clock64();
     p.stats[blockIdx.x].t_total_ns = (t_end - t_start) * 10;
-    p.stats[blockIdx.x].t_final_ns = (t_end - t_final0) * 10;
+    p.stats[blockIdx.x].t_final_ns = (t_end - sc.st_tf) * 10;
   }
 }
 
 // --------------------------------------------------------------------------- merge kernel
-// DeepSelect again, over the slices' survivors of one row: entries are already (key, index)
-// pairs; a 16-byte lane load carries two of them.
-template <int DT, int WAVES, int CPW, int PD>
+// DeepSelect again, over the slices' survivors of one row: items are (key, index) pairs.
+template <int DT, int WAVES, int CPW>
 __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   constexpr uint32_t NT = WAVES * 64;
-  constexpr uint32_t CHUNK = 128;  // entries per wave load
-  constexpr uint32_t B = WAVES * CPW * CHUNK;
+  constexpr uint32_t B = WAVES * CPW * 128;
 
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   __shared__ Scalars sc;
 
-  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t tid = threadIdx.x;
   const uint32_t row = blockIdx.x;
   const uint32_t len = static_cast<uint32_t>(p.entries);
   const uint32_t m = (len + B - 1) / B;
   const uint32_t k = static_cast<uint32_t>(p.k);
   const uint32_t B2 = static_cast<uint32_t>(p.slack);
 
-  uint32_t* hist3;
-  const Cand c = cand_layout(lds, k, B2, B, hist3);
-  for (uint32_t i = tid; i < 3u * kBins; i += NT) hist3[i] = 0;
-  if (tid == 0) {
-    sc.app_count = 0;
-    sc.outpos = 0;
-    sc.listpos = 0;
-  }
+  const Lay L = lay_of(lds, k, B2, B);
+  for (uint32_t i = 4u * tid; i < 2u * kBins; i += 4u * NT) *reinterpret_cast<uint4*>(L.hist + i) = make_uint4(0, 0, 0, 0);
+  if (tid == 0) sc.blk[0] = sc.blk[1] = sc.blk[2] = 0;
   const uint2* base = p.ws + static_cast<uint64_t>(row) * p.row_entries;  // rows padded to 16 bytes
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint2*>(base), 0, static_cast<int>((len * 8u + 15u) & ~15u), kRsrcWord3);
   BlockOrder ord;
   ord.init(p.seed, row, 0x7FFFFFFFu, m);
 
-  bool accept_all = true;
-  uint32_t t_key = 0, t_idx = 0, maxkey = 0;
-  uint32_t nsurv = 0, napp = 0, hctr = 0;
-
-  u32x4 next[CPW];
-  uint32_t next_bid = ord.at(0);
-#pragma unroll
-  for (uint32_t t = 0; t < CPW; ++t) next[t] = load16(rs, (next_bid * B + (wave + t * WAVES) * CHUNK + lane * 2) * 8u);
-  lds_sync();
-
-  for (uint32_t i = 0; i < m; ++i) {
-    u32x4 v[CPW];
-#pragma unroll
-    for (uint32_t t = 0; t < CPW; ++t) v[t] = next[t];
-    const uint32_t bid = next_bid;
-    {
-      const bool live = i + 1 < m;
-      next_bid = live ? ord.at(i + 1) : 0u;
-#pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t)
-        next[t] = load16(rs, live ? (next_bid * B + (wave + t * WAVES) * CHUNK + lane * 2) * 8u : kNoLoad);
-    }
-    const uint32_t blk_lo = bid * B;
-    bool h[CPW][2];
-    uint64_t mk[CPW][2];
-    uint32_t tot = 0;
-#pragma unroll
-    for (uint32_t t = 0; t < CPW; ++t) {
-      const uint32_t first = blk_lo + (wave + t * WAVES) * CHUNK + lane * 2;
-#pragma unroll
-      for (uint32_t e = 0; e < 2; ++e) {
-        const uint32_t key = v[t][2 * e], idx = v[t][2 * e + 1];
-        const bool beats = accept_all || key > t_key || (key == t_key && idx < t_idx);
-        h[t][e] = beats && first + e < len;
-        mk[t][e] = ballot(h[t][e]);
-        tot += popc(mk[t][e]);
-      }
-    }
-    uint32_t pos = 0;
-    if (lane == 0) pos = atomicAdd(&sc.app_count, tot);
-    pos = uni(pos);
-    if (lane == 0) sc.slot[i & 1u][wave] = pos + tot;
-    if (tot) {
-      pos += nsurv;
-#pragma unroll
-      for (uint32_t t = 0; t < CPW; ++t) {
-#pragma unroll
-        for (uint32_t e = 0; e < 2; ++e) {
-          if (mk[t][e]) {
-            const uint32_t q = mbcnt(mk[t][e], pos);
-            if (h[t][e]) {
-              c.key[q] = v[t][2 * e];
-              c.idx[q] = v[t][2 * e + 1];
-            }
-            pos += popc(mk[t][e]);
-          }
-        }
-      }
-    }
-    lds_sync();
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) cnt = max(cnt, sc.slot[i & 1u][w]);
-    napp = cnt;
-    if (nsurv + napp >= k + B2) {
-      compact<DT, WAVES, false>(c, nsurv + napp, nsurv, k, false, 0u, static_cast<uint32_t>(p.n - 1), sc, hist3,
-                                hctr, t_key, t_idx, maxkey);
-      accept_all = false;
-      nsurv = k;
-      napp = 0;
-    }
-  }
-  compact<DT, WAVES, false>(c, nsurv + napp, nsurv, k, true, 0u, static_cast<uint32_t>(p.n - 1), sc, hist3, hctr,
-                            t_key, t_idx, maxkey);
-  sort_and_store<DT, WAVES>(reinterpret_cast<uint64_t*>(c.key), c.tkey, c.tidx, k, p.out_vals, p.out_idx, row);
+  BodyOut bo;
+  deepselect_body<DT, WAVES, CPW, depth_for(WAVES), true>(L, sc, rs, len, 0u, k, B2, ord, 0u,
+                                                           static_cast<uint32_t>(p.n - 1), false, bo);
+  sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, p.out_vals, p.out_idx, row);
 }
 
 // --------------------------------------------------------------------------- probes
@@ -1118,12 +1249,9 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(u32x4* dst, c
   }
 }
 
-// prefetch ring depth: about eight 1 KiB wave chunks in flight per wave
-constexpr int ring_depth(int cpw) { return cpw > 0 ? 1 : 1; }  // one block in flight per wave (two-stage pipeline)
-
 template <int DT, int W, int C>
 hipError_t launch_select_shape(const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream) {
-  auto kern = select_kernel<DT, W, C, ring_depth(C)>;
+  auto kern = select_kernel<DT, W, C>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -1152,7 +1280,7 @@ hipError_t launch_select_dt(int shape, const SelectParams& p, int64_t rows, size
 template <int DT>
 hipError_t launch_merge_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
   constexpr int W = kMergeShape.waves, C = kMergeShape.cpw;
-  auto kern = merge_kernel<DT, W, C, ring_depth(C)>;
+  auto kern = merge_kernel<DT, W, C>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -1166,8 +1294,8 @@ hipError_t launch_merge_dt(const MergeParams& p, int64_t rows, size_t lds, hipSt
 
 size_t select_lds_bytes(int k, int block, int slack, int waves) {
   (void)waves;
-  const size_t cap = round4(static_cast<uint32_t>(k + slack + block)), k4 = round4(static_cast<uint32_t>(k));
-  return (2 * cap + 2 * k4 + 3 * kBins) * 4 + sizeof(Scalars);
+  const size_t k4 = round4(static_cast<uint32_t>(k)), pc = round4(static_cast<uint32_t>(slack + block));
+  return (2 * (k4 + pc) + 2 * k4 + 2 * kBins + kOrdCap) * 4 + sizeof(Scalars);
 }
 
 hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,
