@@ -2,12 +2,17 @@
 """Benchmark: effective input GB/s of one DeepSelect top-k call on one MI355X.
 
 A step is one whole top-k call (select kernel over every row slice, then the merge kernel)
-over one batch of synthetic input already resident in HBM. Timing: W warmup steps, then K
-steps between two events on the launch stream, each step reading a different copy of the
-input from a pool of >= 512 MiB, so the 256 MB Infinity Cache cannot serve it (cold). The
-same loop over one buffer is reported as the warm figure. Events around every launch give
-the select kernel's own average duration (the roofline figure). The CPU oracle is timed on
-the host cores on a bounded sample of the same workload.
+over one batch of synthetic input already resident in HBM. Each step reads a different copy
+of the input from a pool of >= 512 MiB, so the 256 MB Infinity Cache cannot serve it (cold).
+Timing: W warmup steps, then K steps recorded into one HIP graph and replayed between two
+events (the headline: no host launch gaps); then the same K steps launched one by one with
+events around every select launch (the select kernel's own average duration, the roofline
+figure). The same loop over one buffer is reported as the warm figure. The CPU oracle is
+timed on the host cores on a bounded sample of the same workload.
+
+Two more modes serve the committed rocprofv3 counter summary: --counter-pass runs the
+select kernel and a calibration copy of known size under the profiler, and
+--write-counters turns the profiler's FETCH_SIZE / WRITE_SIZE tables into that summary.
 
 Prints ONE JSON line.
 """
@@ -112,10 +117,36 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
         sel = [a.elapsed_time(b) for a, b in mids]
         return total / steps, sum(sel) / len(sel)
 
+    def graph_timed(get_src):
+        """K steps captured into one graph, replayed once between two events."""
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            step(get_src(0))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            for i in range(steps):
+                step(get_src(i))
+        torch.cuda.synchronize()
+        g.replay()  # warm the graph once
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
     ms_cold, sel_cold = timed(lambda i: pool[i % copies])
-    log(f"[bench] {w.name} cold: {ms_cold * 1e3:.2f} us/call, select {sel_cold * 1e3:.2f} us")
+    log(f"[bench] {w.name} cold eager: {ms_cold * 1e3:.2f} us/call, select {sel_cold * 1e3:.2f} us")
     ms_warm, sel_warm = timed(lambda i: pool[0])
-    log(f"[bench] {w.name} warm: {ms_warm * 1e3:.2f} us/call, select {sel_warm * 1e3:.2f} us")
+    log(f"[bench] {w.name} warm eager: {ms_warm * 1e3:.2f} us/call, select {sel_warm * 1e3:.2f} us")
+    ms_graph = graph_timed(lambda i: pool[i % copies])
+    log(f"[bench] {w.name} cold graph: {ms_graph * 1e3:.2f} us/call")
+    ms_graph_warm = graph_timed(lambda i: pool[0])
+    log(f"[bench] {w.name} warm graph: {ms_graph_warm * 1e3:.2f} us/call")
 
     parity = None
     if verify:
@@ -130,8 +161,107 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
         parity = "bit-exact" if ok else "MISMATCH"
         log(f"[bench] {w.name} parity vs oracle: {parity}")
     del pool
-    return dict(x=x, plan=plan, copies=copies, ms_cold=ms_cold, sel_cold=sel_cold, ms_warm=ms_warm,
-                sel_warm=sel_warm, in_bytes=in_bytes, parity=parity, ws_bytes=wsb)
+    return dict(x=x, plan=plan, copies=copies, ms_cold=ms_graph, ms_eager=ms_cold, sel_cold=sel_cold,
+                ms_warm=ms_graph_warm, ms_warm_eager=ms_warm, sel_warm=sel_warm, in_bytes=in_bytes, parity=parity,
+                ws_bytes=wsb)
+
+
+CALIB_BYTES = 256 * 2 ** 20  # calibration copy: reads and writes exactly this many bytes
+
+
+def counter_pass(ts, torch, w, k, launches, pool_mib):
+    """Workload for a rocprofv3 --pmc run: `launches` cold select launches (plus merges), then
+    three calibration copies of CALIB_BYTES with the plain copy kernel."""
+    x = w.make()
+    xd = upload(x, torch)
+    copies = max(1, math.ceil(pool_mib * 2 ** 20 / w.input_bytes()))
+    pool = [xd] + [xd.clone() for _ in range(copies - 1)]
+    rows, n = w.rows, w.n
+    wsb = ts.ds_topk_workspace_size(rows, n, k, w.dtype)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    vals = torch.empty((rows, k), dtype=xd.dtype, device="cuda")
+    idx = None if w.values_only else torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    for i in range(launches):
+        ts.ds_topk_slices(pool[i % copies], k, seed=1, workspace=ws, out_vals=vals, out_idx=idx,
+                          indices=idx is not None)
+        ts.ds_topk_merge(rows, n, k, w.dtype, seed=1, workspace=ws, out_vals=vals, out_idx=idx)
+    torch.cuda.synchronize()
+    del pool
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        ts.ds_probe_copy(dst, src)
+    torch.cuda.synchronize()
+    log(f"[bench] counter pass done: {launches} select launches of {w.name}, 3 copies of {CALIB_BYTES} B")
+
+
+def read_counter_csv(folder, counter):
+    """Mean per-dispatch value of `counter` for the select kernel and the calibration copy."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                kind = "select" if "select_kernel" in name else ("copy" if "probe_copy_kernel" in name else None)
+                if kind is None:
+                    continue
+                key = (kind, row.get("Dispatch_Id"))
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for kind in ("select", "copy"):
+        vals = [v for (kd, _), v in per.items() if kd == kind]
+        out[kind] = (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+    return out
+
+
+def write_counters(workload, fetch_dir, write_dir, command):
+    """Summary of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE), scaled by the copy's."""
+    from workloads import gen
+    w = gen.WORKLOADS[workload]
+    f = read_counter_csv(fetch_dir, "FETCH_SIZE")
+    wr = read_counter_csv(write_dir, "WRITE_SIZE")
+    (fs, nfs), (fc, nfc) = f["select"], f["copy"]
+    (ws_, nws), (wc, nwc) = wr["select"], wr["copy"]
+    if None in (fs, fc, ws_, wc):
+        raise SystemExit("counter tables lack the select or the copy kernel")
+    kf = CALIB_BYTES / (fc * 1024.0)   # bytes per reported KiB, from the copy's known reads
+    kw = CALIB_BYTES / (wc * 1024.0)
+    rd = fs * 1024.0 * kf
+    wt = ws_ * 1024.0 * kw
+    total = rd + wt
+    algo = w.input_bytes()
+    digest = source_digest()
+    lines = [
+        f"# select_kernel HBM traffic, {workload}",
+        "",
+        f"Workload: {w.description}. Algorithmic bytes per launch (the input, read once): {algo}.",
+        "",
+        "Commands (rocprofv3 3.x on one MI355X; counters in runs of their own):",
+        "",
+        "```",
+        command.replace("COUNTER", "FETCH_SIZE"),
+        command.replace("COUNTER", "WRITE_SIZE"),
+        "```",
+        "",
+        "| counter | select_kernel (KiB/dispatch, mean) | dispatches | copy of 256 MiB (KiB/dispatch) | bytes per KiB |",
+        "|---|---|---|---|---|",
+        f"| FETCH_SIZE | {fs:.1f} | {nfs} | {fc:.1f} | {kf:.4f} |",
+        f"| WRITE_SIZE | {ws_:.1f} | {nws} | {wc:.1f} | {kw:.4f} |",
+        "",
+        f"Read bytes per launch (scaled): {rd:.0f} = {rd / algo:.4f} x the input.",
+        f"Written bytes per launch (scaled): {wt:.0f}.",
+        "",
+        f"traffic: source={digest} bytes_per_launch={total:.0f} read_bytes={rd:.0f} write_bytes={wt:.0f}",
+        "",
+    ]
+    path = os.path.join(ROOT, "profiles", f"select_kernel_{workload}_counters.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    log(f"[bench] wrote {path}: {total:.0f} B per launch ({total / algo:.3f} x algorithmic)")
 
 
 def cpu_baseline(w, k, x, seconds):
@@ -161,7 +291,15 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="run select launches and a calibration copy for a rocprofv3 --pmc run, then exit")
+    ap.add_argument("--write-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
+                    help="summarise two rocprofv3 --pmc output folders into profiles/ (no GPU needed)")
     args = ap.parse_args()
+
+    if args.write_counters:
+        write_counters(args.workload, *args.write_counters)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across GPUs "
@@ -175,6 +313,9 @@ def main() -> int:
     torch.cuda.set_device(0)
     w = gen.WORKLOADS[args.workload]
     k = args.k or w.ks[0]
+    if args.counter_pass:
+        counter_pass(ts, torch, w, k, args.steps, args.pool_mib)
+        return 0
     r = time_workload(ts, torch, w, k, args.steps, args.warmup, args.pool_mib)
     value = r["in_bytes"] / (r["ms_cold"] * 1e-3) / 1e9
     sel_gbs = r["in_bytes"] / (r["sel_cold"] * 1e-3) / 1e9
@@ -198,6 +339,9 @@ def main() -> int:
                    "slices": r["plan"]["slices"], "waves": r["plan"]["waves"], "input_pool_copies": r["copies"],
                    "cold_inputs": True, "description": w.description},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "timing": "K steps captured in one HIP graph, replayed between two events",
+        "eager": {"value": round(r["in_bytes"] / (r["ms_eager"] * 1e-3) / 1e9, 2),
+                  "ms_per_step": round(r["ms_eager"], 6), "note": "the same K steps launched one by one"},
         "warm": {"value": round(r["in_bytes"] / (r["ms_warm"] * 1e-3) / 1e9, 2), "ms_per_step": round(r["ms_warm"], 6),
                  "note": "same input buffer every step (may be served by the Infinity Cache)"},
         "pages_style_gbs": round((r["in_bytes"] + w.rows * k * (w.elem_bytes + (0 if w.values_only else 4)))
