@@ -59,12 +59,25 @@ extern "C" {
  *   slack   B2: the buffer is compacted when it holds >= k + B2 entries (B2 >= 1).
  *   slices  S: workgroups per row (the split-row path when > 1).
  *   waves   64-lane waves per workgroup.
+ *   presample  the threshold before the first compaction: DS_PRESAMPLE_OFF starts from
+ *              "accept everything" as the design note does, so the first block fills the
+ *              buffer; DS_PRESAMPLE_ON starts from a lower bound of the first block's k-th
+ *              largest element (each wave takes the ceil(k/waves)-th largest of its lanes'
+ *              maxima, and the bound is the smallest of those, so at least k elements of
+ *              the block reach it), and the block only appends the elements that reach it.
+ *              ON needs k <= 64 * waves and a whole first block; otherwise the plan falls
+ *              back to OFF. Zero (auto) means ON. The result is the same either way.
  */
+#define DS_PRESAMPLE_AUTO 0
+#define DS_PRESAMPLE_OFF 1
+#define DS_PRESAMPLE_ON 2
+
 typedef struct ds_config {
   int32_t block;
   int32_t slack;
   int32_t slices;
   int32_t waves;
+  int32_t presample;
 } ds_config;
 
 /*
@@ -87,7 +100,7 @@ typedef struct ds_stats {
   uint64_t t_compact_ns; /* time in in-loop compactions */
   uint64_t t_sync_ns;   /* time in the per-block barrier */
   uint64_t t_final_ns;  /* time in the final compaction and output */
-  uint64_t reserved;
+  uint64_t passes;      /* histogram passes of all compactions, the final one included */
 } ds_stats;
 
 /*
@@ -125,8 +138,13 @@ int ds_topk_workspace_size(int64_t rows, int64_t n, int k, int dtype, const ds_c
 
 /*
  * ds_topk_ex -- ds_topk with a caller workspace, a forced configuration and counters.
- *   workspace  device, >= ds_topk_workspace_size bytes, 256-byte aligned; may be NULL when
- *              that size is 0. Its contents on entry do not matter; it is overwritten.
+ *   workspace  device, >= ds_topk_workspace_size bytes, 16-byte aligned; may be NULL when
+ *              that size is 0. It must be zero-filled before its first use: its first
+ *              64 KiB hold per-row arrival counters (with 2..8 slices per row the last slice
+ *              of a row to finish merges the row), every completed call leaves them at zero,
+ *              and no call writes anything else there, so a workspace can be reused for any
+ *              later call without clearing it again. Calls that share a workspace must not
+ *              overlap in time.
  *   cfg        NULL or fields to force (see ds_config).
  *   stats      NULL, or device [rows, slices] ds_stats filled by the select kernel.
  * Allocates nothing.
@@ -138,9 +156,10 @@ int ds_topk_ex(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k
 /*
  * ds_topk_slices / ds_topk_merge -- ds_topk_ex as its two launches, for callers that
  * want to time or overlap them separately. ds_topk_slices runs the select kernel: with one
- * slice per row it writes the final outputs; otherwise it writes every slice's k survivors
- * to the workspace. ds_topk_merge then reduces each row's survivors to the sorted top-k
- * (it enqueues nothing when the plan has one slice). Both take the same arguments as
+ * slice per row, or with 2..8 slices whose sorted lists fit in the workgroup's LDS (the
+ * last slice of each row merges them), it writes the final outputs; otherwise it writes
+ * every slice's k survivors to the workspace and ds_topk_merge reduces each row's
+ * survivors to the sorted top-k (it enqueues nothing in the other cases). Both take the same arguments as
  * ds_topk_ex (merge ignores x, row_stride and stats) and must be given the same rows, n, k,
  * dtype, seed, cfg and workspace; the pair then equals one ds_topk_ex call.
  */

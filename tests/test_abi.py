@@ -70,7 +70,8 @@ def test_forced_plans(dtype, n, k, slices):
     per = -(-n // slices)
     assert p["slices"] == -(-n // (-(-per // p["block"]) * p["block"]))
     ws = ts.ds_topk_workspace_size(8, n, k, dtype, {"slices": slices})
-    assert ws == (0 if slices == 1 else 8 * ((slices * k + 1) // 2 * 2) * 8)
+    # 64 KiB of per-row arrival counters, then the slice lists
+    assert ws == (0 if slices == 1 else 65536 + 8 * ((slices * k + 1) // 2 * 2) * 8)
 
 
 def test_forced_block_sizes():
@@ -81,3 +82,26 @@ def test_forced_block_sizes():
     with pytest.raises(ts.DSError) as e:  # too many slices for the row: one would be empty
         ts.ds_topk_plan(1, 4096, 16, ts.FP32, {"slices": 64})
     assert e.value.status == ts.DS_ERR_UNSUPPORTED
+
+
+def test_config_struct_matches_header():
+    """The binding's ds_config has the header's fields in the header's order."""
+    import re
+    text = open(ts._binding.HEADER_PATH).read()
+    body = re.search(r"typedef struct ds_config \{(.*?)\} ds_config;", text, re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [f for f, _ in ts._binding.ds_config._fields_]
+    assert ctypes.sizeof(ts._binding.ds_config) == 4 * len(fields)
+
+
+def test_presample_plan_field():
+    on = ts.ds_topk_plan(64, 131072, 512, ts.BF16, {"slices": 4})
+    assert on["presample"] == ts.PRESAMPLE_ON
+    off = ts.ds_topk_plan(64, 131072, 512, ts.BF16, {"slices": 4, "presample": ts.PRESAMPLE_OFF})
+    assert off["presample"] == ts.PRESAMPLE_OFF
+    # k above 64 per wave of the workgroup: no presampled threshold
+    big = ts.ds_topk_plan(8, 1 << 20, 4096, ts.BF16, {"slices": 8, "waves": 4})
+    assert big["presample"] == ts.PRESAMPLE_OFF
+    with pytest.raises(ts.DSError) as e:
+        ts.ds_topk_plan(4, 32768, 512, ts.BF16, {"presample": 3, "slices": 1})
+    assert e.value.status == ts.DS_ERR_INVALID_ARG

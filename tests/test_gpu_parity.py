@@ -121,10 +121,11 @@ def test_fuzz():
 ])
 def test_counters_match_model(dtype, n, k, block, slack, slices):
     """The kernel's A, R, W, max buffer length and read checksums equal the CPU model's under
-    the same Feistel block order, B, B2 and slicing."""
+    the same Feistel block order, B, B2 and slicing (with the design note's start: no
+    presampled threshold)."""
     x = gen.rows_family("normal", dtype, 17, 2, n)
     x[1] = gen.rows_family("ascending", dtype, 18, 1, n)[0]
-    cfg = {"block": block, "slack": slack, "slices": slices}
+    cfg = {"block": block, "slack": slack, "slices": slices, "presample": ts.PRESAMPLE_OFF}
     seed = 99
     say(f"[gpu] counters: n={n} k={k} cfg={cfg}")
     gv, gi, (plan, st) = run_gpu(x, k, seed=seed, cfg=cfg, stats=True)
@@ -147,3 +148,84 @@ def test_counters_match_model(dtype, n, k, block, slack, slices):
             assert (int(g["appended"]), int(g["compactions"]), int(g["work"]), int(g["max_len"])) == \
                 (ms.A, ms.R, ms.W, ms.max_len), (r, s)
             assert int(g["max_len"]) <= k + plan["slack"] + plan["block"] - 1
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+def test_fused_merge_reuse_and_graph_replays(dtype):
+    """Split rows merged inside the select kernel (the last slice of a row merges): the per-row
+    arrival counters at the end of the workspace are zero after every call, so repeated calls
+    on one workspace, and replays of a captured graph with eager work in between, all give
+    the oracle's result."""
+    import torch
+    from gpu_util import to_device, to_numpy_vals
+    rows, n, k, cfg = 6, 60000, 300, {"slices": 4}
+    x = gen.rows_family("normal", dtype, 31, rows, n)
+    wv, wi = otk.topk(x, k)
+    xd = to_device(x)
+    wsb = ts.ds_topk_workspace_size(rows, n, k, dtype, cfg)
+    assert wsb == 65536 + rows * ((cfg["slices"] * k + 1) // 2 * 2) * 8
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    vals = torch.empty((rows, k), dtype=xd.dtype, device="cuda")
+    idx = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+
+    def check(label):
+        torch.cuda.synchronize()
+        assert_same(x, k, to_numpy_vals(vals), idx.cpu().numpy(), wv, wi, label)
+        assert int(ws[:65536].count_nonzero()) == 0, label
+
+    for rep in range(3):
+        say(f"[gpu] fused merge eager call {rep}")
+        idx.fill_(-1)
+        ts.ds_topk_ex(xd, k, seed=rep, workspace=ws, cfg=cfg, out_vals=vals, out_idx=idx)
+        check(f"eager#{rep}")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ts.ds_topk_ex(xd, k, seed=7, workspace=ws, cfg=cfg, out_vals=vals, out_idx=idx)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ts.ds_topk_ex(xd, k, seed=7, workspace=ws, cfg=cfg, out_vals=vals, out_idx=idx, stream=s)
+    for rep in range(3):
+        say(f"[gpu] fused merge graph replay {rep}")
+        idx.fill_(-1)
+        vals.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        check(f"replay#{rep}")
+    # other plans on the same workspace: fewer rows with another k and slice count (fused),
+    # then more slices than the fused merge takes (the merge kernel), then this plan again
+    for label, xo, ko, co in [("other-fused", gen.rows_family("ties", dtype, 32, 3, 40000), 100, {"slices": 2}),
+                              ("merge-kernel", gen.rows_family("normal", dtype, 33, 2, 16384), 64,
+                               {"block": 1024, "slices": 16})]:
+        say(f"[gpu] fused merge workspace reuse: {label}")
+        assert ts.ds_topk_workspace_size(xo.shape[0], xo.shape[1], ko, dtype, co) <= wsb
+        gv, gi = ts.ds_topk_ex(to_device(xo), ko, seed=3, workspace=ws, cfg=co)
+        torch.cuda.synchronize()
+        ov, oi = otk.topk(xo, ko)
+        assert_same(xo, ko, to_numpy_vals(gv), gi.cpu().numpy(), ov, oi, label)
+        assert int(ws[:65536].count_nonzero()) == 0, label
+    idx.fill_(-1)
+    ts.ds_topk_ex(xd, k, seed=5, workspace=ws, cfg=cfg, out_vals=vals, out_idx=idx)
+    check("after-other-plans")
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+@pytest.mark.parametrize("family", ["normal", "ascending", "ties", "constant", "specials"])
+def test_presample_on_and_off(dtype, family):
+    """A presampled first threshold never drops a top-k element: both starts give the oracle's
+    result; on i.i.d. rows the presampled start appends far fewer elements."""
+    rows, n, k = 4, 65536, 512
+    x = gen.rows_family(family, dtype, 41, rows, n)
+    wv, wi = otk.topk(x, k)
+    res = {}
+    for mode in (ts.PRESAMPLE_OFF, ts.PRESAMPLE_ON):
+        cfg = {"slices": 1, "presample": mode}
+        assert ts.ds_topk_plan(rows, n, k, dtype, cfg)["presample"] == mode
+        say(f"[gpu] presample={mode} {family} dtype={dtype}")
+        gv, gi, (plan, st) = run_gpu(x, k, seed=5, cfg=cfg, stats=True)
+        assert_same(x, k, gv, gi, wv, wi, f"presample={mode} {family}")
+        res[mode] = st
+    for r in range(rows):
+        assert int(res[ts.PRESAMPLE_ON][r, 0]["reads"]) == n
+        if family == "normal":
+            assert 2 * int(res[ts.PRESAMPLE_ON][r, 0]["appended"]) < int(res[ts.PRESAMPLE_OFF][r, 0]["appended"])

@@ -25,6 +25,7 @@ DS_ERR_WORKSPACE = -4
 DS_ERR_LAUNCH = -5
 DS_ERR_DEVICE = -6
 DS_MAX_K = 4096
+PRESAMPLE_AUTO, PRESAMPLE_OFF, PRESAMPLE_ON = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdstopk.so")
@@ -39,11 +40,11 @@ class DSError(RuntimeError):
 
 class ds_config(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("slack", ctypes.c_int32), ("slices", ctypes.c_int32),
-                ("waves", ctypes.c_int32)]
+                ("waves", ctypes.c_int32), ("presample", ctypes.c_int32)]
 
 
 STATS_FIELDS = ["appended", "compactions", "work", "max_len", "reads", "index_sum", "monotone", "slice_lo",
-                "slice_len", "block", "slack", "t_total_ns", "t_compact_ns", "t_sync_ns", "t_final_ns", "reserved"]
+                "slice_len", "block", "slack", "t_total_ns", "t_compact_ns", "t_sync_ns", "t_final_ns", "passes"]
 STATS_DTYPE = np.dtype([(f, np.uint64) for f in STATS_FIELDS])
 
 _lock = threading.Lock()
@@ -100,7 +101,7 @@ def _cfg(cfg: Optional[Dict[str, int]]):
     if cfg is None:
         return None
     c = ds_config(int(cfg.get("block", 0)), int(cfg.get("slack", 0)), int(cfg.get("slices", 0)),
-                  int(cfg.get("waves", 0)))
+                  int(cfg.get("waves", 0)), int(cfg.get("presample", 0)))
     return ctypes.pointer(c)
 
 
@@ -109,7 +110,8 @@ def ds_topk_plan(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, 
     st = lib().ds_topk_plan(rows, n, k, dtype, _cfg(cfg), ctypes.byref(out))
     if st != DS_OK:
         raise DSError(st, "ds_topk_plan")
-    return {"block": out.block, "slack": out.slack, "slices": out.slices, "waves": out.waves}
+    return {"block": out.block, "slack": out.slack, "slices": out.slices, "waves": out.waves,
+            "presample": out.presample}
 
 
 def ds_topk_workspace_size(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, int]] = None) -> int:

@@ -40,9 +40,13 @@ struct Plan {
   int64_t slice_len;
   int sort_cap;
   size_t lds;
-  // merge (slices > 1)
+  bool presample;   // the first whole block sets a presampled threshold
+  // merge (slices > 1): fused into the select kernel (the row's last slice merges sorted
+  // slice lists) or the merge kernel
+  bool fused;
   int mslack;
   size_t mlds;
+  size_t ws_lists;  // bytes of the slice lists (after the counter area)
   size_t ws_bytes;
 };
 
@@ -73,8 +77,10 @@ int check_basic(int64_t rows, int64_t n, int k, int dtype) {
 int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK) return st;
-  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0};
+  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0};
   if (c.block < 0 || c.slack < 0 || c.slices < 0 || c.waves < 0) return DS_ERR_INVALID_ARG;
+  if (c.presample != DS_PRESAMPLE_AUTO && c.presample != DS_PRESAMPLE_OFF && c.presample != DS_PRESAMPLE_ON)
+    return DS_ERR_INVALID_ARG;
   const int chunk = chunk_elems(dtype);
   const int eb = elem_bytes(dtype);
 
@@ -159,6 +165,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   p.slice_len = slice_len;
   p.sort_cap = sort_cap;
   p.lds = lds;
+  p.presample = c.presample != DS_PRESAMPLE_OFF && k <= 64 * kSelectShapes[shape].waves;
   if (slices > 1) {
     int ms = k > kMergeBlock ? k : kMergeBlock;
     if (ms + kMergeBlock < sort_cap) ms = sort_cap - kMergeBlock;
@@ -167,7 +174,12 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
     if (static_cast<int64_t>(p.mlds) > kMaxLdsBytes) return DS_ERR_UNSUPPORTED;
     const int64_t entries = slices * static_cast<int64_t>(k);
     if (entries * 8 > kMaxSliceBytes) return DS_ERR_UNSUPPORTED;
-    p.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>((entries + 1) & ~int64_t(1)) * 8;
+    p.ws_lists = static_cast<size_t>(rows) * static_cast<size_t>((entries + 1) & ~int64_t(1)) * 8;
+    p.fused = slices <= ds::kMaxFusedSlices && rows <= ds::kArriveCounters &&
+              static_cast<size_t>(entries) * 8 <= lds - ds::select_scalars_bytes();
+    // every split plan has the same layout: the fused merge's arrival counters first, the
+    // slice lists after them, so no plan's lists overlap another plan's counters
+    p.ws_bytes = ds::kArriveBytes + p.ws_lists;
   }
   *out = p;
   return DS_OK;
@@ -199,20 +211,22 @@ int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t r
   sp.slack = pl.slack;
   sp.sort_cap = pl.sort_cap;
   sp.seed = seed;
-  sp.ws = static_cast<uint2*>(ws);
+  sp.ws = ws ? reinterpret_cast<uint2*>(static_cast<uint8_t*>(ws) + ds::kArriveBytes) : nullptr;
   sp.ws_row_entries = (static_cast<int64_t>(pl.slices) * k + 1) & ~int64_t(1);
   sp.out_vals = out_vals;
   sp.out_idx = out_idx;
   sp.stats = stats;
+  sp.arrive = pl.fused ? static_cast<uint32_t*>(ws) : nullptr;
+  sp.presample = pl.presample ? 1 : 0;
   return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }
 
 int run_merge(const Plan& pl, int64_t rows, int64_t n, int k, uint64_t seed, void* out_vals, int32_t* out_idx,
               void* ws, hipStream_t stream) {
-  if (pl.slices <= 1) return DS_OK;
+  if (pl.slices <= 1 || pl.fused) return DS_OK;
   (void)hipGetLastError();
   ds::MergeParams mp{};
-  mp.ws = static_cast<const uint2*>(ws);
+  mp.ws = reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(ws) + ds::kArriveBytes);
   mp.entries = static_cast<int64_t>(pl.slices) * k;
   mp.row_entries = (mp.entries + 1) & ~int64_t(1);
   mp.n = n;
@@ -303,6 +317,7 @@ int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg
   out->slack = p.slack;
   out->slices = p.slices;
   out->waves = kSelectShapes[p.shape].waves;
+  out->presample = p.presample ? DS_PRESAMPLE_ON : DS_PRESAMPLE_OFF;
   return DS_OK;
 }
 
@@ -381,6 +396,11 @@ int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, i
       }
       void* ptr = nullptr;
       if (hipMalloc(&ptr, p.ws_bytes) != hipSuccess) return DS_ERR_LAUNCH;
+      // the fused merge's counters start at zero (and every call leaves them at zero)
+      if (hipMemset(ptr, 0, p.ws_bytes) != hipSuccess) {
+        (void)hipFree(ptr);
+        return DS_ERR_LAUNCH;
+      }
       slot = {ptr, p.ws_bytes};
     }
     ws = slot.first;

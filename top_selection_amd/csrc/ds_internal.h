@@ -27,6 +27,8 @@ struct SelectParams {
   void* out_vals;            // slices == 1: sorted output values [rows][k]
   int32_t* out_idx;          // slices == 1: sorted output indices [rows][k]
   ds_stats* stats;           // NULL or [rows][slices]
+  uint32_t* arrive;          // fused merge: per-row arrival counters (zero between calls), else NULL
+  int32_t presample;         // nonzero: the first whole block sets a presampled threshold
 };
 
 // One workgroup per row runs DeepSelect over the row's slices*k survivors.
@@ -55,8 +57,19 @@ constexpr Shape kSelectShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}, {8, 2}, {4, 4
 constexpr int kNumSelectShapes = sizeof(kSelectShapes) / sizeof(kSelectShapes[0]);
 constexpr Shape kMergeShape = {4, 4};  // 4 waves x 4 chunks x 128 entries = 2048 entries per block
 
-// LDS bytes a select/merge workgroup needs.
+// LDS bytes a select/merge workgroup needs, and the part of them that is not the dynamic
+// array (the per-workgroup scalars).
 size_t select_lds_bytes(int k, int block, int slack, int waves);
+size_t select_scalars_bytes();
+
+// Split rows with at most this many slices merge inside the select kernel (the last slice of
+// a row to finish merges the sorted slice lists); more slices use the merge kernel.
+constexpr uint32_t kMaxFusedSlices = 8;
+
+// Split-row workspace layout: kArriveBytes of per-row arrival counters (the fused merge's;
+// zero between calls), then the slice lists. Fused plans need rows <= kArriveCounters.
+constexpr size_t kArriveBytes = 64 * 1024;
+constexpr int64_t kArriveCounters = kArriveBytes / 4;
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,

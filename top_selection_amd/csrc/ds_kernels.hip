@@ -52,6 +52,14 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_
   return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0);
 }
 
+// The same LDS location as an LDS-address-space pointer: accesses through it are always LDS
+// instructions (a generic pointer the compiler cannot trace becomes a flat access, which also
+// counts as an outstanding global access and makes the compiler wait for every global load).
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds_ptr(T* p) {
+  return (__attribute__((address_space(3))) T*)p;
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 __device__ __forceinline__ uint32_t mbcnt(uint64_t m, uint32_t base) {
@@ -123,6 +131,16 @@ __device__ __forceinline__ uint32_t wave_max32(uint32_t x) {
   return __builtin_amdgcn_readlane(x, 63);
 }
 
+__device__ __forceinline__ uint32_t wave_min32(uint32_t x) {
+  x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x111, 0xF, 0xF, false)));
+  x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x112, 0xF, 0xF, false)));
+  x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x114, 0xF, 0xF, false)));
+  x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x118, 0xF, 0xF, false)));
+  x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x142, 0xA, 0xF, false)));
+  x = min(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(~0u, x, 0x143, 0xC, 0xF, false)));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 __device__ __forceinline__ uint32_t u4get(const uint4& v, uint32_t q) {
   return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
@@ -130,6 +148,9 @@ __device__ __forceinline__ uint32_t u4get(const uint4& v, uint32_t q) {
 __device__ __forceinline__ uint32_t bitlen32(uint32_t v) {
   return v ? 32u - static_cast<uint32_t>(__builtin_clz(v)) : 0u;
 }
+
+constexpr uint32_t kLogBins = 11;
+constexpr uint32_t kBins = 1u << kLogBins;  // histogram bins of one radix pass
 
 // --------------------------------------------------------------------------- keys
 // Order-preserving key of a raw element (bf16: the 16 bits in the low half).
@@ -167,6 +188,68 @@ __device__ __forceinline__ uint32_t raw_of_key(uint32_t key) {
 
 __device__ __forceinline__ uint64_t comp_of(uint32_t key, uint32_t idx) {
   return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~idx);
+}
+
+// Key of +infinity: keys above it are NaN patterns, which never occur.
+template <int DT>
+constexpr uint32_t key_of_inf() {
+  return DT == DS_BF16 ? 0xFF80u : 0xFF800000u;
+}
+
+template <int DT>
+__device__ __forceinline__ float value_of_key(uint32_t key) {
+  if constexpr (DT == DS_BF16)
+    return __uint_as_float(raw_of_key<DT>(key) << 16);
+  else
+    return __uint_as_float(raw_of_key<DT>(key));
+}
+
+// Value-space bins: bin(v) = clamp((v - lo) * scale, 0, kBins - 1), truncated, for a window
+// [lo, hi] with scale = kBins / (hi - lo). Each step is a correctly rounded fp32 operation
+// (no contraction), so the bin is a non-decreasing function of the key and every thread that
+// evaluates it gets the same bin; values above hi land in the top bin.
+struct VBins {
+  float lo, scale;
+};
+
+template <int DT>
+__device__ __forceinline__ uint32_t vbin(uint32_t key, const VBins& vb) {
+#pragma clang fp contract(off)
+  const float t = (value_of_key<DT>(key) - vb.lo) * vb.scale;
+  return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(t, 0.0f, static_cast<float>(kBins - 1u)));
+}
+
+// Window [lo, hi] from two keys; false when value bins cannot be used (an infinite bound or
+// span, an empty span, or a scale that overflows).
+template <int DT>
+__device__ __forceinline__ bool vbins_of(uint32_t klo, uint32_t khi, VBins& vb) {
+  const float lo = value_of_key<DT>(klo), hi = value_of_key<DT>(khi);
+  const float span = hi - lo;
+  vb.lo = lo;
+  vb.scale = static_cast<float>(kBins) / span;
+  return __builtin_isfinite(lo) && __builtin_isfinite(hi) && span > 0.0f && __builtin_isfinite(span) &&
+         __builtin_isfinite(vb.scale) && vb.scale > 0.0f;
+}
+
+// Smallest key K in [klo, kmax] with vbin(K) >= b, or kmax + 1 if there is none: a 64-way
+// search by one wave (each round the lanes probe 64 evenly spaced keys).
+template <int DT>
+__device__ __forceinline__ uint64_t vbin_first_key(uint32_t b, uint32_t klo, uint32_t kmax, const VBins& vb,
+                                                   uint32_t lane) {
+  uint64_t lo = klo, cnt = static_cast<uint64_t>(kmax) - klo + 1u;  // the answer lies in [lo, lo + cnt]
+  while (cnt > 0) {
+    const uint64_t step = (cnt + 63u) / 64u;
+    const uint64_t off = lane * step;
+    const bool probe = off < cnt;
+    const bool ok = probe && vbin<DT>(static_cast<uint32_t>(lo + off), vb) >= b;
+    const uint32_t j = popc(ballot(probe && !ok));  // the failing probes are a prefix
+    if (j == 0) break;
+    const uint64_t nlo = lo + (j - 1u) * step + 1u;
+    const uint64_t hi_j = lo + j * step, end = lo + cnt;
+    cnt = (hi_j < end ? hi_j : end) - nlo;
+    lo = nlo;
+  }
+  return lo;
 }
 
 // --------------------------------------------------------------------------- block order
@@ -225,8 +308,6 @@ struct BlockOrder {
 
 // --------------------------------------------------------------------------- shared state
 constexpr int kMaxWaves = 16;
-constexpr uint32_t kLogBins = 11;
-constexpr uint32_t kBins = 1u << kLogBins;  // histogram bins of one radix pass
 constexpr uint32_t kPer = kBins / 64;       // bins per lane in the bin scan
 constexpr uint32_t kListCap = 64;           // pivot-bin entries ranked with lane reads
 constexpr uint32_t kOrdCap = 1024;          // block-order table entries (longer streams compute it)
@@ -235,14 +316,18 @@ struct Scalars {
   uint32_t blk[3];             // entries appended by block i, at blk[i % 3]
   uint32_t outpos;             // scatter cursor of the running compaction
   uint32_t listpos;            // pivot-list cursor of the running compaction
-  uint32_t pub[4];             // bin scan result: bin, entries above it, entries in it, max key
+  uint32_t pub[6];             // bin scan result: bin, entries above it, entries in it, max key,
+                               // and the key bounds of a value-space bin
   uint32_t red[kMaxWaves];     // per-wave maximum keys
+  uint32_t rmin[kMaxWaves];    // per-wave smallest / largest key appended before the first
+  uint32_t rmax[kMaxWaves];    // compaction
   uint32_t lkey[kListCap];     // pivot-bin entries
   uint32_t lidx[kListCap];
   // counters (stats runs only; thread 0 keeps them): appended A, compactions R, work W,
   // largest buffer, threshold monotone, compaction time, block barrier time, start of the
   // final compaction, elements read and the sum of their indices
   unsigned long long st_a, st_r, st_w, st_max, st_mono, st_tc, st_ts, st_tf, reads, index_sum;
+  uint32_t st_p;  // histogram passes (counted in every run; reported in stats runs)
 };
 
 __host__ __device__ constexpr uint32_t round4(uint32_t v) { return (v + 3u) & ~3u; }
@@ -368,62 +453,106 @@ __device__ __forceinline__ void scan_select(const uint32_t* h, uint32_t need, ui
 // Barriers: two per histogram pass (after the counts; after the scan result is published),
 // one after the scatter and one after the list is ranked.
 
-// Histogram of one segment's keys (n entries from kp) over the window. With conv the segment
-// holds raw scores, which are replaced by their keys on the way.
+// Group g of the compaction's entries: the appended segment's groups come first, then the
+// survivors'. Sets the group's key and index pointers and returns how many of its four
+// slots hold entries (the slots up to a multiple of four exist).
+__device__ __forceinline__ uint32_t group_at(const Segs& sg, uint32_t g, uint32_t g1, uint32_t*& kp, uint32_t*& ip) {
+  const bool app = g < g1;
+  const uint32_t h = app ? g : g - g1;
+  kp = (app ? sg.k1 : sg.k0) + 4u * h;
+  ip = (app ? sg.i1 : sg.i0) + 4u * h;
+  return min(4u, (app ? sg.n1 : sg.n0) - 4u * h);
+}
+
+// Histogram of all entries: value bins (vm), else key bins over the window; with raw, appended
+// entries hold raw scores, which are replaced by their keys on the way. Returns this thread's
+// largest key. Two groups per step, so both reads are in flight together.
 template <int DT>
-__device__ __forceinline__ uint32_t hist_keys(uint32_t* kp, uint32_t n, uint32_t tid, uint32_t nt, uint32_t plo,
-                                              uint32_t phi, bool open, uint32_t shift, uint32_t* h, bool conv) {
+__device__ __forceinline__ uint32_t hist_all(const Segs& sg, uint32_t tid, uint32_t nt, uint32_t plo, uint32_t phi,
+                                             bool open, uint32_t shift, uint32_t* h, bool raw, bool vm,
+                                             const VBins& vb) {
+  const uint32_t g1 = (sg.n1 + 3u) / 4u, groups = g1 + (sg.n0 + 3u) / 4u;
   uint32_t mx = 0;
-  for (uint32_t g = tid; 4u * g < n; g += nt) {
-    uint4 kk = *reinterpret_cast<const uint4*>(kp + 4u * g);
-    if (conv) {
-      kk = make_uint4(key_of_score<DT>(kk.x), key_of_score<DT>(kk.y), key_of_score<DT>(kk.z), key_of_score<DT>(kk.w));
-      *reinterpret_cast<uint4*>(kp + 4u * g) = kk;
+  for (uint32_t g = tid; g < groups; g += 2u * nt) {
+    uint4 kk[2];
+    uint32_t nv[2];
+    uint32_t* kp[2];
+#pragma unroll
+    for (uint32_t u = 0; u < 2; ++u) {
+      const uint32_t gu = g + u * nt;
+      uint32_t* ip;
+      nv[u] = 0;
+      kk[u] = make_uint4(0, 0, 0, 0);
+      if (gu < groups) {
+        nv[u] = group_at(sg, gu, g1, kp[u], ip);
+        kk[u] = *reinterpret_cast<const uint4*>(kp[u]);
+      }
     }
 #pragma unroll
-    for (uint32_t q = 0; q < 4; ++q) {
-      const uint32_t key = u4get(kk, q);
-      if (4u * g + q < n) {
-        mx = max(mx, key);
-        if (key >= plo && (key <= phi || open)) atomicAdd(&h[hslot((min(key, phi) - plo) >> shift)], 1u);
+    for (uint32_t u = 0; u < 2; ++u) {
+      if (raw && g + u * nt < g1) {
+        kk[u] = make_uint4(key_of_score<DT>(kk[u].x), key_of_score<DT>(kk[u].y), key_of_score<DT>(kk[u].z),
+                           key_of_score<DT>(kk[u].w));
+        *lds_ptr(reinterpret_cast<u32x4*>(kp[u])) = u32x4{kk[u].x, kk[u].y, kk[u].z, kk[u].w};
+      }
+#pragma unroll
+      for (uint32_t q = 0; q < 4; ++q) {
+        const uint32_t key = u4get(kk[u], q);
+        if (q < nv[u]) {
+          mx = max(mx, key);
+          if (vm)
+            atomicAdd(&h[hslot(vbin<DT>(key, vb))], 1u);
+          else if (key >= plo && (key <= phi || open))
+            atomicAdd(&h[hslot((min(key, phi) - plo) >> shift)], 1u);
+        }
       }
     }
   }
   return mx;
 }
 
-// Histogram of the indices of one segment's entries whose key is pkey.
-__device__ __forceinline__ void hist_ties(const uint32_t* kp, const uint32_t* ip, uint32_t n, uint32_t tid, uint32_t nt,
-                                          uint32_t pkey, uint32_t iplo, uint32_t iphi, uint32_t shift, uint32_t* h) {
-  for (uint32_t g = tid; 4u * g < n; g += nt) {
-    const uint4 kk = *reinterpret_cast<const uint4*>(kp + 4u * g);
-    const uint4 ii = *reinterpret_cast<const uint4*>(ip + 4u * g);
+// Histogram of the indices of the entries whose key is pkey.
+__device__ __forceinline__ void ties_all(const Segs& sg, uint32_t tid, uint32_t nt, uint32_t pkey, uint32_t iplo,
+                                         uint32_t iphi, uint32_t shift, uint32_t* h) {
+  const uint32_t g1 = (sg.n1 + 3u) / 4u, groups = g1 + (sg.n0 + 3u) / 4u;
+  for (uint32_t g = tid; g < groups; g += nt) {
+    uint32_t *kp, *ip;
+    const uint32_t nv = group_at(sg, g, g1, kp, ip);
+    const uint4 kk = *reinterpret_cast<const uint4*>(kp);
+    const uint4 ii = *reinterpret_cast<const uint4*>(ip);
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
       const uint32_t key = u4get(kk, q), id = u4get(ii, q);
-      if (4u * g + q < n && key == pkey && id >= iplo && id <= iphi)
+      if (q < nv && key == pkey && id >= iplo && id <= iphi)
         atomicAdd(&h[hslot(kBins - 1u - ((id - iplo) >> shift))], 1u);
     }
   }
 }
 
-// Where the compaction sends one segment's entries: above the pivot window to (dk, di), inside
-// it to the list.
+// The pivot window a compaction ends with: value bin vbin_p (vm), else keys [plo, phi], or,
+// for ties, key pkey with indices [iplo, iphi].
 struct Pivot {
-  uint32_t plo, phi, pkey, iplo, iphi, k;
-  bool tie;
+  uint32_t plo, phi, pkey, iplo, iphi, k, vbin_p;
+  VBins vb;
+  bool tie, vm;
 };
 
-__device__ __forceinline__ void scatter_seg(const uint32_t* kp, const uint32_t* ip, uint32_t n, uint32_t tid,
-                                            uint32_t nt, uint32_t lane, const Pivot& pv, uint32_t* dk, uint32_t* di,
-                                            Scalars& sc) {
-  const uint32_t iters = (n + 4u * nt - 1u) / (4u * nt);
+// Scatter of all entries: those above the pivot window go to (dk, di), those inside it to
+// the list.
+template <int DT>
+__device__ __forceinline__ void scatter_all(const Segs& sg, uint32_t tid, uint32_t nt, uint32_t lane, const Pivot& pv,
+                                            uint32_t* dk, uint32_t* di, Scalars& sc) {
+  const uint32_t g1 = (sg.n1 + 3u) / 4u, groups = g1 + (sg.n0 + 3u) / 4u;
+  const uint32_t iters = (groups + nt - 1u) / nt;
   for (uint32_t it = 0; it < iters; ++it) {
     const uint32_t g = it * nt + tid;
     uint4 kk = make_uint4(0, 0, 0, 0), ii = make_uint4(0, 0, 0, 0);
-    if (4u * g < n) {
-      kk = *reinterpret_cast<const uint4*>(kp + 4u * g);
-      ii = *reinterpret_cast<const uint4*>(ip + 4u * g);
+    uint32_t nv = 0;
+    if (g < groups) {
+      uint32_t *kp, *ip;
+      nv = group_at(sg, g, g1, kp, ip);
+      kk = *reinterpret_cast<const uint4*>(kp);
+      ii = *reinterpret_cast<const uint4*>(ip);
     }
     bool up[4], mid[4];
     uint64_t bu[4], bm[4];
@@ -431,8 +560,12 @@ __device__ __forceinline__ void scatter_seg(const uint32_t* kp, const uint32_t* 
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
       const uint32_t key = u4get(kk, q), id = u4get(ii, q);
-      const bool valid = 4u * g + q < n;
-      if (!pv.tie) {
+      const bool valid = q < nv;
+      if (pv.vm) {
+        const uint32_t b = vbin<DT>(key, pv.vb);
+        up[q] = valid && b > pv.vbin_p;
+        mid[q] = valid && b == pv.vbin_p;
+      } else if (!pv.tie) {
         up[q] = valid && key > pv.phi;
         mid[q] = valid && key >= pv.plo && key <= pv.phi;
       } else {
@@ -475,12 +608,11 @@ __device__ __forceinline__ void scatter_seg(const uint32_t* kp, const uint32_t* 
   }
 }
 
-// RAW: the appended segment holds raw scores (the select kernel); they become keys in the first
-// histogram pass (or in the copy when everything is kept).
 template <int WAVES, int DT, bool RAW>
 __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, bool fin, bool have_t,
                         uint32_t key_hi, uint32_t ilo, uint32_t ihi, Scalars& sc, uint32_t* hist2, uint32_t& hpar,
-                        uint32_t& tkey, uint32_t& tidx, uint32_t& maxkey) {
+                        uint32_t& tkey, uint32_t& tidx, uint32_t& maxkey, uint32_t vlo_key, uint32_t vhi_key,
+                        bool vok) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t n = sg.n0 + sg.n1;
@@ -516,6 +648,8 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
   pv.iplo = ilo;
   pv.iphi = ihi;
   pv.k = k;
+  pv.vbin_p = 0;
+  pv.vm = vok && vbins_of<DT>(vlo_key, vhi_key, pv.vb);
   bool open = have_t, first = true;
   uint32_t need = k, above_total = 0, cnt = 0, seen_max = 0;
   for (;;) {
@@ -526,20 +660,17 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
     // the other histogram was last read by the previous scan, before the last barrier
     for (uint32_t b = 4u * tid; b < kBins; b += 4u * NT) *reinterpret_cast<uint4*>(hz + b) = make_uint4(0, 0, 0, 0);
     if (!pv.tie) {
-      // survivors are counted from the last thread down, appended entries from the first up,
-      // so that the threads share the groups evenly
-      uint32_t mx = hist_keys<DT>(sg.k0, sg.n0, NT - 1u - tid, NT, pv.plo, pv.phi, open, shift, h, false);
-      mx = max(mx, hist_keys<DT>(sg.k1, sg.n1, tid, NT, pv.plo, pv.phi, open, shift, h, RAW && first));
+      uint32_t mx = hist_all<DT>(sg, tid, NT, pv.plo, pv.phi, open, shift, h, RAW && first, pv.vm, pv.vb);
       if (first) {
         mx = wave_max32(mx);
         if (lane == 0) sc.red[wave] = mx;
       }
     } else {
-      hist_ties(sg.k0, sg.i0, sg.n0, NT - 1u - tid, NT, pv.pkey, pv.iplo, pv.iphi, shift, h);
-      hist_ties(sg.k1, sg.i1, sg.n1, tid, NT, pv.pkey, pv.iplo, pv.iphi, shift, h);
+      ties_all(sg, tid, NT, pv.pkey, pv.iplo, pv.iphi, shift, h);
     }
     lds_sync();
     ++hpar;
+    if (tid == 0) ++sc.st_p;
     if (wave == 0) {
       uint32_t smax = 0;
       if (first) {
@@ -548,11 +679,20 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
       }
       uint32_t bin, above, c;
       scan_select(h, need, lane, bin, above, c);
+      uint32_t blo = 0, bhi = 0;
+      if (pv.vm && c > kListCap) {  // the key range of the value bin, for the key passes
+        blo = static_cast<uint32_t>(vbin_first_key<DT>(bin, vlo_key, key_of_inf<DT>(), pv.vb, lane));
+        bhi = bin + 1u < kBins
+                  ? static_cast<uint32_t>(vbin_first_key<DT>(bin + 1u, vlo_key, key_of_inf<DT>(), pv.vb, lane) - 1u)
+                  : key_of_inf<DT>();
+      }
       if (lane == 0) {
         sc.pub[0] = bin;
         sc.pub[1] = above;
         sc.pub[2] = c;
         sc.pub[3] = smax;
+        sc.pub[4] = blo;
+        sc.pub[5] = bhi;
       }
     }
     lds_sync();
@@ -562,7 +702,21 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
     first = false;
     need -= above;
     above_total += above;
-    if (!pv.tie) {
+    if (pv.vm) {
+      if (cnt <= kListCap) {
+        pv.vbin_p = bin;
+        break;
+      }
+      // continue with key bins over the value bin's keys (all of them <= the largest key)
+      pv.vm = false;
+      open = false;
+      pv.plo = sc.pub[4];
+      pv.phi = min(sc.pub[5], seen_max);
+      if (pv.plo == pv.phi) {
+        pv.tie = true;
+        pv.pkey = pv.plo;
+      }
+    } else if (!pv.tie) {
       const bool open_bin = open && bin == ((pv.phi - pv.plo) >> shift);
       const uint32_t nlo = pv.plo + (bin << shift);
       const uint64_t nhi64 = static_cast<uint64_t>(nlo) + (1ull << shift) - 1u;
@@ -585,8 +739,7 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
   cnt = cnt < kListCap ? cnt : kListCap;  // more only if (key, index) pairs repeat
 
   // scatter: entries above the pivot window go to the destination, the window's to the list
-  scatter_seg(sg.k0, sg.i0, sg.n0, NT - 1u - tid, NT, lane, pv, dk, di, sc);
-  scatter_seg(sg.k1, sg.i1, sg.n1, tid, NT, lane, pv, dk, di, sc);
+  scatter_all<DT>(sg, tid, NT, lane, pv, dk, di, sc);
   lds_sync();
 
   // wave 0 ranks the short list, places the `need` best of it after the above_total entries
@@ -675,9 +828,15 @@ constexpr int bitonic_barriers() {
   return c;
 }
 
+// Stores entry c (a composite) at position `at` of the outputs, or, with pairs, as a (key,
+// index) pair at pairs[at].
 template <int DT>
-__device__ __forceinline__ void store_out(void* out_vals, int32_t* out_idx, uint64_t at, uint64_t c) {
+__device__ __forceinline__ void store_out(void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t at, uint64_t c) {
   const uint32_t key = static_cast<uint32_t>(c >> 32), id = ~static_cast<uint32_t>(c);
+  if (pairs) {
+    pairs[at] = make_uint2(key, id);
+    return;
+  }
   if (out_vals) {
     if constexpr (DT == DS_BF16)
       static_cast<uint16_t*>(out_vals)[at] = static_cast<uint16_t>(raw_of_key<DT>(key));
@@ -693,7 +852,7 @@ __device__ __forceinline__ void store_out(void* out_vals, int32_t* out_idx, uint
 // (fk, fi) and hold 2^LOGT words each.
 template <int DT, int WAVES, uint32_t LOGT>
 __device__ __forceinline__ void sort_store_t(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi, uint32_t k,
-                             void* out_vals, int32_t* out_idx, uint64_t row) {
+                             void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64, TOTAL = 1u << LOGT;
   constexpr uint32_t TH = TOTAL > NT ? NT : TOTAL;
   constexpr int E = static_cast<int>(TOTAL / TH);
@@ -709,7 +868,7 @@ __device__ __forceinline__ void sort_store_t(const uint32_t* fk, const uint32_t*
 #pragma unroll
     for (uint32_t j = 0; j < static_cast<uint32_t>(E); ++j) {
       const uint32_t e = tid * E + j;
-      if (e < k) store_out<DT>(out_vals, out_idx, row * k + e, v[j]);
+      if (e < k) store_out<DT>(out_vals, out_idx, pairs, row * k + e, v[j]);
     }
   } else {
     constexpr int NB = bitonic_barriers<E, TOTAL>();
@@ -721,7 +880,7 @@ __device__ __forceinline__ void sort_store_t(const uint32_t* fk, const uint32_t*
 // (a power of two >= k) composites held as (xk, xi) halves, best first, and stores the first k.
 template <int DT, int WAVES>
 __device__ __forceinline__ void sort_store_lds(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi, uint32_t k,
-                               uint32_t cap, void* out_vals, int32_t* out_idx, uint64_t row) {
+                               uint32_t cap, void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < cap; i += NT) {
@@ -748,34 +907,79 @@ __device__ __forceinline__ void sort_store_lds(const uint32_t* fk, const uint32_
     }
   }
   for (uint32_t i = tid; i < k; i += NT)
-    store_out<DT>(out_vals, out_idx, row * k + i, (static_cast<uint64_t>(xk[i]) << 32) | xi[i]);
+    store_out<DT>(out_vals, out_idx, pairs, row * k + i, (static_cast<uint64_t>(xk[i]) << 32) | xi[i]);
 }
 
-// Register sort when at most eight entries per thread are needed, else the LDS sort.
+// Register sort when at most eight entries per thread are needed, else the LDS sort. The
+// sorted entries go to row `row` of the outputs, or, with pairs, to pairs[row * k ...].
 template <int DT, int WAVES>
 __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi, uint32_t k,
-                               void* out_vals, int32_t* out_idx, uint64_t row) {
+                               void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
   uint32_t cap = 64;
   while (cap < k) cap <<= 1;
   if (cap > 8 * NT) {
-    sort_store_lds<DT, WAVES>(fk, fi, xk, xi, k, cap, out_vals, out_idx, row);
+    sort_store_lds<DT, WAVES>(fk, fi, xk, xi, k, cap, out_vals, out_idx, pairs, row);
     return;
   }
   switch (cap) {
-    case 64: sort_store_t<DT, WAVES, 6>(fk, fi, xk, xi, k, out_vals, out_idx, row); break;
-    case 128: sort_store_t<DT, WAVES, 7>(fk, fi, xk, xi, k, out_vals, out_idx, row); break;
-    case 256: sort_store_t<DT, WAVES, 8>(fk, fi, xk, xi, k, out_vals, out_idx, row); break;
-    case 512: sort_store_t<DT, WAVES, 9>(fk, fi, xk, xi, k, out_vals, out_idx, row); break;
+    case 64: sort_store_t<DT, WAVES, 6>(fk, fi, xk, xi, k, out_vals, out_idx, pairs, row); break;
+    case 128: sort_store_t<DT, WAVES, 7>(fk, fi, xk, xi, k, out_vals, out_idx, pairs, row); break;
+    case 256: sort_store_t<DT, WAVES, 8>(fk, fi, xk, xi, k, out_vals, out_idx, pairs, row); break;
+    case 512: sort_store_t<DT, WAVES, 9>(fk, fi, xk, xi, k, out_vals, out_idx, pairs, row); break;
     case 1024:
-      if constexpr (1024 <= 8 * NT) sort_store_t<DT, WAVES, 10>(fk, fi, xk, xi, k, out_vals, out_idx, row);
+      if constexpr (1024 <= 8 * NT) sort_store_t<DT, WAVES, 10>(fk, fi, xk, xi, k, out_vals, out_idx, pairs, row);
       break;
     case 2048:
-      if constexpr (2048 <= 8 * NT) sort_store_t<DT, WAVES, 11>(fk, fi, xk, xi, k, out_vals, out_idx, row);
+      if constexpr (2048 <= 8 * NT) sort_store_t<DT, WAVES, 11>(fk, fi, xk, xi, k, out_vals, out_idx, pairs, row);
       break;
     default:
-      if constexpr (4096 <= 8 * NT) sort_store_t<DT, WAVES, 12>(fk, fi, xk, xi, k, out_vals, out_idx, row);
+      if constexpr (4096 <= 8 * NT) sort_store_t<DT, WAVES, 12>(fk, fi, xk, xi, k, out_vals, out_idx, pairs, row);
       break;
+  }
+}
+
+// --------------------------------------------------------------------------- slice merge
+
+// Merge of a row's S sorted slice lists (S <= kMaxFusedSlices, k entries each, best first,
+// as (key, index) pairs at src[s * k + i]) into the row's k best, sorted, written to the
+// outputs. The lists are loaded into LDS (lds: S * k 64-bit words) as composites; an entry's
+// place in the merged order is its position in its own list plus, for every other list, the
+// number of that list's entries that rank above it (a binary search; all composites are
+// distinct apart from padding, which ranks below every element and is never placed).
+template <int DT, int WAVES>
+__device__ __forceinline__ void merge_sorted_lists(const uint2* src, uint32_t S, uint32_t k, uint64_t* lds,
+                                                   void* out_vals, int32_t* out_idx, uint64_t row) {
+  constexpr uint32_t NT = WAVES * 64;
+  const uint32_t tid = threadIdx.x, total = S * k;
+  __attribute__((address_space(3))) uint64_t* lw = lds_ptr(lds);
+  for (uint32_t e = tid; e < total; e += NT) {
+    const uint2 v = src[e];
+    lw[e] = comp_of(v.x, v.y);
+  }
+  lds_sync();
+  const uint32_t top = 1u << (31u - static_cast<uint32_t>(__builtin_clz(k)));  // largest power of two <= k
+  for (uint32_t e = tid; e < total; e += NT) {
+    uint32_t s = 0;
+#pragma unroll
+    for (uint32_t q = 1; q < kMaxFusedSlices; ++q) s += (q < S && e >= q * k) ? 1u : 0u;
+    const uint64_t c = lw[e];
+    uint32_t rank = e - s * k;
+    uint32_t pos[kMaxFusedSlices];
+#pragma unroll
+    for (uint32_t q = 0; q < kMaxFusedSlices; ++q) pos[q] = 0;
+    for (uint32_t step = top; step > 0; step >>= 1) {
+#pragma unroll
+      for (uint32_t q = 0; q < kMaxFusedSlices; ++q) {
+        if (q < S && q != s) {
+          const uint32_t at = pos[q] + step;
+          if (at <= k && lw[q * k + at - 1u] > c) pos[q] = at;
+        }
+      }
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < kMaxFusedSlices; ++q) rank += pos[q];
+    if (rank < k) store_out<DT>(out_vals, out_idx, nullptr, row * k + rank, c);
   }
 }
 
@@ -830,7 +1034,7 @@ struct BodyOut {
 template <int DT, int WAVES, int CPW, int D, bool MERGE>
 __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amdgpu_buffer_rsrc_t rs, uint32_t len,
                                                 uint32_t idx_base, uint32_t k, uint32_t B2, const BlockOrder& ord,
-                                                uint32_t ilo, uint32_t ihi, bool stats, BodyOut& out) {
+                                                uint32_t ilo, uint32_t ihi, bool stats, bool presample, BodyOut& out) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t IB = MERGE ? 8 : (DT == DS_BF16 ? 2 : 4);  // bytes per item
   constexpr uint32_t VEC = 16 / IB;                            // items per lane per chunk
@@ -853,6 +1057,14 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   uint32_t t_key = 0, t_idx = 0, maxkey = 0;
   uint32_t nsurv = 0, napp = 0, hpar = 0, b3 = 0;
   bool sur_a = false;  // survivors in set A (else set B)
+  // key range of the entries appended before the first compaction (the select kernel tracks
+  // it; the merge kernel does not)
+  uint32_t rmin_w = ~0u, rmax_w = 0;
+  constexpr bool range_ok = !MERGE;
+  // presampled threshold (a lower bound of the first block's k-th element) and the first
+  // block's largest key, the value-bin window of the first compaction
+  bool presampled = false;
+  uint32_t pre_hi = 0;
   const bool st0 = stats && tid == 0;  // the thread that keeps the counters in sc.st_*
   uint64_t t_mark = 0;
   uint64_t my_reads = 0, my_jsum = 0;
@@ -874,8 +1086,24 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     const Segs sg = nsurv ? make_segs(sur_a ? L.ck : L.bk, sur_a ? L.ci : L.bi, nsurv, L.ck + L.k4, L.ci + L.k4, napp)
                           : make_segs(nullptr, nullptr, 0u, L.ck, L.ci, napp);
     const bool to_a = nsurv != 0 && !sur_a;  // first compaction: entries start in A, go to B
+    // value bins over [T, previous maximum], or over the appended keys' range the first time
+    uint32_t vlo = t_key, vhi = maxkey;
+    bool vok = nsurv != 0;
+    if (!nsurv && presampled) {
+      vhi = pre_hi;
+      vok = true;
+    } else if (!nsurv) {
+      vlo = ~0u;
+      vhi = 0;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        vlo = min(vlo, sc.rmin[w]);
+        vhi = max(vhi, sc.rmax[w]);
+      }
+      vok = range_ok;
+    }
     compact<WAVES, DT, !MERGE>(sg, to_a ? L.ck : L.bk, to_a ? L.ci : L.bi, k, fin, nsurv != 0, key_hi, ilo, ihi, sc,
-                               L.hist, hpar, t_key, t_idx, maxkey);
+                               L.hist, hpar, t_key, t_idx, maxkey, vlo, vhi, vok);
     if (st0) {
       sc.st_a += napp;
       sc.st_w += nsurv + napp;
@@ -891,8 +1119,6 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     const uint32_t abase = (nsurv ? L.k4 : 0u) + napp;  // append position of this block's first entry
     const uint32_t nxt = (b3 == 2 ? 0u : b3 + 1u);
     if constexpr (!MERGE) {
-      const bool strict = idx_base + blk_lo > t_idx;
-      const uint32_t thr = strict ? thr_s : thr_n;
       uint32_t s[CPW][VEC];
 #pragma unroll
       for (uint32_t t = 0; t < CPW; ++t) {
@@ -916,6 +1142,47 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
           my_jsum += nval * static_cast<uint64_t>(idx_base + first) + (static_cast<uint64_t>(nval) * (nval - 1)) / 2;
         }
       }
+      if (presample && i == 0 && blk_lo + B <= len) {
+        // Threshold from the first (whole) block instead of "accept everything": each wave
+        // takes the j-th largest of its lanes' maxima, j = ceil(k / WAVES), found bit by bit
+        // over the key's top 16 bits (a truncation can only lower it); the smallest of the
+        // waves' values T0 has at least WAVES * j >= k distinct elements (one per lane) at
+        // or above it, so T0 does not exceed the k-th element and "key >= T0" keeps every
+        // element that can be in the top k.
+        constexpr uint32_t KB = DT == DS_BF16 ? 16u : 32u;
+        uint32_t lmax = 0;
+#pragma unroll
+        for (uint32_t t = 0; t < CPW; ++t) {
+#pragma unroll
+          for (uint32_t q = 0; q < VEC; ++q) lmax = max(lmax, key_of_score<DT>(s[t][q]));
+        }
+        const uint32_t j = (k + WAVES - 1) / WAVES;
+        uint32_t pre = 0;
+#pragma unroll
+        for (uint32_t b = KB; b > KB - 16u; --b) {
+          const uint32_t cand = pre | (1u << (b - 1u));
+          pre = popc(ballot(lmax >= cand)) >= j ? cand : pre;
+        }
+        const uint32_t wmax = wave_max32(lmax);
+        if (lane == 0) {
+          sc.rmin[wave] = pre;
+          sc.rmax[wave] = wmax;
+        }
+        lds_sync();
+        uint32_t t0 = ~0u, hi = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+          t0 = min(t0, sc.rmin[w]);
+          hi = max(hi, sc.rmax[w]);
+        }
+        t_key = t0;
+        t_idx = ~0u;  // ties with T0 are kept in every block
+        pre_hi = hi;
+        presampled = true;
+        filter_thresholds<DT>(t_key, mode, thr_s, thr_n);
+      }
+      const bool strict = idx_base + blk_lo > t_idx;
+      const uint32_t thr = strict ? thr_s : thr_n;
       if (mode == 0 && blk_lo + B <= len) {
         // accept everything: each wave stores its chunks (raw) contiguously
         constexpr uint32_t tot = CPW * CHUNK;
@@ -923,6 +1190,22 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
         if (lane == 0) pos = atomicAdd(&sc.blk[b3], tot);
         pos = uni(pos) + abase;
         if (tid == 0) sc.blk[nxt] = 0;
+        uint32_t kmn = ~0u, kmx = 0;
+#pragma unroll
+        for (uint32_t t = 0; t < CPW; ++t) {
+#pragma unroll
+          for (uint32_t q = 0; q < VEC; ++q) {
+            const uint32_t key = key_of_score<DT>(s[t][q]);
+            kmn = min(kmn, key);
+            kmx = max(kmx, key);
+          }
+        }
+        rmin_w = min(rmin_w, wave_min32(kmn));
+        rmax_w = max(rmax_w, wave_max32(kmx));
+        if (lane == 0) {
+          sc.rmin[wave] = rmin_w;
+          sc.rmax[wave] = rmax_w;
+        }
         if (pos % 4u == 0) {
 #pragma unroll
           for (uint32_t t = 0; t < CPW; ++t) {
@@ -947,6 +1230,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
           }
         }
       } else {
+        uint32_t kmn = ~0u, kmx = 0;  // key range of the hits while there is no threshold
         // one reservation per chunk: only that chunk's hit masks are live. Hits are stored raw.
 #pragma unroll
         for (uint32_t t = 0; t < CPW; ++t) {
@@ -963,6 +1247,14 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
             const uint32_t nval = first >= len ? 0u : min(VEC, len - first);
 #pragma unroll
             for (uint32_t e = 0; e < VEC; ++e) h[e] = h[e] && e < nval;
+          }
+          if (mode == 0) {
+#pragma unroll
+            for (uint32_t e = 0; e < VEC; ++e) {
+              const uint32_t key = key_of_score<DT>(s[t][e]);
+              kmn = h[e] ? min(kmn, key) : kmn;
+              kmx = h[e] ? max(kmx, key) : kmx;
+            }
           }
           uint64_t mk[VEC];
           uint32_t tot = 0;
@@ -990,6 +1282,14 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
           }
         }
         if (tid == 0) sc.blk[nxt] = 0;
+        if (mode == 0) {
+          rmin_w = min(rmin_w, wave_min32(kmn));
+          rmax_w = max(rmax_w, wave_max32(kmx));
+          if (lane == 0) {
+            sc.rmin[wave] = rmin_w;
+            sc.rmax[wave] = rmax_w;
+          }
+        }
       }
     } else {
       // merge: items are (key, index) pairs; a hit beats T in the composite order
@@ -1109,6 +1409,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
     sc.blk[0] = sc.blk[1] = sc.blk[2] = 0;
     sc.st_a = sc.st_r = sc.st_w = sc.st_max = sc.st_tc = sc.st_ts = sc.st_tf = 0;
     sc.st_mono = 1;
+    sc.st_p = 0;
     sc.reads = 0;
     sc.index_sum = 0;
   }
@@ -1124,7 +1425,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
 
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES), false>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
-                                                            slice_lo + len - 1u, stats, bo);
+                                                            slice_lo + len - 1u, stats, p.presample != 0, bo);
 
   if (stats) {
     uint64_t my_reads = bo.reads, my_jsum = bo.jsum;
@@ -1152,15 +1453,36 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
       o->slack = B2;
       o->t_compact_ns = sc.st_tc * 10;
       o->t_sync_ns = sc.st_ts * 10;
-      o->reserved = 0;
+      o->passes = sc.st_p;
     }
   }
 
   if (p.slices == 1) {
-    sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, p.out_vals, p.out_idx, row);
-  } else {
+    sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, p.out_vals, p.out_idx, nullptr, row);
+  } else if (!p.arrive) {
     uint2* const dst = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + static_cast<uint64_t>(slice) * k;
     for (uint32_t i = tid; i < k; i += NT) dst[i] = make_uint2(bo.fk[i], bo.fi[i]);
+  } else {
+    // fused merge: each slice stores its survivors sorted; the row's last slice to finish
+    // (counted by a device-scope atomic) merges the lists and writes the output, then resets
+    // the counter for the next call
+    uint2* const rws = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries;
+    sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, nullptr, nullptr, rws + slice * k, 0);
+    // every wave's list stores are complete (workgroup barrier with global fences); one
+    // device-scope release by thread 0 then publishes them all before the arrival
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      sc.pub[0] = atomicAdd(p.arrive + row, 1u);
+      if (sc.pub[0] == static_cast<uint32_t>(p.slices) - 1u)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other slices' lists
+    }
+    __syncthreads();
+    if (sc.pub[0] == static_cast<uint32_t>(p.slices) - 1u) {
+      merge_sorted_lists<DT, WAVES>(rws, static_cast<uint32_t>(p.slices), k, reinterpret_cast<uint64_t*>(lds),
+                                    p.out_vals, p.out_idx, row);
+      if (tid == 0) p.arrive[row] = 0;
+    }
   }
   if (stats && tid == 0) {
     const uint64_t t_end = wall_clock64();
@@ -1188,7 +1510,10 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
 
   const Lay L = lay_of(lds, k, B2, B);
   for (uint32_t i = 4u * tid; i < 2u * kBins; i += 4u * NT) *reinterpret_cast<uint4*>(L.hist + i) = make_uint4(0, 0, 0, 0);
-  if (tid == 0) sc.blk[0] = sc.blk[1] = sc.blk[2] = 0;
+  if (tid == 0) {
+    sc.blk[0] = sc.blk[1] = sc.blk[2] = 0;
+    sc.st_p = 0;
+  }
   const uint2* base = p.ws + static_cast<uint64_t>(row) * p.row_entries;  // rows padded to 16 bytes
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint2*>(base), 0, static_cast<int>((len * 8u + 15u) & ~15u), kRsrcWord3);
@@ -1197,8 +1522,8 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
 
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES), true>(L, sc, rs, len, 0u, k, B2, ord, 0u,
-                                                           static_cast<uint32_t>(p.n - 1), false, bo);
-  sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, p.out_vals, p.out_idx, row);
+                                                           static_cast<uint32_t>(p.n - 1), false, false, bo);
+  sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, p.out_vals, p.out_idx, nullptr, row);
 }
 
 // --------------------------------------------------------------------------- probes
@@ -1291,6 +1616,8 @@ hipError_t launch_merge_dt(const MergeParams& p, int64_t rows, size_t lds, hipSt
 }
 
 }  // namespace
+
+size_t select_scalars_bytes() { return sizeof(Scalars); }
 
 size_t select_lds_bytes(int k, int block, int slack, int waves) {
   (void)waves;
