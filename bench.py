@@ -84,7 +84,7 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
     rows, n = w.rows, w.n
     plan = ts.ds_topk_plan(rows, n, k, w.dtype)
     wsb = ts.ds_topk_workspace_size(rows, n, k, w.dtype)
-    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
     vals = torch.empty((rows, k), dtype=xd.dtype, device="cuda")
     idx = None if w.values_only else torch.empty((rows, k), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -178,7 +178,7 @@ def counter_pass(ts, torch, w, k, launches, pool_mib):
     pool = [xd] + [xd.clone() for _ in range(copies - 1)]
     rows, n = w.rows, w.n
     wsb = ts.ds_topk_workspace_size(rows, n, k, w.dtype)
-    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
     vals = torch.empty((rows, k), dtype=xd.dtype, device="cuda")
     idx = None if w.values_only else torch.empty((rows, k), dtype=torch.int32, device="cuda")
     for i in range(launches):

@@ -139,12 +139,8 @@ int ds_topk_workspace_size(int64_t rows, int64_t n, int k, int dtype, const ds_c
 /*
  * ds_topk_ex -- ds_topk with a caller workspace, a forced configuration and counters.
  *   workspace  device, >= ds_topk_workspace_size bytes, 16-byte aligned; may be NULL when
- *              that size is 0. It must be zero-filled before its first use: its first
- *              64 KiB hold per-row arrival counters (with 2..8 slices per row the last slice
- *              of a row to finish merges the row), every completed call leaves them at zero,
- *              and no call writes anything else there, so a workspace can be reused for any
- *              later call without clearing it again. Calls that share a workspace must not
- *              overlap in time.
+ *              that size is 0. Its contents on entry do not matter; it is overwritten.
+ *              Calls that share a workspace must not overlap in time.
  *   cfg        NULL or fields to force (see ds_config).
  *   stats      NULL, or device [rows, slices] ds_stats filled by the select kernel.
  * Allocates nothing.
@@ -156,10 +152,10 @@ int ds_topk_ex(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k
 /*
  * ds_topk_slices / ds_topk_merge -- ds_topk_ex as its two launches, for callers that
  * want to time or overlap them separately. ds_topk_slices runs the select kernel: with one
- * slice per row, or with 2..8 slices whose sorted lists fit in the workgroup's LDS (the
- * last slice of each row merges them), it writes the final outputs; otherwise it writes
- * every slice's k survivors to the workspace and ds_topk_merge reduces each row's
- * survivors to the sorted top-k (it enqueues nothing in the other cases). Both take the same arguments as
+ * slice per row it writes the final outputs; otherwise it writes every slice's k survivors
+ * to the workspace (sorted, for 2..8 slices whose lists fit in LDS) and ds_topk_merge
+ * reduces each row's survivors to the sorted top-k (it enqueues nothing when the plan has
+ * one slice). Both take the same arguments as
  * ds_topk_ex (merge ignores x, row_stride and stats) and must be given the same rows, n, k,
  * dtype, seed, cfg and workspace; the pair then equals one ds_topk_ex call.
  */

@@ -50,8 +50,7 @@ def run_gpu(x: np.ndarray, k: int, seed: int = 1, cfg=None, values=True, indices
         dt = ts.BF16 if x.dtype == np.uint16 else ts.FP32
         plan = ts.ds_topk_plan(rows, n, k, dt, cfg)
         wsb = ts.ds_topk_workspace_size(rows, n, k, dt, cfg)
-        # a caller workspace starts zero-filled (the fused merge's counters); calls leave it so
-        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
         sb = ts.stats_buffer(rows, plan["slices"], "cuda") if stats else None
         v, i = ts.ds_topk_ex(xd, k, seed=seed, workspace=ws, cfg=cfg, stats=sb, values=values, indices=indices)
         if stats:

@@ -70,8 +70,7 @@ def test_forced_plans(dtype, n, k, slices):
     per = -(-n // slices)
     assert p["slices"] == -(-n // (-(-per // p["block"]) * p["block"]))
     ws = ts.ds_topk_workspace_size(8, n, k, dtype, {"slices": slices})
-    # 64 KiB of per-row arrival counters, then the slice lists
-    assert ws == (0 if slices == 1 else 65536 + 8 * ((slices * k + 1) // 2 * 2) * 8)
+    assert ws == (0 if slices == 1 else 8 * ((slices * k + 1) // 2 * 2) * 8)
 
 
 def test_forced_block_sizes():

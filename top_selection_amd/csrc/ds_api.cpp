@@ -41,12 +41,10 @@ struct Plan {
   int sort_cap;
   size_t lds;
   bool presample;   // the first whole block sets a presampled threshold
-  // merge (slices > 1): fused into the select kernel (the row's last slice merges sorted
-  // slice lists) or the merge kernel
-  bool fused;
+  // merge (slices > 1): the list-merge kernel over sorted slice lists, or the merge kernel
+  bool list_merge;
   int mslack;
   size_t mlds;
-  size_t ws_lists;  // bytes of the slice lists (after the counter area)
   size_t ws_bytes;
 };
 
@@ -174,12 +172,10 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
     if (static_cast<int64_t>(p.mlds) > kMaxLdsBytes) return DS_ERR_UNSUPPORTED;
     const int64_t entries = slices * static_cast<int64_t>(k);
     if (entries * 8 > kMaxSliceBytes) return DS_ERR_UNSUPPORTED;
-    p.ws_lists = static_cast<size_t>(rows) * static_cast<size_t>((entries + 1) & ~int64_t(1)) * 8;
-    p.fused = slices <= ds::kMaxFusedSlices && rows <= ds::kArriveCounters &&
-              static_cast<size_t>(entries) * 8 <= lds - ds::select_scalars_bytes();
-    // every split plan has the same layout: the fused merge's arrival counters first, the
-    // slice lists after them, so no plan's lists overlap another plan's counters
-    p.ws_bytes = ds::kArriveBytes + p.ws_lists;
+    // the list merge holds a row's lists in LDS (as much as the select kernel's dynamic LDS)
+    p.list_merge = slices <= ds::kMaxListSlices &&
+                   static_cast<size_t>(entries) * 8 <= lds - ds::select_scalars_bytes();
+    p.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>((entries + 1) & ~int64_t(1)) * 8;
   }
   *out = p;
   return DS_OK;
@@ -211,22 +207,22 @@ int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t r
   sp.slack = pl.slack;
   sp.sort_cap = pl.sort_cap;
   sp.seed = seed;
-  sp.ws = ws ? reinterpret_cast<uint2*>(static_cast<uint8_t*>(ws) + ds::kArriveBytes) : nullptr;
+  sp.ws = static_cast<uint2*>(ws);
   sp.ws_row_entries = (static_cast<int64_t>(pl.slices) * k + 1) & ~int64_t(1);
   sp.out_vals = out_vals;
   sp.out_idx = out_idx;
   sp.stats = stats;
-  sp.arrive = pl.fused ? static_cast<uint32_t*>(ws) : nullptr;
+  sp.sorted_lists = pl.list_merge ? 1 : 0;
   sp.presample = pl.presample ? 1 : 0;
   return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }
 
 int run_merge(const Plan& pl, int64_t rows, int64_t n, int k, uint64_t seed, void* out_vals, int32_t* out_idx,
               void* ws, hipStream_t stream) {
-  if (pl.slices <= 1 || pl.fused) return DS_OK;
+  if (pl.slices <= 1) return DS_OK;
   (void)hipGetLastError();
   ds::MergeParams mp{};
-  mp.ws = reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(ws) + ds::kArriveBytes);
+  mp.ws = static_cast<const uint2*>(ws);
   mp.entries = static_cast<int64_t>(pl.slices) * k;
   mp.row_entries = (mp.entries + 1) & ~int64_t(1);
   mp.n = n;
@@ -236,6 +232,7 @@ int run_merge(const Plan& pl, int64_t rows, int64_t n, int k, uint64_t seed, voi
   mp.seed = seed;
   mp.out_vals = out_vals;
   mp.out_idx = out_idx;
+  if (pl.list_merge) return ds::launch_merge_lists(pl.dtype, mp, rows, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
   return ds::launch_merge(pl.dtype, mp, rows, pl.mlds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }
 
@@ -396,11 +393,6 @@ int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, i
       }
       void* ptr = nullptr;
       if (hipMalloc(&ptr, p.ws_bytes) != hipSuccess) return DS_ERR_LAUNCH;
-      // the fused merge's counters start at zero (and every call leaves them at zero)
-      if (hipMemset(ptr, 0, p.ws_bytes) != hipSuccess) {
-        (void)hipFree(ptr);
-        return DS_ERR_LAUNCH;
-      }
       slot = {ptr, p.ws_bytes};
     }
     ws = slot.first;

@@ -27,7 +27,7 @@ struct SelectParams {
   void* out_vals;            // slices == 1: sorted output values [rows][k]
   int32_t* out_idx;          // slices == 1: sorted output indices [rows][k]
   ds_stats* stats;           // NULL or [rows][slices]
-  uint32_t* arrive;          // fused merge: per-row arrival counters (zero between calls), else NULL
+  int32_t sorted_lists;      // slices > 1: store each slice's survivors sorted (for the list merge)
   int32_t presample;         // nonzero: the first whole block sets a presampled threshold
 };
 
@@ -62,19 +62,16 @@ constexpr Shape kMergeShape = {4, 4};  // 4 waves x 4 chunks x 128 entries = 204
 size_t select_lds_bytes(int k, int block, int slack, int waves);
 size_t select_scalars_bytes();
 
-// Split rows with at most this many slices merge inside the select kernel (the last slice of
-// a row to finish merges the sorted slice lists); more slices use the merge kernel.
-constexpr uint32_t kMaxFusedSlices = 8;
-
-// Split-row workspace layout: kArriveBytes of per-row arrival counters (the fused merge's;
-// zero between calls), then the slice lists. Fused plans need rows <= kArriveCounters.
-constexpr size_t kArriveBytes = 64 * 1024;
-constexpr int64_t kArriveCounters = kArriveBytes / 4;
+// Split rows with at most this many slices store sorted slice lists, which the list-merge
+// kernel merges; more slices use the merge kernel (DeepSelect over the survivors).
+constexpr uint32_t kMaxListSlices = 8;
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,
                          hipStream_t stream);
 hipError_t launch_merge(int dtype, const MergeParams& p, int64_t rows, size_t lds_bytes, hipStream_t stream);
+// One workgroup per row merges the row's p.entries / p.k sorted slice lists.
+hipError_t launch_merge_lists(int dtype, const MergeParams& p, int64_t rows, hipStream_t stream);
 hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 int64_t probe_read_groups(int64_t bytes);
 hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);

@@ -910,12 +910,102 @@ __device__ __forceinline__ void sort_store_lds(const uint32_t* fk, const uint32_
     store_out<DT>(out_vals, out_idx, pairs, row * k + i, (static_cast<uint64_t>(xk[i]) << 32) | xi[i]);
 }
 
-// Register sort when at most eight entries per thread are needed, else the LDS sort. The
-// sorted entries go to row `row` of the outputs, or, with pairs, to pairs[row * k ...].
+// Sort by runs and pairwise merges, for k <= 64 * kMaxRuns: every wave sorts runs of 64
+// entries in registers (a bitonic network over lane exchanges, best first), then RUNS runs
+// (a power of two; runs past k hold zero padding, which ranks below every element) are
+// merged in pairs until one is left. In a merge an entry's place is its position in its run
+// plus the number of entries of the partner run that rank above it (a binary search; equal
+// entries of the earlier run count as above, so equal padding gets distinct places). Each
+// round reads one half of xs and writes the other (xs: 2 * 64 * RUNS 64-bit words); the last
+// round stores the places below k.
+constexpr uint32_t kMaxRuns = 16;
+
+// Bitonic sort of one value per lane over the 64 lanes, largest first.
+__device__ __forceinline__ uint64_t wave_sort64(uint64_t v, uint32_t lane) {
+#pragma unroll
+  for (uint32_t size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t o = xor_lane64(v, stride, lane);
+      const bool take_max = ((lane & stride) == 0) == ((lane & size) == 0);
+      v = ((o > v) == take_max) ? o : v;
+    }
+  }
+  return v;
+}
+
+template <int DT, int WAVES, uint32_t RUNS>
+__device__ __forceinline__ void sort_runs_store(const uint32_t* fk, const uint32_t* fi, uint64_t* xs, uint32_t k,
+                                                void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t row) {
+  constexpr uint32_t NT = WAVES * 64, N = 64 * RUNS;
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  if constexpr (RUNS == 1) {
+    if (wave == 0) {
+      const uint64_t v = wave_sort64(lane < k ? comp_of(fk[lane], fi[lane]) : 0ull, lane);
+      if (lane < k) store_out<DT>(out_vals, out_idx, pairs, row * k + lane, v);
+    }
+    return;
+  }
+  __attribute__((address_space(3))) uint64_t* src = lds_ptr(xs);
+  __attribute__((address_space(3))) uint64_t* dst = src + N;
+  for (uint32_t r = wave; r < RUNS; r += WAVES) {
+    const uint32_t e = 64u * r + lane;
+    src[e] = wave_sort64(e < k ? comp_of(fk[e], fi[e]) : 0ull, lane);
+  }
+  lds_sync();
+#pragma unroll
+  for (uint32_t L = 64; L < N; L <<= 1) {
+    const bool last = 2u * L == N;
+    for (uint32_t e = tid; e < N; e += NT) {
+      const uint32_t r = e / L, i = e % L, pb = (r ^ 1u) * L;
+      const bool before = (r & 1u) != 0;  // the partner run comes first
+      const uint64_t c = src[e];
+      uint32_t pos = 0;
+#pragma unroll
+      for (uint32_t step = L; step > 0; step >>= 1) {
+        const uint64_t x = src[pb + min(pos + step, L) - 1u];
+        const bool above = x > c || (before && x == c);
+        pos = (pos + step <= L && above) ? pos + step : pos;
+      }
+      const uint32_t at = (r & ~1u) * L + i + pos;
+      if (last) {
+        if (at < k) store_out<DT>(out_vals, out_idx, pairs, row * k + at, c);
+      } else {
+        dst[at] = c;
+      }
+    }
+    if (!last) {
+      lds_sync();
+      __attribute__((address_space(3))) uint64_t* t = src;
+      src = dst;
+      dst = t;
+    }
+  }
+}
+
+// Sort of the k final entries, best first: by runs and ranks up to 64 * kMaxRuns entries
+// (xs: 64-bit scratch), the register bitonic sort when at most eight entries per thread are
+// needed, else the LDS bitonic sort. The sorted entries go to row `row` of the outputs, or,
+// with pairs, to pairs[row * k ...].
 template <int DT, int WAVES>
-__device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi, uint32_t k,
-                               void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t row) {
+__device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi,
+                                               uint64_t* xs, uint32_t k, void* out_vals, int32_t* out_idx,
+                                               uint2* pairs, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
+  if (k <= 64u * kMaxRuns) {
+    const uint32_t runs = (k + 63u) / 64u;
+    if (runs <= 1)
+      sort_runs_store<DT, WAVES, 1>(fk, fi, xs, k, out_vals, out_idx, pairs, row);
+    else if (runs <= 2)
+      sort_runs_store<DT, WAVES, 2>(fk, fi, xs, k, out_vals, out_idx, pairs, row);
+    else if (runs <= 4)
+      sort_runs_store<DT, WAVES, 4>(fk, fi, xs, k, out_vals, out_idx, pairs, row);
+    else if (runs <= 8)
+      sort_runs_store<DT, WAVES, 8>(fk, fi, xs, k, out_vals, out_idx, pairs, row);
+    else
+      sort_runs_store<DT, WAVES, 16>(fk, fi, xs, k, out_vals, out_idx, pairs, row);
+    return;
+  }
   uint32_t cap = 64;
   while (cap < k) cap <<= 1;
   if (cap > 8 * NT) {
@@ -941,15 +1031,18 @@ __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_
 
 // --------------------------------------------------------------------------- slice merge
 
-// Merge of a row's S sorted slice lists (S <= kMaxFusedSlices, k entries each, best first,
+// Merge of a row's S sorted slice lists (S <= kMaxListSlices, k entries each, best first,
 // as (key, index) pairs at src[s * k + i]) into the row's k best, sorted, written to the
 // outputs. The lists are loaded into LDS (lds: S * k 64-bit words) as composites; an entry's
 // place in the merged order is its position in its own list plus, for every other list, the
-// number of that list's entries that rank above it (a binary search; all composites are
-// distinct apart from padding, which ranks below every element and is never placed).
-template <int DT, int WAVES>
-__device__ __forceinline__ void merge_sorted_lists(const uint2* src, uint32_t S, uint32_t k, uint64_t* lds,
-                                                   void* out_vals, int32_t* out_idx, uint64_t row) {
+// number of that list's entries that rank above it (binary searches, all lists searched in
+// the same step with clamped, always valid indices; equal entries of earlier lists count as
+// above). Padding ranks below every element and is never placed.
+// Places the entries of lists [l0, l1) (all lists are loaded and searched).
+template <int DT, int WAVES, uint32_t MAXS>
+__device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint32_t k, uint64_t* lds,
+                                              void* out_vals, int32_t* out_idx, uint64_t row, uint32_t l0,
+                                              uint32_t l1) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x, total = S * k;
   __attribute__((address_space(3))) uint64_t* lw = lds_ptr(lds);
@@ -959,28 +1052,41 @@ __device__ __forceinline__ void merge_sorted_lists(const uint2* src, uint32_t S,
   }
   lds_sync();
   const uint32_t top = 1u << (31u - static_cast<uint32_t>(__builtin_clz(k)));  // largest power of two <= k
-  for (uint32_t e = tid; e < total; e += NT) {
+  for (uint32_t e = l0 * k + tid; e < l1 * k; e += NT) {
     uint32_t s = 0;
 #pragma unroll
-    for (uint32_t q = 1; q < kMaxFusedSlices; ++q) s += (q < S && e >= q * k) ? 1u : 0u;
+    for (uint32_t q = 1; q < MAXS; ++q) s += (q < S && e >= q * k) ? 1u : 0u;
     const uint64_t c = lw[e];
-    uint32_t rank = e - s * k;
-    uint32_t pos[kMaxFusedSlices];
+    uint32_t pos[MAXS];
 #pragma unroll
-    for (uint32_t q = 0; q < kMaxFusedSlices; ++q) pos[q] = 0;
+    for (uint32_t q = 0; q < MAXS; ++q) pos[q] = 0;
     for (uint32_t step = top; step > 0; step >>= 1) {
+      uint64_t x[MAXS];
 #pragma unroll
-      for (uint32_t q = 0; q < kMaxFusedSlices; ++q) {
-        if (q < S && q != s) {
-          const uint32_t at = pos[q] + step;
-          if (at <= k && lw[q * k + at - 1u] > c) pos[q] = at;
-        }
+      for (uint32_t q = 0; q < MAXS; ++q) x[q] = lw[min(q, S - 1u) * k + min(pos[q] + step, k) - 1u];
+#pragma unroll
+      for (uint32_t q = 0; q < MAXS; ++q) {
+        const bool above = x[q] > c || (q < s && x[q] == c);
+        pos[q] = (pos[q] + step <= k && above) ? pos[q] + step : pos[q];
       }
     }
+    uint32_t rank = e - s * k;
 #pragma unroll
-    for (uint32_t q = 0; q < kMaxFusedSlices; ++q) rank += pos[q];
+    for (uint32_t q = 0; q < MAXS; ++q) rank += (q < S && q != s) ? pos[q] : 0u;
     if (rank < k) store_out<DT>(out_vals, out_idx, nullptr, row * k + rank, c);
   }
+}
+
+template <int DT, int WAVES>
+__device__ __forceinline__ void merge_sorted_lists(const uint2* src, uint32_t S, uint32_t k, uint64_t* lds,
+                                                   void* out_vals, int32_t* out_idx, uint64_t row, uint32_t l0,
+                                                   uint32_t l1) {
+  if (S <= 2)
+    merge_lists_t<DT, WAVES, 2>(src, S, k, lds, out_vals, out_idx, row, l0, l1);
+  else if (S <= 4)
+    merge_lists_t<DT, WAVES, 4>(src, S, k, lds, out_vals, out_idx, row, l0, l1);
+  else
+    merge_lists_t<DT, WAVES, kMaxListSlices>(src, S, k, lds, out_vals, out_idx, row, l0, l1);
 }
 
 // Integer compare values for the streaming filter, from the threshold pair (key, idx).
@@ -1041,7 +1147,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   constexpr uint32_t CHUNK = 64 * VEC;
   constexpr uint32_t B = WAVES * CPW * CHUNK;
   constexpr uint32_t key_hi = DT == DS_BF16 ? 0xFFFFu : 0xFFFFFFFFu;  // largest possible key
-  static_assert(D == 2 || D == 4, "two or four buffers");
+  static_assert(D >= 2 && D <= 4, "two to four buffers");
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t m = (len + B - 1) / B;
 
@@ -1118,8 +1224,9 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     const uint32_t blk_lo = bid * B;
     const uint32_t abase = (nsurv ? L.k4 : 0u) + napp;  // append position of this block's first entry
     const uint32_t nxt = (b3 == 2 ? 0u : b3 + 1u);
+    bool accept_all = false;  // every element of the (whole) block was appended
     if constexpr (!MERGE) {
-      uint32_t s[CPW][VEC];
+      uint32_t s[CPW][VEC];  // the block's scores (bf16: the element in bits 16-31)
 #pragma unroll
       for (uint32_t t = 0; t < CPW; ++t) {
         if constexpr (DT == DS_BF16) {
@@ -1184,11 +1291,10 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
       const bool strict = idx_base + blk_lo > t_idx;
       const uint32_t thr = strict ? thr_s : thr_n;
       if (mode == 0 && blk_lo + B <= len) {
-        // accept everything: each wave stores its chunks (raw) contiguously
+        // accept everything: each wave stores its chunks (raw) contiguously, in wave order
         constexpr uint32_t tot = CPW * CHUNK;
-        uint32_t pos = 0;
-        if (lane == 0) pos = atomicAdd(&sc.blk[b3], tot);
-        pos = uni(pos) + abase;
+        const uint32_t pos = abase + wave * tot;
+        accept_all = true;
         if (tid == 0) sc.blk[nxt] = 0;
         uint32_t kmn = ~0u, kmx = 0;
 #pragma unroll
@@ -1338,7 +1444,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     if (st0) t_mark = wall_clock64();
     lds_sync();
     if (st0) sc.st_ts += wall_clock64() - t_mark;
-    napp += sc.blk[b3];
+    napp += accept_all ? B : sc.blk[b3];
     b3 = nxt;
     if (st0) sc.st_max = max(sc.st_max, static_cast<unsigned long long>(nsurv + napp));
     if (nsurv + napp >= k + B2) {
@@ -1364,10 +1470,8 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   for (uint32_t i = 0; i < m; i += D) {
     process(buf[0], bids[0], i);
     process(buf[1], bids[1], i + 1);
-    if constexpr (D == 4) {
-      process(buf[2], bids[2], i + 2);
-      process(buf[3], bids[3], i + 3);
-    }
+    if constexpr (D >= 3) process(buf[2], bids[2], i + 2);
+    if constexpr (D >= 4) process(buf[3], bids[3], i + 3);
   }
 
   // final compaction
@@ -1379,8 +1483,9 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   out.jsum = my_jsum;
 }
 
-// Buffers in flight per wave: four when the workgroup is small enough to leave the registers.
-constexpr int depth_for(int waves) { return waves >= 16 ? 2 : 4; }
+// Blocks in flight per wave (each CPW 16-byte chunks per lane): two for 16 waves (deeper
+// prefetch in 16-wave workgroups measured slower), four for smaller workgroups.
+constexpr int depth_for(int waves) { return waves < 16 ? 4 : 2; }
 
 // --------------------------------------------------------------------------- select kernel
 template <int DT, int WAVES, int CPW>
@@ -1458,31 +1563,16 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   }
 
   if (p.slices == 1) {
-    sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, p.out_vals, p.out_idx, nullptr, row);
-  } else if (!p.arrive) {
+    sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
+                              p.out_vals, p.out_idx, nullptr, row);
+  } else if (!p.sorted_lists) {
     uint2* const dst = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + static_cast<uint64_t>(slice) * k;
     for (uint32_t i = tid; i < k; i += NT) dst[i] = make_uint2(bo.fk[i], bo.fi[i]);
   } else {
-    // fused merge: each slice stores its survivors sorted; the row's last slice to finish
-    // (counted by a device-scope atomic) merges the lists and writes the output, then resets
-    // the counter for the next call
+    // the list-merge kernel merges the slices' sorted lists
     uint2* const rws = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries;
-    sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, nullptr, nullptr, rws + slice * k, 0);
-    // every wave's list stores are complete (workgroup barrier with global fences); one
-    // device-scope release by thread 0 then publishes them all before the arrival
-    __syncthreads();
-    if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      sc.pub[0] = atomicAdd(p.arrive + row, 1u);
-      if (sc.pub[0] == static_cast<uint32_t>(p.slices) - 1u)
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other slices' lists
-    }
-    __syncthreads();
-    if (sc.pub[0] == static_cast<uint32_t>(p.slices) - 1u) {
-      merge_sorted_lists<DT, WAVES>(rws, static_cast<uint32_t>(p.slices), k, reinterpret_cast<uint64_t*>(lds),
-                                    p.out_vals, p.out_idx, row);
-      if (tid == 0) p.arrive[row] = 0;
-    }
+    sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k, nullptr,
+                              nullptr, rws + slice * k, 0);
   }
   if (stats && tid == 0) {
     const uint64_t t_end = wall_clock64();
@@ -1523,7 +1613,21 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES), true>(L, sc, rs, len, 0u, k, B2, ord, 0u,
                                                            static_cast<uint32_t>(p.n - 1), false, false, bo);
-  sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, k, p.out_vals, p.out_idx, nullptr, row);
+  sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
+                            p.out_vals, p.out_idx, nullptr, row);
+}
+
+// --------------------------------------------------------------------------- list-merge kernel
+// One workgroup per (row, slice list) places that list's entries among the row's sorted slice
+// lists (at most kMaxListSlices).
+template <int DT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(MergeParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  const uint32_t S = static_cast<uint32_t>(p.entries / p.k);
+  const uint32_t row = blockIdx.x / S, list = blockIdx.x % S;
+  const uint32_t k = static_cast<uint32_t>(p.k);
+  merge_sorted_lists<DT, WAVES>(p.ws + static_cast<uint64_t>(row) * p.row_entries, S, k,
+                                reinterpret_cast<uint64_t*>(lds), p.out_vals, p.out_idx, row, list, list + 1u);
 }
 
 // --------------------------------------------------------------------------- probes
@@ -1603,6 +1707,19 @@ hipError_t launch_select_dt(int shape, const SelectParams& p, int64_t rows, size
 }
 
 template <int DT>
+hipError_t launch_merge_lists_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
+  auto kern = merge_lists_kernel<DT, 8>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  const int64_t S = p.entries / p.k;
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(rows * S)), dim3(8 * 64), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int DT>
 hipError_t launch_merge_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
   constexpr int W = kMergeShape.waves, C = kMergeShape.cpw;
   auto kern = merge_kernel<DT, W, C>;
@@ -1630,6 +1747,12 @@ hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int6
   const size_t dyn = lds_bytes - sizeof(Scalars);
   return dtype == DS_BF16 ? launch_select_dt<DS_BF16>(shape_index, p, rows, dyn, stream)
                           : launch_select_dt<DS_FP32>(shape_index, p, rows, dyn, stream);
+}
+
+hipError_t launch_merge_lists(int dtype, const MergeParams& p, int64_t rows, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(p.entries) * 8;
+  return dtype == DS_BF16 ? launch_merge_lists_dt<DS_BF16>(p, rows, lds, stream)
+                          : launch_merge_lists_dt<DS_FP32>(p, rows, lds, stream);
 }
 
 hipError_t launch_merge(int dtype, const MergeParams& p, int64_t rows, size_t lds_bytes, hipStream_t stream) {
