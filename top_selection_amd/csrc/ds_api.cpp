@@ -16,7 +16,7 @@ constexpr int64_t kMaxLdsBytes = 160 * 1024;    // LDS per workgroup on gfx950
 constexpr int64_t kMaxSliceBytes = 0x7FFFFF00;  // buffer offsets are 31-bit
 constexpr int kChunkBf16 = 512, kChunkFp32 = 256;
 constexpr int kMergeBlock = ds::kMergeShape.waves * ds::kMergeShape.cpw * 128;
-constexpr int kDefaultSlack = 2048;  // B2 when not forced (at least k)
+constexpr int kDefaultSlacks[] = {4096, 2048};  // B2 when not forced (at least k), largest that fits
 // default select shapes (indices into kSelectShapes), best first
 constexpr int kDefaultFp32[] = {8, 7, 2, 1};  // 16x2 (B=8192), 16x1 (4096), 4x2 (2048), 4x1 (1024)
 constexpr int kDefaultBf16[] = {7, 3, 1, 0};  // 16x1 (B=8192), 8x1 (4096), 4x1 (2048), 2x1 (1024)
@@ -90,18 +90,24 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   size_t lds = 0;
   auto fit = [&](int s) -> bool {
     const int b = kSelectShapes[s].waves * kSelectShapes[s].cpw * chunk;
-    int sl = c.slack ? c.slack : std::max(k, kDefaultSlack);
-    if (sl + b < sort_cap) {
-      if (c.slack) return false;  // the final sort runs in the append region
-      sl = sort_cap - b;
+    for (int want : kDefaultSlacks) {
+      int sl = c.slack ? c.slack : std::max(k, want);
+      if (sl + b < sort_cap) {
+        if (c.slack) return false;  // the final sort runs in the append region
+        sl = sort_cap - b;
+      }
+      const size_t l = ds::select_lds_bytes(k, b, sl, kSelectShapes[s].waves);
+      if (static_cast<int64_t>(l) > kMaxLdsBytes) {
+        if (c.slack) return false;
+        continue;
+      }
+      shape = s;
+      block = b;
+      slack = sl;
+      lds = l;
+      return true;
     }
-    const size_t l = ds::select_lds_bytes(k, b, sl, kSelectShapes[s].waves);
-    if (static_cast<int64_t>(l) > kMaxLdsBytes) return false;
-    shape = s;
-    block = b;
-    slack = sl;
-    lds = l;
-    return true;
+    return false;
   };
   if (c.block || c.waves) {
     for (int s = 0; s < kNumSelectShapes && shape < 0; ++s) {
