@@ -67,6 +67,10 @@ extern "C" {
  *              the block reach it), and the block only appends the elements that reach it.
  *              ON needs k <= 64 * waves and a whole first block; otherwise the plan falls
  *              back to OFF. Zero (auto) means ON. The result is the same either way.
+ *   order_group  G in {1, 2, 4}: the random order is drawn over groups of G consecutive
+ *              blocks, which are read in turn (G = 1 is the design note's order of single
+ *              blocks; larger G keeps consecutive loads in flight, measured faster on
+ *              MI355X). Zero (auto) means 2. The result is the same for every G.
  */
 #define DS_PRESAMPLE_AUTO 0
 #define DS_PRESAMPLE_OFF 1
@@ -78,6 +82,7 @@ typedef struct ds_config {
   int32_t slices;
   int32_t waves;
   int32_t presample;
+  int32_t order_group;
 } ds_config;
 
 /*

@@ -104,3 +104,11 @@ def test_presample_plan_field():
     with pytest.raises(ts.DSError) as e:
         ts.ds_topk_plan(4, 32768, 512, ts.BF16, {"presample": 3, "slices": 1})
     assert e.value.status == ts.DS_ERR_INVALID_ARG
+
+
+def test_order_group_plan_field():
+    assert ts.ds_topk_plan(64, 131072, 512, ts.BF16, {"slices": 4})["order_group"] == 2
+    assert ts.ds_topk_plan(64, 131072, 512, ts.BF16, {"slices": 4, "order_group": 1})["order_group"] == 1
+    with pytest.raises(ts.DSError) as e:
+        ts.ds_topk_plan(4, 32768, 512, ts.BF16, {"order_group": 3, "slices": 1})
+    assert e.value.status == ts.DS_ERR_INVALID_ARG

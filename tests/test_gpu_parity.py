@@ -121,11 +121,11 @@ def test_fuzz():
 ])
 def test_counters_match_model(dtype, n, k, block, slack, slices):
     """The kernel's A, R, W, max buffer length and read checksums equal the CPU model's under
-    the same Feistel block order, B, B2 and slicing (with the design note's start: no
-    presampled threshold)."""
+    the same Feistel block order, B, B2 and slicing (with the design note's start and order:
+    no presampled threshold, a random order of single blocks)."""
     x = gen.rows_family("normal", dtype, 17, 2, n)
     x[1] = gen.rows_family("ascending", dtype, 18, 1, n)[0]
-    cfg = {"block": block, "slack": slack, "slices": slices, "presample": ts.PRESAMPLE_OFF}
+    cfg = {"block": block, "slack": slack, "slices": slices, "presample": ts.PRESAMPLE_OFF, "order_group": 1}
     seed = 99
     say(f"[gpu] counters: n={n} k={k} cfg={cfg}")
     gv, gi, (plan, st) = run_gpu(x, k, seed=seed, cfg=cfg, stats=True)
@@ -226,3 +226,17 @@ def test_presample_on_and_off(dtype, family):
         assert int(res[ts.PRESAMPLE_ON][r, 0]["reads"]) == n
         if family == "normal":
             assert 2 * int(res[ts.PRESAMPLE_ON][r, 0]["appended"]) < int(res[ts.PRESAMPLE_OFF][r, 0]["appended"])
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+@pytest.mark.parametrize("group", [1, 2, 4])
+def test_order_groups(dtype, group):
+    """A random order over groups of G consecutive blocks gives the same result for every G,
+    including streams whose last group is partial (its missing blocks read nothing)."""
+    rows, k = 3, 256
+    for n in (6 * 8192 + 100, 13 * 8192, 3 * 8192 - 5):
+        for fam in ("normal", "ascending"):
+            x = gen.rows_family(fam, dtype, 51, rows, n)
+            cfg = {"slices": 1, "block": 8192, "order_group": group}
+            assert ts.ds_topk_plan(rows, n, k, dtype, cfg)["order_group"] == group
+            _check(x, k, f"group={group} n={n} {fam}", seed=9, cfg=cfg)

@@ -40,7 +40,7 @@ class DSError(RuntimeError):
 
 class ds_config(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("slack", ctypes.c_int32), ("slices", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("presample", ctypes.c_int32)]
+                ("waves", ctypes.c_int32), ("presample", ctypes.c_int32), ("order_group", ctypes.c_int32)]
 
 
 STATS_FIELDS = ["appended", "compactions", "work", "max_len", "reads", "index_sum", "monotone", "slice_lo",
@@ -101,7 +101,7 @@ def _cfg(cfg: Optional[Dict[str, int]]):
     if cfg is None:
         return None
     c = ds_config(int(cfg.get("block", 0)), int(cfg.get("slack", 0)), int(cfg.get("slices", 0)),
-                  int(cfg.get("waves", 0)), int(cfg.get("presample", 0)))
+                  int(cfg.get("waves", 0)), int(cfg.get("presample", 0)), int(cfg.get("order_group", 0)))
     return ctypes.pointer(c)
 
 
@@ -111,7 +111,7 @@ def ds_topk_plan(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, 
     if st != DS_OK:
         raise DSError(st, "ds_topk_plan")
     return {"block": out.block, "slack": out.slack, "slices": out.slices, "waves": out.waves,
-            "presample": out.presample}
+            "presample": out.presample, "order_group": out.order_group}
 
 
 def ds_topk_workspace_size(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, int]] = None) -> int:

@@ -41,6 +41,7 @@ struct Plan {
   int sort_cap;
   size_t lds;
   bool presample;   // the first whole block sets a presampled threshold
+  int order_group;  // G: the random order is over groups of G consecutive blocks
   // merge (slices > 1): the list-merge kernel over sorted slice lists, or the merge kernel
   bool list_merge;
   int mslack;
@@ -75,9 +76,11 @@ int check_basic(int64_t rows, int64_t n, int k, int dtype) {
 int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK) return st;
-  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0};
+  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0};
   if (c.block < 0 || c.slack < 0 || c.slices < 0 || c.waves < 0) return DS_ERR_INVALID_ARG;
   if (c.presample != DS_PRESAMPLE_AUTO && c.presample != DS_PRESAMPLE_OFF && c.presample != DS_PRESAMPLE_ON)
+    return DS_ERR_INVALID_ARG;
+  if (c.order_group != 0 && c.order_group != 1 && c.order_group != 2 && c.order_group != 4)
     return DS_ERR_INVALID_ARG;
   const int chunk = chunk_elems(dtype);
   const int eb = elem_bytes(dtype);
@@ -170,6 +173,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   p.sort_cap = sort_cap;
   p.lds = lds;
   p.presample = c.presample != DS_PRESAMPLE_OFF && k <= 64 * kSelectShapes[shape].waves;
+  p.order_group = c.order_group ? c.order_group : 2;
   if (slices > 1) {
     int ms = k > kMergeBlock ? k : kMergeBlock;
     if (ms + kMergeBlock < sort_cap) ms = sort_cap - kMergeBlock;
@@ -220,6 +224,7 @@ int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t r
   sp.stats = stats;
   sp.sorted_lists = pl.list_merge ? 1 : 0;
   sp.presample = pl.presample ? 1 : 0;
+  sp.group_shift = pl.order_group == 4 ? 2 : (pl.order_group == 2 ? 1 : 0);
   return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }
 
@@ -321,6 +326,7 @@ int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg
   out->slices = p.slices;
   out->waves = kSelectShapes[p.shape].waves;
   out->presample = p.presample ? DS_PRESAMPLE_ON : DS_PRESAMPLE_OFF;
+  out->order_group = p.order_group;
   return DS_OK;
 }
 

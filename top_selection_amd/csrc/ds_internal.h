@@ -29,6 +29,7 @@ struct SelectParams {
   ds_stats* stats;           // NULL or [rows][slices]
   int32_t sorted_lists;      // slices > 1: store each slice's survivors sorted (for the list merge)
   int32_t presample;         // nonzero: the first whole block sets a presampled threshold
+  int32_t group_shift;       // log2 of G: the block order is random over groups of G blocks
 };
 
 // One workgroup per row runs DeepSelect over the row's slices*k survivors.

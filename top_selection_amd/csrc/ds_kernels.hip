@@ -1140,7 +1140,8 @@ struct BodyOut {
 template <int DT, int WAVES, int CPW, int D, bool MERGE>
 __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amdgpu_buffer_rsrc_t rs, uint32_t len,
                                                 uint32_t idx_base, uint32_t k, uint32_t B2, const BlockOrder& ord,
-                                                uint32_t ilo, uint32_t ihi, bool stats, bool presample, BodyOut& out) {
+                                                uint32_t ilo, uint32_t ihi, bool stats, bool presample, uint32_t gshift,
+                                                BodyOut& out) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t IB = MERGE ? 8 : (DT == DS_BF16 ? 2 : 4);  // bytes per item
   constexpr uint32_t VEC = 16 / IB;                            // items per lane per chunk
@@ -1151,12 +1152,20 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t m = (len + B - 1) / B;
 
-  // block order: a table for streams of up to kOrdCap blocks, computed on the fly beyond
-  const bool tab = m <= kOrdCap;
+  // Block order: the permutation `ord` is over groups of 2^gshift consecutive blocks (ng of
+  // them); the i-th block read is block (i mod 2^gshift) of group ord(i >> gshift). Positions
+  // past the last block (the last group's padding, or steps past the end) read nothing. The
+  // group order is a table for up to kOrdCap groups, computed on the fly beyond.
+  const uint32_t ng = (m + (1u << gshift) - 1u) >> gshift, m_iter = ng << gshift;
+  const bool tab = ng <= kOrdCap;
   if (tab)
-    for (uint32_t i = tid; i < m; i += NT) L.ordt[i] = ord.at(i);
+    for (uint32_t i = tid; i < ng; i += NT) L.ordt[i] = ord.at(i);
   lds_sync();
-  auto bid_of = [&](uint32_t i) -> uint32_t { return i >= m ? m : (tab ? uni(L.ordt[i]) : ord.at(i)); };
+  auto bid_of = [&](uint32_t i) -> uint32_t {
+    if (i >= m_iter) return m;
+    const uint32_t b = ((tab ? uni(L.ordt[i >> gshift]) : ord.at(i >> gshift)) << gshift) | (i & ((1u << gshift) - 1u));
+    return b < m ? b : m;
+  };
 
   // threshold state (uniform across the workgroup)
   uint32_t mode = 0, thr_s = ~0u, thr_n = ~0u;  // mode 0: accept everything (no threshold yet)
@@ -1222,6 +1231,9 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   auto process = [&](u32x4(&bf)[CPW], uint32_t& bid_ref, uint32_t i) {
     const uint32_t bid = bid_ref;
     const uint32_t blk_lo = bid * B;
+    // the id of block i+D, read now: read after the filter's LDS stores, its wait would also
+    // wait for those stores and hold back the refill
+    const uint32_t next_bid = bid_of(i + D);
     const uint32_t abase = (nsurv ? L.k4 : 0u) + napp;  // append position of this block's first entry
     const uint32_t nxt = (b3 == 2 ? 0u : b3 + 1u);
     bool accept_all = false;  // every element of the (whole) block was appended
@@ -1437,7 +1449,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     }
 
     // refill this buffer with block i+D (blocks i+1 .. i+D-1 are already in flight)
-    bid_ref = bid_of(i + D);
+    bid_ref = next_bid;
 #pragma unroll
     for (uint32_t t = 0; t < CPW; ++t) bf[t] = load16(rs, addr(bid_ref, t));
 
@@ -1467,7 +1479,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   };
 
   // Steps past the last block use the empty block id m: no loads, no hits, no effect.
-  for (uint32_t i = 0; i < m; i += D) {
+  for (uint32_t i = 0; i < m_iter; i += D) {
     process(buf[0], bids[0], i);
     process(buf[1], bids[1], i + 1);
     if constexpr (D >= 3) process(buf[2], bids[2], i + 2);
@@ -1525,12 +1537,13 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   // starts are 16-byte aligned, so the rounded range never leaves the row's last chunk.
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(base), 0, static_cast<int>((len * EB + 15u) & ~15u), kRsrcWord3);
+  const uint32_t gshift = static_cast<uint32_t>(p.group_shift);
   BlockOrder ord;
-  ord.init(p.seed, row, slice, m);
+  ord.init(p.seed, row, slice, (m + (1u << gshift) - 1u) >> gshift);
 
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES), false>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
-                                                            slice_lo + len - 1u, stats, p.presample != 0, bo);
+                                                            slice_lo + len - 1u, stats, p.presample != 0, gshift, bo);
 
   if (stats) {
     uint64_t my_reads = bo.reads, my_jsum = bo.jsum;
@@ -1612,7 +1625,7 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
 
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES), true>(L, sc, rs, len, 0u, k, B2, ord, 0u,
-                                                           static_cast<uint32_t>(p.n - 1), false, false, bo);
+                                                           static_cast<uint32_t>(p.n - 1), false, false, 0u, bo);
   sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
                             p.out_vals, p.out_idx, nullptr, row);
 }
