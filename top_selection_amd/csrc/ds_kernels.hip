@@ -529,6 +529,37 @@ __device__ __forceinline__ void ties_all(const Segs& sg, uint32_t tid, uint32_t 
   }
 }
 
+// Stores entry c (a composite) at position `at` of the outputs, or, with pairs, as a (key,
+// index) pair at pairs[at].
+template <int DT>
+__device__ __forceinline__ void store_out(void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t at, uint64_t c) {
+  const uint32_t key = static_cast<uint32_t>(c >> 32), id = ~static_cast<uint32_t>(c);
+  if (pairs) {
+    pairs[at] = make_uint2(key, id);
+    return;
+  }
+  if (out_vals) {
+    if constexpr (DT == DS_BF16)
+      static_cast<uint16_t*>(out_vals)[at] = static_cast<uint16_t>(raw_of_key<DT>(key));
+    else
+      static_cast<uint32_t*>(out_vals)[at] = raw_of_key<DT>(key);
+  }
+  if (out_idx) out_idx[at] = static_cast<int32_t>(id);
+}
+
+// Where a final compaction may write its survivors directly, sorted: row `row` of the
+// outputs, or pairs[row * k ...] when pairs is set.
+struct OutSpec {
+  void* vals;
+  int32_t* idx;
+  uint2* pairs;
+  uint64_t row;
+};
+
+// A final compaction sorts its survivors itself (a counting sort over its value bins) when
+// no value bin above the pivot holds more entries than this.
+constexpr uint32_t kSortedBinCap = 32;
+
 // The pivot window a compaction ends with: value bin vbin_p (vm), else keys [plo, phi], or,
 // for ties, key pkey with indices [iplo, iphi].
 struct Pivot {
@@ -539,9 +570,12 @@ struct Pivot {
 
 // Scatter of all entries: those above the pivot window go to (dk, di), those inside it to
 // the list.
+// With bin_slots (value bins only), an entry above the pivot bin takes the next slot of its
+// bin from bin_slots (each bin's first slot, highest bins first) instead of a slot in arrival
+// order, so the destination ends up ordered by bin.
 template <int DT>
 __device__ __forceinline__ void scatter_all(const Segs& sg, uint32_t tid, uint32_t nt, uint32_t lane, const Pivot& pv,
-                                            uint32_t* dk, uint32_t* di, Scalars& sc) {
+                                            uint32_t* dk, uint32_t* di, Scalars& sc, uint32_t* bin_slots) {
   const uint32_t g1 = (sg.n1 + 3u) / 4u, groups = g1 + (sg.n0 + 3u) / 4u;
   const uint32_t iters = (groups + nt - 1u) / nt;
   for (uint32_t it = 0; it < iters; ++it) {
@@ -565,6 +599,12 @@ __device__ __forceinline__ void scatter_all(const Segs& sg, uint32_t tid, uint32
         const uint32_t b = vbin<DT>(key, pv.vb);
         up[q] = valid && b > pv.vbin_p;
         mid[q] = valid && b == pv.vbin_p;
+        if (bin_slots && up[q]) {  // sorted mode: the bin's next slot
+          const uint32_t at = __atomic_fetch_add(lds_ptr(&bin_slots[hslot(b)]), 1u, __ATOMIC_RELAXED);
+          dk[at] = key;
+          di[at] = id;
+          up[q] = false;
+        }
       } else if (!pv.tie) {
         up[q] = valid && key > pv.phi;
         mid[q] = valid && key >= pv.plo && key <= pv.phi;
@@ -612,11 +652,12 @@ template <int WAVES, int DT, bool RAW>
 __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, bool fin, bool have_t,
                         uint32_t key_hi, uint32_t ilo, uint32_t ihi, Scalars& sc, uint32_t* hist2, uint32_t& hpar,
                         uint32_t& tkey, uint32_t& tidx, uint32_t& maxkey, uint32_t vlo_key, uint32_t vhi_key,
-                        bool vok) {
+                        bool vok, const OutSpec* so, bool& sorted) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t n = sg.n0 + sg.n1;
 
+  sorted = false;
   if (n <= k) {  // keep everything (only the final call can get here)
     const uint32_t k4 = round4(k);
     for (uint32_t i = tid; i < k4; i += NT) {
@@ -680,6 +721,42 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
       uint32_t bin, above, c;
       scan_select(h, need, lane, bin, above, c);
       uint32_t blo = 0, bhi = 0;
+      if (so && fin && pv.vm && c <= kListCap) {
+        // Counting sort for the output: each bin above the pivot gets its first slot (the
+        // entries of the higher bins come first), written over its count, and blo becomes
+        // the largest such count. Lane l holds bins [32 (63 - l), 32 (64 - l)).
+        // (16-byte groups of four bins at the bin scan's swizzled addresses; in a group the
+        // lowest bin comes first)
+        constexpr uint32_t Q = kPer / 4;
+        const uint32_t hb = 63u - lane, sw = hb & 7u;
+        uint4 g[Q];  // g[0]: the lane's highest four bins
+        uint32_t lsum = 0, lmax = 0;
+#pragma unroll
+        for (uint32_t j = 0; j < Q; ++j) {
+          g[j] = *reinterpret_cast<const uint4*>(h + 32u * hb + 4u * ((Q - 1u - j) ^ sw));
+          const uint32_t b0 = 32u * hb + 4u * (Q - 1u - j);
+          lsum += g[j].x + g[j].y + g[j].z + g[j].w;
+          lmax = b0 + 3u > bin ? max(lmax, g[j].w) : lmax;
+          lmax = b0 + 2u > bin ? max(lmax, g[j].z) : lmax;
+          lmax = b0 + 1u > bin ? max(lmax, g[j].y) : lmax;
+          lmax = b0 > bin ? max(lmax, g[j].x) : lmax;
+        }
+        uint32_t off = wave_incl_scan(lsum) - lsum;
+#pragma unroll
+        for (uint32_t j = 0; j < Q; ++j) {
+          uint4 o;
+          o.w = off;
+          off += g[j].w;
+          o.z = off;
+          off += g[j].z;
+          o.y = off;
+          off += g[j].y;
+          o.x = off;
+          off += g[j].x;
+          *reinterpret_cast<uint4*>(h + 32u * hb + 4u * ((Q - 1u - j) ^ sw)) = o;
+        }
+        blo = wave_max32(lmax);
+      }
       if (pv.vm && c > kListCap) {  // the key range of the value bin, for the key passes
         blo = static_cast<uint32_t>(vbin_first_key<DT>(bin, vlo_key, key_of_inf<DT>(), pv.vb, lane));
         bhi = bin + 1u < kBins
@@ -737,9 +814,12 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
     }
   }
   cnt = cnt < kListCap ? cnt : kListCap;  // more only if (key, index) pairs repeat
+  // the final pass's histogram holds bin slots when the output can be sorted here
+  uint32_t* const slots = hist2 + kBins * ((hpar + 1u) & 1u);
+  const bool srt = so && fin && pv.vm && sc.pub[4] <= kSortedBinCap;
 
   // scatter: entries above the pivot window go to the destination, the window's to the list
-  scatter_all<DT>(sg, tid, NT, lane, pv, dk, di, sc);
+  scatter_all<DT>(sg, tid, NT, lane, pv, dk, di, sc, srt ? slots : nullptr);
   lds_sync();
 
   // wave 0 ranks the short list, places the `need` best of it after the above_total entries
@@ -751,8 +831,12 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
     uint32_t rank = 0;
     for (uint32_t m = 0; m < cnt; ++m) rank += readlane64(mine, m) > mine ? 1u : 0u;
     if (have && rank < need) {
-      dk[above_total + rank] = lk;
-      di[above_total + rank] = li;
+      if (srt) {
+        store_out<DT>(so->vals, so->idx, so->pairs, so->row * k + above_total + rank, mine);
+      } else {
+        dk[above_total + rank] = lk;
+        di[above_total + rank] = li;
+      }
     }
     const uint64_t piv = ballot(have && rank == need - 1u);
     const uint32_t pl = piv ? static_cast<uint32_t>(__builtin_ctzll(piv)) : 0u;
@@ -761,11 +845,25 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
       sc.pub[1] = __builtin_amdgcn_readlane(li, pl);
     }
   }
+  if (srt) {
+    // each entry above the pivot bin sits inside its bin's slots, [end of the next higher
+    // bin, end of its bin); its place is the bin's start plus the entries of the bin that
+    // rank above it
+    for (uint32_t s = tid; s < above_total; s += NT) {
+      const uint32_t key = dk[s], id = di[s];
+      const uint32_t b = vbin<DT>(key, pv.vb);
+      const uint32_t end = slots[hslot(b)], start = b + 1u < kBins ? slots[hslot(b + 1u)] : 0u;
+      const uint64_t c = comp_of(key, id);
+      uint32_t r = 0;
+      for (uint32_t j = start; j < end; ++j) r += comp_of(dk[j], di[j]) > c ? 1u : 0u;
+      store_out<DT>(so->vals, so->idx, so->pairs, so->row * k + start + r, c);
+    }
+    sorted = true;
+  }
   lds_sync();
   tkey = sc.pub[0];
   tidx = sc.pub[1];
   maxkey = seen_max;
-  (void)fin;
 }
 
 // --------------------------------------------------------------------------- final sort
@@ -826,24 +924,6 @@ constexpr int bitonic_barriers() {
     for (uint32_t stride = size >> 1; stride > 0; stride >>= 1)
       if (stride >= 64u * E) c += 2;
   return c;
-}
-
-// Stores entry c (a composite) at position `at` of the outputs, or, with pairs, as a (key,
-// index) pair at pairs[at].
-template <int DT>
-__device__ __forceinline__ void store_out(void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t at, uint64_t c) {
-  const uint32_t key = static_cast<uint32_t>(c >> 32), id = ~static_cast<uint32_t>(c);
-  if (pairs) {
-    pairs[at] = make_uint2(key, id);
-    return;
-  }
-  if (out_vals) {
-    if constexpr (DT == DS_BF16)
-      static_cast<uint16_t*>(out_vals)[at] = static_cast<uint16_t>(raw_of_key<DT>(key));
-    else
-      static_cast<uint32_t*>(out_vals)[at] = raw_of_key<DT>(key);
-  }
-  if (out_idx) out_idx[at] = static_cast<int32_t>(id);
 }
 
 // Sorts the k entries (fk, fi) (k <= 2^LOGT, padded with zeros) best first and stores them.
@@ -1131,6 +1211,7 @@ struct BodyOut {
   const uint32_t* fk;
   const uint32_t* fi;
   uint64_t reads, jsum;  // this thread's share of the elements read and of their indices
+  bool sorted;           // the final compaction already wrote the sorted output
 };
 
 // D buffers of CPW chunks per wave are in flight: block i+D is loaded into the registers of
@@ -1141,7 +1222,7 @@ template <int DT, int WAVES, int CPW, int D, bool MERGE>
 __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amdgpu_buffer_rsrc_t rs, uint32_t len,
                                                 uint32_t idx_base, uint32_t k, uint32_t B2, const BlockOrder& ord,
                                                 uint32_t ilo, uint32_t ihi, bool stats, bool presample, uint32_t gshift,
-                                                BodyOut& out) {
+                                                const OutSpec* fso, BodyOut& out) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t IB = MERGE ? 8 : (DT == DS_BF16 ? 2 : 4);  // bytes per item
   constexpr uint32_t VEC = 16 / IB;                            // items per lane per chunk
@@ -1197,6 +1278,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     for (uint32_t t = 0; t < CPW; ++t) buf[d][t] = load16(rs, addr(bids[d], t));
   }
 
+  bool sorted = false;
   auto compaction = [&](bool fin) {
     const Segs sg = nsurv ? make_segs(sur_a ? L.ck : L.bk, sur_a ? L.ci : L.bi, nsurv, L.ck + L.k4, L.ci + L.k4, napp)
                           : make_segs(nullptr, nullptr, 0u, L.ck, L.ci, napp);
@@ -1218,7 +1300,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
       vok = range_ok;
     }
     compact<WAVES, DT, !MERGE>(sg, to_a ? L.ck : L.bk, to_a ? L.ci : L.bi, k, fin, nsurv != 0, key_hi, ilo, ihi, sc,
-                               L.hist, hpar, t_key, t_idx, maxkey, vlo, vhi, vok);
+                               L.hist, hpar, t_key, t_idx, maxkey, vlo, vhi, vok, fin ? fso : nullptr, sorted);
     if (st0) {
       sc.st_a += napp;
       sc.st_w += nsurv + napp;
@@ -1493,6 +1575,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   out.fi = sur_a ? L.ci : L.bi;
   out.reads = my_reads;
   out.jsum = my_jsum;
+  out.sorted = sorted;
 }
 
 // Blocks in flight per wave (each CPW 16-byte chunks per lane): two for 16 waves (deeper
@@ -1541,9 +1624,16 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   BlockOrder ord;
   ord.init(p.seed, row, slice, (m + (1u << gshift) - 1u) >> gshift);
 
+  // the final compaction writes the sorted output itself when it can: the row's outputs, or
+  // the slice's sorted list for the list merge
+  OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
+  if (p.slices > 1) fso = OutSpec{nullptr, nullptr, p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + slice * k, 0};
+  const bool own_sort = p.slices == 1 || p.sorted_lists;
+
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES), false>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
-                                                            slice_lo + len - 1u, stats, p.presample != 0, gshift, bo);
+                                                            slice_lo + len - 1u, stats, p.presample != 0, gshift,
+                                                            own_sort ? &fso : nullptr, bo);
 
   if (stats) {
     uint64_t my_reads = bo.reads, my_jsum = bo.jsum;
@@ -1575,7 +1665,9 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
     }
   }
 
-  if (p.slices == 1) {
+  if (bo.sorted) {
+    // done by the final compaction
+  } else if (p.slices == 1) {
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
                               p.out_vals, p.out_idx, nullptr, row);
   } else if (!p.sorted_lists) {
@@ -1623,11 +1715,13 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   BlockOrder ord;
   ord.init(p.seed, row, 0x7FFFFFFFu, m);
 
+  const OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES), true>(L, sc, rs, len, 0u, k, B2, ord, 0u,
-                                                           static_cast<uint32_t>(p.n - 1), false, false, 0u, bo);
-  sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
-                            p.out_vals, p.out_idx, nullptr, row);
+                                                           static_cast<uint32_t>(p.n - 1), false, false, 0u, &fso, bo);
+  if (!bo.sorted)
+    sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
+                              p.out_vals, p.out_idx, nullptr, row);
 }
 
 // --------------------------------------------------------------------------- list-merge kernel
