@@ -5,9 +5,10 @@ A step is one whole top-k call (select kernel over every row slice, then the mer
 over one batch of synthetic input already resident in HBM. Each step reads a different copy
 of the input from a pool of >= 512 MiB, so the 256 MB Infinity Cache cannot serve it (cold).
 Timing: W warmup steps, then K steps recorded into one HIP graph and replayed between two
-events (the headline: no host launch gaps); then the same K steps launched one by one with
-events around every select launch (the select kernel's own average duration, the roofline
-figure). The same loop over one buffer is reported as the warm figure. The CPU oracle is
+events (the headline: no host launch gaps); K select launches alone in one graph (the select
+kernel's average duration per launch, the roofline figure; it agrees with the profiler's
+kernel time); and the same K steps launched one by one (eager). The same loops over one
+buffer are reported as the warm figures. The CPU oracle is
 timed on the host cores on a bounded sample of the same workload.
 
 Two more modes serve the committed rocprofv3 counter summary: --counter-pass runs the
@@ -117,17 +118,21 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
         sel = [a.elapsed_time(b) for a, b in mids]
         return total / steps, sum(sel) / len(sel)
 
-    def graph_timed(get_src):
-        """K steps captured into one graph, replayed once between two events."""
+    def select_only(src):
+        ts.ds_topk_slices(src, k, seed=seed, workspace=ws, out_vals=vals, out_idx=idx, indices=idx is not None)
+
+    def graph_timed(get_src, fn=step):
+        """K steps (or K launches of fn) captured into one graph, replayed once between two
+        events; returns ms per step."""
         gs = torch.cuda.Stream()
         gs.wait_stream(stream)
         with torch.cuda.stream(gs):
-            step(get_src(0))
+            fn(get_src(0))
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=gs):
             for i in range(steps):
-                step(get_src(i))
+                fn(get_src(i))
         torch.cuda.synchronize()
         g.replay()  # warm the graph once
         torch.cuda.synchronize()
@@ -147,6 +152,9 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
     log(f"[bench] {w.name} cold graph: {ms_graph * 1e3:.2f} us/call")
     ms_graph_warm = graph_timed(lambda i: pool[0])
     log(f"[bench] {w.name} warm graph: {ms_graph_warm * 1e3:.2f} us/call")
+    # the select kernel alone, back to back in a graph: its average duration per launch
+    ms_select = graph_timed(lambda i: pool[i % copies], select_only)
+    log(f"[bench] {w.name} select kernel (graph, cold): {ms_select * 1e3:.2f} us/launch")
 
     parity = None
     if verify:
@@ -161,7 +169,7 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
         parity = "bit-exact" if ok else "MISMATCH"
         log(f"[bench] {w.name} parity vs oracle: {parity}")
     del pool
-    return dict(x=x, plan=plan, copies=copies, ms_cold=ms_graph, ms_eager=ms_cold, sel_cold=sel_cold,
+    return dict(x=x, plan=plan, copies=copies, ms_cold=ms_graph, ms_eager=ms_cold, sel_cold=ms_select, sel_eager=sel_cold,
                 ms_warm=ms_graph_warm, ms_warm_eager=ms_warm, sel_warm=sel_warm, in_bytes=in_bytes, parity=parity,
                 ws_bytes=wsb)
 
@@ -264,6 +272,45 @@ def write_counters(workload, fetch_dir, write_dir, command):
     log(f"[bench] wrote {path}: {total:.0f} B per launch ({total / algo:.3f} x algorithmic)")
 
 
+def write_trace(workload, trace_dir, command):
+    """Summary of a rocprofv3 --kernel-trace --stats run of bench.py into profiles/."""
+    import csv
+    import glob
+    from workloads import gen
+    w = gen.WORKLOADS[workload]
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    with open(paths[0]) as f:
+        rows = list(csv.DictReader(f))
+    lines = [
+        f"# Kernel trace, {workload}",
+        "",
+        f"Workload: {w.description}; the bench's default plan, its timed steps plus warmup (graph, eager and "
+        f"warm passes, the select-only graph and one parity call).",
+        "",
+        "Command (on one MI355X, from the repository root; R is the repository path):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in rows[:8]:
+        name = r["Name"].replace("void ds::(anonymous namespace)::", "")
+        if len(name) > 70:
+            name = name[:67] + "..."
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} % |")
+    lines.append("")
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}_trace.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    log(f"[bench] wrote {path}")
+
+
 def cpu_baseline(w, k, x, seconds):
     from oracle import topk as otk
     threads = otk.hw_threads()
@@ -295,10 +342,15 @@ def main() -> int:
                     help="run select launches and a calibration copy for a rocprofv3 --pmc run, then exit")
     ap.add_argument("--write-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
                     help="summarise two rocprofv3 --pmc output folders into profiles/ (no GPU needed)")
+    ap.add_argument("--write-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
+                    help="summarise a rocprofv3 --kernel-trace --stats output folder into profiles/ (no GPU needed)")
     args = ap.parse_args()
 
     if args.write_counters:
         write_counters(args.workload, *args.write_counters)
+        return 0
+    if args.write_trace:
+        write_trace(args.workload, *args.write_trace)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -341,7 +393,9 @@ def main() -> int:
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "timing": "K steps captured in one HIP graph, replayed between two events",
         "eager": {"value": round(r["in_bytes"] / (r["ms_eager"] * 1e-3) / 1e9, 2),
-                  "ms_per_step": round(r["ms_eager"], 6), "note": "the same K steps launched one by one"},
+                  "ms_per_step": round(r["ms_eager"], 6), "select_us": round(r["sel_eager"] * 1e3, 3),
+                  "note": "the same K steps launched one by one; select_us spans event to event around "
+                          "each select launch (host launch latency included)"},
         "warm": {"value": round(r["in_bytes"] / (r["ms_warm"] * 1e-3) / 1e9, 2), "ms_per_step": round(r["ms_warm"], 6),
                  "note": "same input buffer every step (may be served by the Infinity Cache)"},
         "pages_style_gbs": round((r["in_bytes"] + w.rows * k * (w.elem_bytes + (0 if w.values_only else 4)))
@@ -350,6 +404,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "select_kernel", "achieved": round(sel_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(sel_gbs / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(r["sel_cold"] * 1e3, 3),
+                     "timing": "K select launches back to back in one HIP graph, events on its stream",
                      "algorithmic_bytes_per_launch": r["in_bytes"],
                      "traffic": traffic, "source": digest},
     }
