@@ -243,6 +243,7 @@ int run_merge(const Plan& pl, int64_t rows, int64_t n, int k, uint64_t seed, voi
   mp.seed = seed;
   mp.out_vals = out_vals;
   mp.out_idx = out_idx;
+  mp.presample = pl.presample && k <= 64 * ds::kMergeShape.waves ? 1 : 0;
   if (pl.list_merge) return ds::launch_merge_lists(pl.dtype, mp, rows, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
   return ds::launch_merge(pl.dtype, mp, rows, pl.mlds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }

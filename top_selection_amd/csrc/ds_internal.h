@@ -44,6 +44,7 @@ struct MergeParams {
   uint64_t seed;
   void* out_vals;
   int32_t* out_idx;
+  int32_t presample;   // nonzero: the first whole block sets a presampled threshold
 };
 
 // A compiled kernel shape: waves per workgroup and 16-byte chunks per wave per block.
@@ -56,7 +57,7 @@ struct Shape {
 // waves * cpw * 64 lanes * (16 / elem_bytes) elements.
 constexpr Shape kSelectShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}, {8, 2}, {4, 4}, {8, 4}, {16, 1}, {16, 2}};
 constexpr int kNumSelectShapes = sizeof(kSelectShapes) / sizeof(kSelectShapes[0]);
-constexpr Shape kMergeShape = {4, 4};  // 4 waves x 4 chunks x 128 entries = 2048 entries per block
+constexpr Shape kMergeShape = {16, 2};  // 16 waves x 2 chunks x 128 entries = 4096 entries per block
 
 // LDS bytes a select/merge workgroup needs, and the part of them that is not the dynamic
 // array (the per-workgroup scalars).

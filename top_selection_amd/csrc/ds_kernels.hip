@@ -1308,6 +1308,40 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     sur_a = to_a;
   };
 
+  // Threshold from the first (whole) block instead of "accept everything", from each lane's
+  // largest key lmax: each wave takes the j-th largest of its lanes' maxima, j = ceil(k /
+  // WAVES), found bit by bit over the key's top 16 bits (a truncation can only lower it); the
+  // smallest of the waves' values T0 has at least WAVES * j >= k distinct elements (one per
+  // lane) at or above it, so T0 does not exceed the k-th element and "key >= T0" keeps every
+  // element that can be in the top k.
+  auto presample_from = [&](uint32_t lmax) {
+    constexpr uint32_t KB = DT == DS_BF16 ? 16u : 32u;
+    const uint32_t j = (k + WAVES - 1) / WAVES;
+    uint32_t pre = 0;
+#pragma unroll
+    for (uint32_t b = KB; b > KB - 16u; --b) {
+      const uint32_t cand = pre | (1u << (b - 1u));
+      pre = popc(ballot(lmax >= cand)) >= j ? cand : pre;
+    }
+    const uint32_t wmax = wave_max32(lmax);
+    if (lane == 0) {
+      sc.rmin[wave] = pre;
+      sc.rmax[wave] = wmax;
+    }
+    lds_sync();
+    uint32_t t0 = ~0u, hi = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      t0 = min(t0, sc.rmin[w]);
+      hi = max(hi, sc.rmax[w]);
+    }
+    t_key = t0;
+    t_idx = ~0u;  // ties with T0 are kept in every block
+    pre_hi = hi;
+    presampled = true;
+    mode = 1;
+  };
+
   // Filter block `bid` (the i-th in the order) from `buf`, refill `buf` with block i+D, sync,
   // and compact when the buffer is full.
   auto process = [&](u32x4(&bf)[CPW], uint32_t& bid_ref, uint32_t i) {
@@ -1344,42 +1378,13 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
         }
       }
       if (presample && i == 0 && blk_lo + B <= len) {
-        // Threshold from the first (whole) block instead of "accept everything": each wave
-        // takes the j-th largest of its lanes' maxima, j = ceil(k / WAVES), found bit by bit
-        // over the key's top 16 bits (a truncation can only lower it); the smallest of the
-        // waves' values T0 has at least WAVES * j >= k distinct elements (one per lane) at
-        // or above it, so T0 does not exceed the k-th element and "key >= T0" keeps every
-        // element that can be in the top k.
-        constexpr uint32_t KB = DT == DS_BF16 ? 16u : 32u;
         uint32_t lmax = 0;
 #pragma unroll
         for (uint32_t t = 0; t < CPW; ++t) {
 #pragma unroll
           for (uint32_t q = 0; q < VEC; ++q) lmax = max(lmax, key_of_score<DT>(s[t][q]));
         }
-        const uint32_t j = (k + WAVES - 1) / WAVES;
-        uint32_t pre = 0;
-#pragma unroll
-        for (uint32_t b = KB; b > KB - 16u; --b) {
-          const uint32_t cand = pre | (1u << (b - 1u));
-          pre = popc(ballot(lmax >= cand)) >= j ? cand : pre;
-        }
-        const uint32_t wmax = wave_max32(lmax);
-        if (lane == 0) {
-          sc.rmin[wave] = pre;
-          sc.rmax[wave] = wmax;
-        }
-        lds_sync();
-        uint32_t t0 = ~0u, hi = 0;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-          t0 = min(t0, sc.rmin[w]);
-          hi = max(hi, sc.rmax[w]);
-        }
-        t_key = t0;
-        t_idx = ~0u;  // ties with T0 are kept in every block
-        pre_hi = hi;
-        presampled = true;
+        presample_from(lmax);
         filter_thresholds<DT>(t_key, mode, thr_s, thr_n);
       }
       const bool strict = idx_base + blk_lo > t_idx;
@@ -1492,6 +1497,12 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
         }
       }
     } else {
+      if (presample && i == 0 && blk_lo + B <= len) {
+        uint32_t lmax = 0;  // every item of a whole block is real
+#pragma unroll
+        for (uint32_t t = 0; t < CPW; ++t) lmax = max(lmax, max(bf[t][0], bf[t][2]));
+        presample_from(lmax);
+      }
       // merge: items are (key, index) pairs; a hit beats T in the composite order
       bool h[CPW][2];
       uint64_t mk[CPW][2];
@@ -1718,7 +1729,8 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   const OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES), true>(L, sc, rs, len, 0u, k, B2, ord, 0u,
-                                                           static_cast<uint32_t>(p.n - 1), false, false, 0u, &fso, bo);
+                                                           static_cast<uint32_t>(p.n - 1), false, p.presample != 0, 0u,
+                                                           &fso, bo);
   if (!bo.sorted)
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
                               p.out_vals, p.out_idx, nullptr, row);
