@@ -453,6 +453,25 @@ __device__ __forceinline__ void scan_select(const uint32_t* h, uint32_t need, ui
 // Barriers: two per histogram pass (after the counts; after the scan result is published),
 // one after the scatter and one after the list is ranked.
 
+// Adds one group's four counts (cnt[q] in {0, 1}) to their bins (bin[q]), one atomic per
+// run of equal neighbouring bins: entries next to each other in the buffer are usually
+// neighbours in the stream, and on rows with long runs of equal values this turns thousands
+// of same-address atomics into a few.
+__device__ __forceinline__ void add_runs(uint32_t* h, const uint32_t (&bin)[4], const uint32_t (&cnt)[4]) {
+  uint32_t emit[4];
+  uint32_t acc = cnt[3];
+#pragma unroll
+  for (int q = 2; q >= 0; --q) {
+    const bool same = bin[q] == bin[q + 1];
+    emit[q + 1] = same ? 0u : acc;
+    acc = same ? acc + cnt[q] : cnt[q];
+  }
+  emit[0] = acc;
+#pragma unroll
+  for (uint32_t q = 0; q < 4; ++q)
+    if (emit[q]) atomicAdd(&h[hslot(bin[q])], emit[q]);
+}
+
 // Group g of the compaction's entries: the appended segment's groups come first, then the
 // survivors'. Sets the group's key and index pointers and returns how many of its four
 // slots hold entries (the slots up to a multiple of four exist).
@@ -495,16 +514,26 @@ __device__ __forceinline__ uint32_t hist_all(const Segs& sg, uint32_t tid, uint3
                            key_of_score<DT>(kk[u].w));
         *lds_ptr(reinterpret_cast<u32x4*>(kp[u])) = u32x4{kk[u].x, kk[u].y, kk[u].z, kk[u].w};
       }
+      if (vm) {  // value bins spread entries: one atomic each
 #pragma unroll
-      for (uint32_t q = 0; q < 4; ++q) {
-        const uint32_t key = u4get(kk[u], q);
-        if (q < nv[u]) {
-          mx = max(mx, key);
-          if (vm)
+        for (uint32_t q = 0; q < 4; ++q) {
+          const uint32_t key = u4get(kk[u], q);
+          if (q < nv[u]) {
+            mx = max(mx, key);
             atomicAdd(&h[hslot(vbin<DT>(key, vb))], 1u);
-          else if (key >= plo && (key <= phi || open))
-            atomicAdd(&h[hslot((min(key, phi) - plo) >> shift)], 1u);
+          }
         }
+      } else {  // key bins: runs of equal keys are common (ties), one atomic per run
+        uint32_t bin[4], cnt[4];
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+          const uint32_t key = u4get(kk[u], q);
+          const bool valid = q < nv[u];
+          mx = valid ? max(mx, key) : mx;
+          bin[q] = (min(key, phi) - plo) >> shift;
+          cnt[q] = (valid && key >= plo && (key <= phi || open)) ? 1u : 0u;
+        }
+        add_runs(h, bin, cnt);
       }
     }
   }
@@ -520,12 +549,14 @@ __device__ __forceinline__ void ties_all(const Segs& sg, uint32_t tid, uint32_t 
     const uint32_t nv = group_at(sg, g, g1, kp, ip);
     const uint4 kk = *reinterpret_cast<const uint4*>(kp);
     const uint4 ii = *reinterpret_cast<const uint4*>(ip);
+    uint32_t bin[4], cnt[4];
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
       const uint32_t key = u4get(kk, q), id = u4get(ii, q);
-      if (q < nv && key == pkey && id >= iplo && id <= iphi)
-        atomicAdd(&h[hslot(kBins - 1u - ((id - iplo) >> shift))], 1u);
+      bin[q] = kBins - 1u - ((id - iplo) >> shift);
+      cnt[q] = (q < nv && key == pkey && id >= iplo && id <= iphi) ? 1u : 0u;
     }
+    add_runs(h, bin, cnt);
   }
 }
 
