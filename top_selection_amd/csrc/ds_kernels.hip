@@ -5,7 +5,9 @@
 // beating T to an on-chip candidate buffer, a radix-select compaction back to k entries
 // whenever the buffer reaches k + B2 (which also raises T to the smallest survivor), and a
 // final compaction. The split-row path (design note, "Implementation", cluster paragraph)
-// runs the same method on slices of a row and merges the slices' survivors with it again.
+// runs the same method on slices of a row and merges the slices' survivors: up to 8 slices
+// store sorted lists that a list-merge kernel places by rank, more slices go through the
+// method again.
 //
 // Order used everywhere: an element is the pair (value, index); larger value first,
 // +0 before -0, then smaller index first. On the device an element's value is replaced
@@ -18,19 +20,23 @@
 //    loads (1 KiB per wave per chunk). Each wave keeps D blocks in flight (D buffers of
 //    registers): block i+D is loaded into the registers of block i as soon as block i has
 //    been filtered, so loads stay in flight through the block barrier and any compaction.
-//    The block order is a table in LDS, computed once per workgroup;
+//    The random order is over groups of G consecutive blocks (a table in LDS, computed once
+//    per workgroup), so consecutive loads are in flight together;
+//  * the first whole block may set a presampled threshold (a lower bound of its k-th
+//    element, from the lanes' maxima) instead of accepting everything;
 //  * the filter compares raw bit patterns against a per-block integer threshold; hit masks
 //    are 64-lane SGPR masks, positions come from mbcnt, and one LDS atomic per wave and chunk
 //    reserves buffer space. Hits are stored raw; the compaction's first pass turns them
 //    into keys;
 //  * barriers are LDS-only (s_barrier with workgroup/local fences), so in-flight global
 //    loads are never drained by a barrier;
-//  * the compaction is an LDS radix select with 2048-bin histograms over an adaptive key
-//    window [T, previous maximum]: all waves count (survivors from the last thread down,
-//    appended entries from the first up), one wave scans the bins and publishes the pivot
-//    bin, and in the usual case one or two passes leave at most 64 pivot-bin entries, which
+//  * the compaction is an LDS radix select with 2048-bin histograms: the first pass bins
+//    values linearly over [T, previous maximum] (floats crowd into few key bins), later
+//    passes bin keys or indices. All waves count, one wave scans the bins and publishes the
+//    pivot bin, and in the usual case one pass leaves at most 64 pivot-bin entries, which
 //    one wave ranks with lane reads. Survivors alternate between two k-entry sets, so
-//    nothing is copied back; appends always go to the region after the survivor set A.
+//    nothing is copied back; appends always go to the region after the survivor set A. The
+//    final compaction can write its survivors sorted (a counting sort over its value bins).
 #include "ds_internal.h"
 
 namespace ds {
@@ -440,15 +446,20 @@ __device__ __forceinline__ void scan_select(const uint32_t* h, uint32_t need, ui
 // calls return the smallest survivor as the new threshold (tkey, tidx) and the largest key
 // seen in maxkey.
 //
-// Search: a kBins-bin histogram of (min(key, hi) - lo) >> shift over a key window [lo, hi]
-// that holds every entry locates the bin of the k-th best; while that bin holds more than
-// kListCap entries the window shrinks to it and the histogram repeats; a bin that is a single
-// key (ties) continues on the indices in [ilo, ihi] (smaller index = higher bin). Then the
-// entries above the pivot window are scattered to the destination, the window's entries are
-// gathered in a short list, and the list is ranked to place the rest and find the threshold.
-// The first window is the whole key space [0, key_hi]; later ones are [T.key, previous
-// maximum], with keys above the previous maximum counted in the top bin ("open" bin, refined
-// over [bin start, new maximum] when it is chosen).
+// Search: the first pass is a kBins-bin histogram of value bins (vbin) over the window
+// [value(vlo_key), value(vhi_key)] when vok and the window is usable; values above it count in
+// the top bin. If the pivot's value bin holds more than kListCap entries, its exact key
+// bounds are found by a search over keys and the search continues with key bins
+// (min(key, hi) - lo) >> shift over a key window [lo, hi]; while the pivot bin holds more
+// than kListCap entries the window shrinks to it and the histogram repeats; a bin that is a
+// single key (ties) continues on the indices in [ilo, ihi] (smaller index = higher bin).
+// Without value bins the first key window is [0, key_hi] or [T.key, previous maximum] with
+// keys above the maximum counted in the top ("open") bin. Then the entries above the pivot
+// are scattered to the destination, the pivot bin's entries are gathered in a short list, and
+// the list is ranked to place the rest and find the threshold.
+//
+// With so (final call only) and a single value pass, the survivors are written sorted to
+// *so instead (sorted = true): a counting sort over the value bins (see below).
 //
 // Barriers: two per histogram pass (after the counts; after the scan result is published),
 // one after the scatter and one after the list is ranked.
