@@ -70,7 +70,8 @@ extern "C" {
  *   order_group  G in {1, 2, 4}: the random order is drawn over groups of G consecutive
  *              blocks, which are read in turn (G = 1 is the design note's order of single
  *              blocks; larger G keeps consecutive loads in flight, measured faster on
- *              MI355X). Zero (auto) means 2. The result is the same for every G.
+ *              MI355X). Zero (auto) means 2 when a slice has at least 8 blocks, else 1.
+ *              The result is the same for every G.
  */
 #define DS_PRESAMPLE_AUTO 0
 #define DS_PRESAMPLE_OFF 1

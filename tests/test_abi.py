@@ -107,7 +107,8 @@ def test_presample_plan_field():
 
 
 def test_order_group_plan_field():
-    assert ts.ds_topk_plan(64, 131072, 512, ts.BF16, {"slices": 4})["order_group"] == 2
+    assert ts.ds_topk_plan(256, 129280, 512, ts.FP32, {"slices": 1})["order_group"] == 2  # 16 blocks
+    assert ts.ds_topk_plan(64, 131072, 512, ts.BF16, {"slices": 4})["order_group"] == 1  # 4 blocks
     assert ts.ds_topk_plan(64, 131072, 512, ts.BF16, {"slices": 4, "order_group": 1})["order_group"] == 1
     with pytest.raises(ts.DSError) as e:
         ts.ds_topk_plan(4, 32768, 512, ts.BF16, {"order_group": 3, "slices": 1})

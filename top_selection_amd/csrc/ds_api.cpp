@@ -173,7 +173,9 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   p.sort_cap = sort_cap;
   p.lds = lds;
   p.presample = c.presample != DS_PRESAMPLE_OFF && k <= 64 * kSelectShapes[shape].waves;
-  p.order_group = c.order_group ? c.order_group : 2;
+  // groups of two blocks pay off on long slices (consecutive loads in flight); short slices
+  // keep single blocks, which randomise adversarial (sorted) slices better
+  p.order_group = c.order_group ? c.order_group : ((slice_len + block - 1) / block >= 8 ? 2 : 1);
   if (slices > 1) {
     int ms = k > kMergeBlock ? k : kMergeBlock;
     if (ms + kMergeBlock < sort_cap) ms = sort_cap - kMergeBlock;
