@@ -1351,11 +1351,11 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   };
 
   // Threshold from the first (whole) block instead of "accept everything", from each lane's
-  // largest key lmax: each wave takes the j-th largest of its lanes' maxima, j = ceil(k /
-  // WAVES), found bit by bit over the key's top 16 bits (a truncation can only lower it); the
-  // smallest of the waves' values T0 has at least WAVES * j >= k distinct elements (one per
-  // lane) at or above it, so T0 does not exceed the k-th element and "key >= T0" keeps every
-  // element that can be in the top k.
+  // largest key lmax (over elements of the stream, each lane its own): each wave takes the
+  // j-th largest of its lanes' maxima, j = ceil(k / WAVES), found bit by bit over the key's
+  // top 16 bits (a truncation can only lower it); the smallest of the waves' values T0 has
+  // at least WAVES * j >= k distinct elements (one per lane) at or above it, so T0 does not
+  // exceed the k-th element and "key >= T0" keeps every element that can be in the top k.
   auto presample_from = [&](uint32_t lmax) {
     constexpr uint32_t KB = DT == DS_BF16 ? 16u : 32u;
     const uint32_t j = (k + WAVES - 1) / WAVES;
@@ -1420,11 +1420,30 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
         }
       }
       if (presample && i == 0 && blk_lo + B <= len) {
+        // each lane's maximum over its elements of this block and, on short streams (fewer
+        // than 8 blocks) when it is a whole block too, of the second block read (already in
+        // flight in buf[1]): a tighter T0 where the final compaction dominates; long streams
+        // do not wait for the second block (measured slower there)
         uint32_t lmax = 0;
 #pragma unroll
         for (uint32_t t = 0; t < CPW; ++t) {
 #pragma unroll
           for (uint32_t q = 0; q < VEC; ++q) lmax = max(lmax, key_of_score<DT>(s[t][q]));
+        }
+        if (m < 8 && bids[1] < m && bids[1] * B + B <= len) {
+#pragma unroll
+          for (uint32_t t = 0; t < CPW; ++t) {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+              const uint32_t w = buf[1][t][q];
+              if constexpr (DT == DS_BF16) {
+                lmax = max(lmax, key_of_score<DT>(w << 16));
+                lmax = max(lmax, key_of_score<DT>(w));
+              } else {
+                lmax = max(lmax, key_of_score<DT>(w));
+              }
+            }
+          }
         }
         presample_from(lmax);
         filter_thresholds<DT>(t_key, mode, thr_s, thr_n);
