@@ -72,10 +72,22 @@ extern "C" {
  *              blocks; larger G keeps consecutive loads in flight, measured faster on
  *              MI355X). Zero (auto) means 2 when a slice has at least 8 blocks, else 1.
  *              The result is the same for every G.
+ *   merge      the merge step of split rows (slices > 1). DS_MERGE_LISTS: every slice
+ *              writes its k survivors sorted, and the lists are merged in levels: each
+ *              level merges groups of up to 16 consecutive lists (as many as fit in 128 KiB
+ *              of LDS at 8 bytes an entry) into one sorted list of the group's k best, one
+ *              workgroup per list placing its entries by binary searches in the group's
+ *              other lists; the plan takes the fewest levels and the smallest equal group
+ *              sizes that reach one list. DS_MERGE_SELECT: one workgroup per row runs
+ *              DeepSelect again over the row's slices * k survivors. Zero (auto) means
+ *              LISTS. The plan reports the merge used (0 when slices == 1).
  */
 #define DS_PRESAMPLE_AUTO 0
 #define DS_PRESAMPLE_OFF 1
 #define DS_PRESAMPLE_ON 2
+#define DS_MERGE_AUTO 0
+#define DS_MERGE_LISTS 1
+#define DS_MERGE_SELECT 2
 
 typedef struct ds_config {
   int32_t block;
@@ -84,6 +96,7 @@ typedef struct ds_config {
   int32_t waves;
   int32_t presample;
   int32_t order_group;
+  int32_t merge;
 } ds_config;
 
 /*
@@ -159,9 +172,9 @@ int ds_topk_ex(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k
  * ds_topk_slices / ds_topk_merge -- ds_topk_ex as its two launches, for callers that
  * want to time or overlap them separately. ds_topk_slices runs the select kernel: with one
  * slice per row it writes the final outputs; otherwise it writes every slice's k survivors
- * to the workspace (sorted, for 2..8 slices whose lists fit in LDS) and ds_topk_merge
- * reduces each row's survivors to the sorted top-k (it enqueues nothing when the plan has
- * one slice). Both take the same arguments as
+ * to the workspace (sorted, for the list merge) and ds_topk_merge reduces each row's
+ * survivors to the sorted top-k (one launch per list-merge level, or one merge-kernel
+ * launch; nothing when the plan has one slice). Both take the same arguments as
  * ds_topk_ex (merge ignores x, row_stride and stats) and must be given the same rows, n, k,
  * dtype, seed, cfg and workspace; the pair then equals one ds_topk_ex call.
  */

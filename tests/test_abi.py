@@ -70,7 +70,64 @@ def test_forced_plans(dtype, n, k, slices):
     per = -(-n // slices)
     assert p["slices"] == -(-n // (-(-per // p["block"]) * p["block"]))
     ws = ts.ds_topk_workspace_size(8, n, k, dtype, {"slices": slices})
-    assert ws == (0 if slices == 1 else 8 * ((slices * k + 1) // 2 * 2) * 8)
+    assert ws == _list_merge_ws(8, slices, k)
+    assert p["merge"] == (0 if slices == 1 else ts.MERGE_LISTS)
+    sel = ts.ds_topk_workspace_size(8, n, k, dtype, {"slices": slices, "merge": ts.MERGE_SELECT})
+    assert sel == (0 if slices == 1 else 8 * ((slices * k + 1) // 2 * 2) * 8)
+
+
+def _even(v):
+    return (v + 1) // 2 * 2
+
+
+def _merge_levels(slices, k):
+    """Group sizes of the list merge's levels, from the rule the header states: at most 16
+    lists and 128 KiB of 8-byte entries per group, the fewest levels, then per level the
+    smallest group size that still reaches one list in the levels left."""
+    gmax = min(16, (128 * 1024) // 8 // k)
+    levels, reach = 0, 1
+    while reach < slices:
+        reach *= gmax
+        levels += 1
+    groups, lists = [], slices
+    for lv in range(levels):
+        g = 2
+        while g ** (levels - lv) < lists:
+            g += 1
+        groups.append(g)
+        lists = -(-lists // g)
+    assert lists == 1 or slices == 1
+    return groups
+
+
+def _list_merge_ws(rows, slices, k):
+    if slices == 1:
+        return 0
+    groups = _merge_levels(slices, k)
+    ws = rows * _even(slices * k) * 8
+    if len(groups) > 1:
+        ws += rows * _even(-(-slices // groups[0]) * k) * 8
+    return ws
+
+
+def test_merge_levels_rule():
+    assert _merge_levels(4, 512) == [4]
+    assert _merge_levels(16, 512) == [16]
+    assert _merge_levels(32, 512) == [6, 6]
+    assert _merge_levels(33, 512) == [6, 6]
+    assert _merge_levels(32, 4096) == [4, 3, 3]  # 32 -> 8 -> 3 -> 1
+    assert _merge_levels(256, 32) == [16, 16]
+    assert _merge_levels(512, 32) == [8, 8, 8]
+
+
+def test_merge_plan_field():
+    assert ts.ds_topk_plan(8, 1 << 20, 512, ts.BF16, {"slices": 32})["merge"] == ts.MERGE_LISTS
+    assert ts.ds_topk_plan(8, 1 << 20, 512, ts.BF16, {"slices": 32, "merge": ts.MERGE_SELECT})["merge"] == \
+        ts.MERGE_SELECT
+    assert ts.ds_topk_plan(8, 1 << 20, 512, ts.BF16, {"slices": 1, "merge": ts.MERGE_SELECT})["merge"] == 0
+    with pytest.raises(ts.DSError) as e:
+        ts.ds_topk_plan(4, 32768, 512, ts.BF16, {"merge": 3, "slices": 2})
+    assert e.value.status == ts.DS_ERR_INVALID_ARG
 
 
 def test_forced_block_sizes():

@@ -154,7 +154,7 @@ def test_counters_match_model(dtype, n, k, block, slack, slices):
 def test_split_rows_reuse_and_graph_replays(dtype):
     """Split rows (sorted slice lists merged by the list-merge kernel): repeated calls on one
     workspace, replays of a captured graph with eager work in between, and other plans on the
-    same workspace (including the merge kernel for many slices) all give the oracle's result;
+    same workspace (the merge kernel, a two-level list merge) all give the oracle's result;
     the workspace's contents on entry never matter."""
     import torch
     from gpu_util import to_device, to_numpy_vals
@@ -194,7 +194,9 @@ def test_split_rows_reuse_and_graph_replays(dtype):
         check(f"replay#{rep}")
     for label, xo, ko, co in [("other-lists", gen.rows_family("ties", dtype, 32, 3, 40000), 100, {"slices": 2}),
                               ("merge-kernel", gen.rows_family("normal", dtype, 33, 2, 16384), 64,
-                               {"block": 1024, "slices": 16})]:
+                               {"block": 1024, "slices": 16, "merge": ts.MERGE_SELECT}),
+                              ("list-levels", gen.rows_family("normal", dtype, 34, 2, 40 * 1024 - 500), 16,
+                               {"block": 1024, "slices": 40})]:
         say(f"[gpu] split rows workspace reuse: {label}")
         assert ts.ds_topk_workspace_size(xo.shape[0], xo.shape[1], ko, dtype, co) <= wsb
         gv, gi = ts.ds_topk_ex(to_device(xo), ko, seed=3, workspace=ws, cfg=co)
@@ -240,3 +242,39 @@ def test_order_groups(dtype, group):
             cfg = {"slices": 1, "block": 8192, "order_group": group}
             assert ts.ds_topk_plan(rows, n, k, dtype, cfg)["order_group"] == group
             _check(x, k, f"group={group} n={n} {fam}", seed=9, cfg=cfg)
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+@pytest.mark.parametrize("family,rows,n,k,slices,block", [
+    ("normal", 3, 40 * 1024 - 500, 64, 40, 1024),    # two levels (7, 6); the last group has 5 lists
+    ("ties", 3, 40 * 1024 - 500, 64, 40, 1024),
+    ("normal", 2, 43 * 1024 - 1000, 512, 43, 1024),  # last slice 24 < k elements, alone in its group
+    ("ascending", 2, 43 * 1024 - 1000, 512, 43, 1024),
+    ("normal", 2, 40 * 1024 - 5, 1, 40, 1024),       # k = 1
+    ("normal", 2, 200000, 4096, 5, 0),               # k = 4096: two levels (3, 2)
+    ("ties", 2, 200000, 4096, 5, 0),
+    ("normal", 4, 32 * 8192 - 1000, 300, 32, 0),     # two levels (6, 6)
+    ("normal", 4, 16 * 8192 - 1000, 300, 16, 0),     # one level of 16 lists
+])
+def test_list_merge_levels(dtype, family, rows, n, k, slices, block):
+    """The list merge's levels (groups, a ragged last group, short padded lists, k = 1 and
+    4096) and the merge kernel on the same split give the oracle's result."""
+    x = gen.rows_family(family, dtype, 51, rows, n)
+    base = {"slices": slices}
+    if block:
+        base["block"] = block
+    for merge in (ts.MERGE_LISTS, ts.MERGE_SELECT):
+        cfg = dict(base, merge=merge)
+        assert ts.ds_topk_plan(rows, n, k, dtype, cfg)["merge"] == merge
+        _check(x, k, f"{family} merge={merge}", seed=5, cfg=cfg)
+
+
+def test_list_merge_values_only_many_slices():
+    """A values-only giant row cut into 256 slices of two blocks: two list-merge levels with
+    sixteen lists per workgroup (k = 32)."""
+    x = gen.WORKLOADS["c5_giant"].make(n=1 << 22)
+    cfg = {"slices": 256}
+    plan = ts.ds_topk_plan(1, 1 << 22, 32, gen.FP32, cfg)
+    assert plan["merge"] == ts.MERGE_LISTS and plan["block"] == 8192
+    _check(x, 32, "values-only 256 slices", cfg=cfg, indices=False)
+    _check(x, 32, "values+indices 256 slices", cfg=cfg)

@@ -21,6 +21,7 @@ constexpr int kDefaultSlacks[] = {4096, 2048};  // B2 when not forced (at least 
 constexpr int kDefaultFp32[] = {8, 7, 2, 1};  // 16x2 (B=8192), 16x1 (4096), 4x2 (2048), 4x1 (1024)
 constexpr int kDefaultBf16[] = {7, 3, 1, 0};  // 16x1 (B=8192), 8x1 (4096), 4x1 (2048), 2x1 (1024)
 constexpr int kNumDefaults = 4;
+constexpr int kMaxMergeLevels = 8;  // 16 slices per level at k <= 1024, 4 at k = 4096
 
 int elem_bytes(int dtype) { return dtype == DS_BF16 ? 2 : 4; }
 int chunk_elems(int dtype) { return dtype == DS_BF16 ? kChunkBf16 : kChunkFp32; }
@@ -42,10 +43,15 @@ struct Plan {
   size_t lds;
   bool presample;   // the first whole block sets a presampled threshold
   int order_group;  // G: the random order is over groups of G consecutive blocks
-  // merge (slices > 1): the list-merge kernel over sorted slice lists, or the merge kernel
-  bool list_merge;
+  // merge (slices > 1): DS_MERGE_LISTS (levels of the list-merge kernel over sorted slice
+  // lists, group[l] lists merged together at level l) or DS_MERGE_SELECT (the merge kernel)
+  int merge;
+  int levels;
+  int group[kMaxMergeLevels];
   int mslack;
   size_t mlds;
+  int64_t ws_row_a;  // workspace row stride (entries) of the slice lists
+  int64_t ws_row_b;  // and of the first list-merge level's output (after all rows of the former)
   size_t ws_bytes;
 };
 
@@ -76,12 +82,13 @@ int check_basic(int64_t rows, int64_t n, int k, int dtype) {
 int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK) return st;
-  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0};
+  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0};
   if (c.block < 0 || c.slack < 0 || c.slices < 0 || c.waves < 0) return DS_ERR_INVALID_ARG;
   if (c.presample != DS_PRESAMPLE_AUTO && c.presample != DS_PRESAMPLE_OFF && c.presample != DS_PRESAMPLE_ON)
     return DS_ERR_INVALID_ARG;
   if (c.order_group != 0 && c.order_group != 1 && c.order_group != 2 && c.order_group != 4)
     return DS_ERR_INVALID_ARG;
+  if (c.merge != DS_MERGE_AUTO && c.merge != DS_MERGE_LISTS && c.merge != DS_MERGE_SELECT) return DS_ERR_INVALID_ARG;
   const int chunk = chunk_elems(dtype);
   const int eb = elem_bytes(dtype);
 
@@ -177,17 +184,41 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   // keep single blocks, which randomise adversarial (sorted) slices better
   p.order_group = c.order_group ? c.order_group : ((slice_len + block - 1) / block >= 8 ? 2 : 1);
   if (slices > 1) {
-    int ms = k > kMergeBlock ? k : kMergeBlock;
-    if (ms + kMergeBlock < sort_cap) ms = sort_cap - kMergeBlock;
-    p.mslack = ms;
-    p.mlds = ds::select_lds_bytes(k, kMergeBlock, ms, ds::kMergeShape.waves);
-    if (static_cast<int64_t>(p.mlds) > kMaxLdsBytes) return DS_ERR_UNSUPPORTED;
     const int64_t entries = slices * static_cast<int64_t>(k);
     if (entries * 8 > kMaxSliceBytes) return DS_ERR_UNSUPPORTED;
-    // the list merge holds a row's lists in LDS (as much as the select kernel's dynamic LDS)
-    p.list_merge = slices <= ds::kMaxListSlices &&
-                   static_cast<size_t>(entries) * 8 <= lds - ds::select_scalars_bytes();
-    p.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>((entries + 1) & ~int64_t(1)) * 8;
+    p.ws_row_a = (entries + 1) & ~int64_t(1);
+    p.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>(p.ws_row_a) * 8;
+    p.merge = c.merge ? c.merge : DS_MERGE_LISTS;
+    if (p.merge == DS_MERGE_LISTS) {
+      // the fewest levels of at most gmax lists each, then the smallest group size per level
+      // that still reaches one list in the levels left
+      const int64_t gmax = std::min<int64_t>(ds::kMaxListGroup, ds::kListMergeLds / 8 / k);
+      int levels = 0;
+      for (int64_t reach = 1; reach < slices; reach *= gmax) ++levels;
+      if (levels > kMaxMergeLevels) return DS_ERR_UNSUPPORTED;
+      int64_t lists = slices;
+      for (int l = 0; l < levels; ++l) {
+        int64_t g = 2;
+        for (;; ++g) {
+          int64_t reach = 1;
+          for (int e = l; e < levels; ++e) reach *= g;
+          if (reach >= lists) break;
+        }
+        p.group[l] = static_cast<int>(g);
+        lists = (lists + g - 1) / g;
+        if (l == 0 && levels > 1) {
+          p.ws_row_b = (lists * k + 1) & ~int64_t(1);
+          p.ws_bytes += static_cast<size_t>(rows) * static_cast<size_t>(p.ws_row_b) * 8;
+        }
+      }
+      p.levels = levels;
+    } else {
+      int ms = k > kMergeBlock ? k : kMergeBlock;
+      if (ms + kMergeBlock < sort_cap) ms = sort_cap - kMergeBlock;
+      p.mslack = ms;
+      p.mlds = ds::select_lds_bytes(k, kMergeBlock, ms, ds::kMergeShape.waves);
+      if (static_cast<int64_t>(p.mlds) > kMaxLdsBytes) return DS_ERR_UNSUPPORTED;
+    }
   }
   *out = p;
   return DS_OK;
@@ -220,11 +251,11 @@ int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t r
   sp.sort_cap = pl.sort_cap;
   sp.seed = seed;
   sp.ws = static_cast<uint2*>(ws);
-  sp.ws_row_entries = (static_cast<int64_t>(pl.slices) * k + 1) & ~int64_t(1);
+  sp.ws_row_entries = pl.ws_row_a;
   sp.out_vals = out_vals;
   sp.out_idx = out_idx;
   sp.stats = stats;
-  sp.sorted_lists = pl.list_merge ? 1 : 0;
+  sp.sorted_lists = pl.merge == DS_MERGE_LISTS ? 1 : 0;
   sp.presample = pl.presample ? 1 : 0;
   sp.group_shift = pl.order_group == 4 ? 2 : (pl.order_group == 2 ? 1 : 0);
   return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
@@ -246,8 +277,26 @@ int run_merge(const Plan& pl, int64_t rows, int64_t n, int k, uint64_t seed, voi
   mp.out_vals = out_vals;
   mp.out_idx = out_idx;
   mp.presample = pl.presample && k <= 64 * ds::kMergeShape.waves ? 1 : 0;
-  if (pl.list_merge) return ds::launch_merge_lists(pl.dtype, mp, rows, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
-  return ds::launch_merge(pl.dtype, mp, rows, pl.mlds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
+  if (pl.merge == DS_MERGE_SELECT)
+    return ds::launch_merge(pl.dtype, mp, rows, pl.mlds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
+  // list merge: level l reads one workspace region and writes the other (or the outputs)
+  uint2* const region[2] = {static_cast<uint2*>(ws), static_cast<uint2*>(ws) + rows * pl.ws_row_a};
+  const int64_t row_of[2] = {pl.ws_row_a, pl.ws_row_b};
+  int64_t lists = pl.slices;
+  for (int l = 0; l < pl.levels; ++l) {
+    const int g = pl.group[l];
+    const bool last = l + 1 == pl.levels;
+    mp.ws = region[l & 1];
+    mp.row_entries = row_of[l & 1];
+    mp.dst = last ? nullptr : region[(l + 1) & 1];
+    mp.dst_row_entries = last ? 0 : row_of[(l + 1) & 1];
+    mp.lists = static_cast<int32_t>(lists);
+    mp.group = g;
+    mp.per_wg = std::max(1, std::min(g, ds::kListMergeWaves * 64 / k));
+    if (ds::launch_merge_lists(pl.dtype, mp, rows, stream) != hipSuccess) return DS_ERR_LAUNCH;
+    lists = (lists + g - 1) / g;
+  }
+  return DS_OK;
 }
 
 int run(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, uint64_t seed,
@@ -330,6 +379,7 @@ int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg
   out->waves = kSelectShapes[p.shape].waves;
   out->presample = p.presample ? DS_PRESAMPLE_ON : DS_PRESAMPLE_OFF;
   out->order_group = p.order_group;
+  out->merge = p.slices > 1 ? p.merge : DS_MERGE_AUTO;
   return DS_OK;
 }
 

@@ -32,11 +32,16 @@ struct SelectParams {
   int32_t group_shift;       // log2 of G: the block order is random over groups of G blocks
 };
 
-// One workgroup per row runs DeepSelect over the row's slices*k survivors.
+// The merge of split rows. The merge kernel: one workgroup per row runs DeepSelect over the
+// row's slices*k survivors (ws, entries, row_entries, slack, seed, presample). One level of
+// the list merge: the row's `lists` sorted lists of k entries at ws are merged in groups of
+// `group` consecutive lists; group g's k best go to dst (row r at dst + r*dst_row_entries,
+// group g at +g*k) as sorted pairs, or to the outputs when dst is NULL (the level has one
+// group). Each list-merge workgroup places per_wg lists of one group.
 struct MergeParams {
   const uint2* ws;     // row r's entries at ws + r*row_entries
   int64_t entries;     // slices * k
-  int64_t row_entries; // entries rounded up to even
+  int64_t row_entries; // entries rounded up to even (16-byte rows)
   int64_t n;           // row length (indices lie in [0, n))
   int32_t k;
   int32_t slack;
@@ -45,6 +50,13 @@ struct MergeParams {
   void* out_vals;
   int32_t* out_idx;
   int32_t presample;   // nonzero: the first whole block sets a presampled threshold
+  uint2* dst;
+  int64_t dst_row_entries;
+  int32_t lists;
+  int32_t group;
+  int32_t per_wg;
+  int32_t pk;    // ceil(k / group), set by the launcher
+  int64_t row0;  // first row of a launch, set by the launcher
 };
 
 // A compiled kernel shape: waves per workgroup and 16-byte chunks per wave per block.
@@ -64,15 +76,17 @@ constexpr Shape kMergeShape = {16, 2};  // 16 waves x 2 chunks x 128 entries = 4
 size_t select_lds_bytes(int k, int block, int slack, int waves);
 size_t select_scalars_bytes();
 
-// Split rows with at most this many slices store sorted slice lists, which the list-merge
-// kernel merges; more slices use the merge kernel (DeepSelect over the survivors).
-constexpr uint32_t kMaxListSlices = 8;
+// The list merge merges at most this many sorted lists together (one level), whose entries
+// take at most kListMergeLds bytes of LDS, with kListMergeWaves waves per workgroup.
+constexpr uint32_t kMaxListGroup = 16;
+constexpr int64_t kListMergeLds = 128 * 1024;
+constexpr int kListMergeWaves = 8;
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,
                          hipStream_t stream);
 hipError_t launch_merge(int dtype, const MergeParams& p, int64_t rows, size_t lds_bytes, hipStream_t stream);
-// One workgroup per row merges the row's p.entries / p.k sorted slice lists.
+// One level of the list merge (p.lists, p.group, p.per_wg, p.dst).
 hipError_t launch_merge_lists(int dtype, const MergeParams& p, int64_t rows, hipStream_t stream);
 hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 int64_t probe_read_groups(int64_t bytes);

@@ -37,6 +37,8 @@
 //    one wave ranks with lane reads. Survivors alternate between two k-entry sets, so
 //    nothing is copied back; appends always go to the region after the survivor set A. The
 //    final compaction can write its survivors sorted (a counting sort over its value bins).
+#include <type_traits>
+
 #include "ds_internal.h"
 
 namespace ds {
@@ -1153,62 +1155,110 @@ __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_
 
 // --------------------------------------------------------------------------- slice merge
 
-// Merge of a row's S sorted slice lists (S <= kMaxListSlices, k entries each, best first,
-// as (key, index) pairs at src[s * k + i]) into the row's k best, sorted, written to the
-// outputs. The lists are loaded into LDS (lds: S * k 64-bit words) as composites; an entry's
-// place in the merged order is its position in its own list plus, for every other list, the
-// number of that list's entries that rank above it (binary searches, all lists searched in
-// the same step with clamped, always valid indices; equal entries of earlier lists count as
-// above). Padding ranks below every element and is never placed.
+// Merge of S sorted lists (S <= MAXS <= kMaxListGroup, k entries each, best first, as (key, index)
+// pairs at src[s * k + i]) into their k best, sorted: written to the outputs at at0 + rank,
+// or, with pairs, as pairs at pairs[rank]. The lists are loaded into LDS (lds: S * k 64-bit
+// words, then S 32-bit prefix lengths) as composites; an entry's place in the merged order is its position in its own
+// list plus, for every other list, the number of that list's entries that rank above it
+// (binary searches, all lists searched in the same step with clamped, always valid indices;
+// equal entries of earlier lists count as above). Padding (composite 0) ranks below every
+// element; it is placed only when the lists hold fewer than k elements together, as padding.
 // Places the entries of lists [l0, l1) (all lists are loaded and searched).
 template <int DT, int WAVES, uint32_t MAXS>
-__device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint32_t k, uint64_t* lds,
-                                              void* out_vals, int32_t* out_idx, uint64_t row, uint32_t l0,
-                                              uint32_t l1) {
+__device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint32_t k, uint32_t pk, uint64_t* lds,
+                                              void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t at0,
+                                              uint32_t l0, uint32_t l1) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x, total = S * k;
   __attribute__((address_space(3))) uint64_t* lw = lds_ptr(lds);
-  for (uint32_t e = tid; e < total; e += NT) {
-    const uint2 v = src[e];
-    lw[e] = comp_of(v.x, v.y);
-  }
+  // fill: LU 16-byte loads (two entries each) in flight per thread before their LDS writes
+  // (a plain loop waits for each load in turn); buffer loads past the lists read zeros
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint2*>(src), 0, static_cast<int>(total * 8u), kRsrcWord3);
+  const uint32_t npair = (total + 1u) / 2u;
+  auto fill = [&](auto lu) {
+    constexpr uint32_t LU = decltype(lu)::value;
+    for (uint32_t p0 = tid; p0 < npair; p0 += LU * NT) {
+      u32x4 v[LU];
+#pragma unroll
+      for (uint32_t u = 0; u < LU; ++u) v[u] = load16(rs, (p0 + u * NT) * 16u);
+#pragma unroll
+      for (uint32_t u = 0; u < LU; ++u) {
+        const uint32_t e = 2u * (p0 + u * NT);
+        if (e < total) lw[e] = comp_of(v[u][0], v[u][1]);
+        if (e + 1u < total) lw[e + 1u] = comp_of(v[u][2], v[u][3]);
+      }
+    }
+  };
+  if (npair <= 2u * NT)
+    fill(std::integral_constant<uint32_t, 2>{});  // short lists: no loads wasted past the end
+  else
+    fill(std::integral_constant<uint32_t, 8>{});
   lds_sync();
+  // Entries below T cannot reach the first k places, so they are not searched: one list's
+  // k-th entry has k entries (its list's first k) at or above it, and each of the S lists
+  // has ceil(k/S) entries at or above the smallest of the lists' ceil(k/S)-th entries; T is
+  // the larger of the two bounds (broadcast LDS reads, the same in every thread).
+  uint64_t ta = 0, tb = ~0ull;
+#pragma unroll
+  for (uint32_t q = 0; q < MAXS; ++q) {
+    const uint32_t qq = min(q, S - 1u);
+    const uint64_t a = lw[qq * k + k - 1u], b = lw[qq * k + pk - 1u];
+    ta = a > ta ? a : ta;
+    tb = b < tb ? b : tb;
+  }
+  const uint64_t T = ta > tb ? ta : tb;
   const uint32_t top = 1u << (31u - static_cast<uint32_t>(__builtin_clz(k)));  // largest power of two <= k
+  // nq[q]: the length of list q's prefix at or above T. Entries that rank above an entry at
+  // or above T are themselves above T, so each search stays inside that prefix, and lists
+  // with an empty prefix are not searched. Found for groups of 8 or more lists (for fewer,
+  // the extra search and barrier cost more than they save).
+  uint32_t nq[MAXS], top_n = top;
+  if constexpr (MAXS >= 8) {
+    __attribute__((address_space(3))) uint32_t* nql = lds_ptr(reinterpret_cast<uint32_t*>(lds + S * k));
+    if (tid < S) {
+      uint32_t n = 0;
+      for (uint32_t step = top; step > 0; step >>= 1)
+        n = (n + step <= k && lw[tid * k + n + step - 1u] >= T) ? n + step : n;
+      nql[tid] = n;
+    }
+    lds_sync();
+    uint32_t maxn = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < MAXS; ++q) {
+      nq[q] = q < S ? nql[q] : 0u;
+      maxn = max(maxn, nq[q]);
+    }
+    top_n = maxn ? 1u << (31u - static_cast<uint32_t>(__builtin_clz(maxn))) : 0u;
+  } else {
+#pragma unroll
+    for (uint32_t q = 0; q < MAXS; ++q) nq[q] = q < S ? k : 0u;
+  }
   for (uint32_t e = l0 * k + tid; e < l1 * k; e += NT) {
     uint32_t s = 0;
 #pragma unroll
     for (uint32_t q = 1; q < MAXS; ++q) s += (q < S && e >= q * k) ? 1u : 0u;
     const uint64_t c = lw[e];
+    if (c < T) continue;
     uint32_t pos[MAXS];
 #pragma unroll
     for (uint32_t q = 0; q < MAXS; ++q) pos[q] = 0;
-    for (uint32_t step = top; step > 0; step >>= 1) {
+    for (uint32_t step = top_n; step > 0; step >>= 1) {
       uint64_t x[MAXS];
 #pragma unroll
-      for (uint32_t q = 0; q < MAXS; ++q) x[q] = lw[min(q, S - 1u) * k + min(pos[q] + step, k) - 1u];
+      for (uint32_t q = 0; q < MAXS; ++q)  // always a valid address; empty prefixes never move pos
+        x[q] = lw[min(q, S - 1u) * k + min(pos[q] + step, max(nq[q], 1u)) - 1u];
 #pragma unroll
       for (uint32_t q = 0; q < MAXS; ++q) {
         const bool above = x[q] > c || (q < s && x[q] == c);
-        pos[q] = (pos[q] + step <= k && above) ? pos[q] + step : pos[q];
+        pos[q] = (pos[q] + step <= nq[q] && above) ? pos[q] + step : pos[q];
       }
     }
     uint32_t rank = e - s * k;
 #pragma unroll
     for (uint32_t q = 0; q < MAXS; ++q) rank += (q < S && q != s) ? pos[q] : 0u;
-    if (rank < k) store_out<DT>(out_vals, out_idx, nullptr, row * k + rank, c);
+    if (rank < k) store_out<DT>(out_vals, out_idx, pairs, at0 + rank, c);
   }
-}
-
-template <int DT, int WAVES>
-__device__ __forceinline__ void merge_sorted_lists(const uint2* src, uint32_t S, uint32_t k, uint64_t* lds,
-                                                   void* out_vals, int32_t* out_idx, uint64_t row, uint32_t l0,
-                                                   uint32_t l1) {
-  if (S <= 2)
-    merge_lists_t<DT, WAVES, 2>(src, S, k, lds, out_vals, out_idx, row, l0, l1);
-  else if (S <= 4)
-    merge_lists_t<DT, WAVES, 4>(src, S, k, lds, out_vals, out_idx, row, l0, l1);
-  else
-    merge_lists_t<DT, WAVES, kMaxListSlices>(src, S, k, lds, out_vals, out_idx, row, l0, l1);
 }
 
 // Integer compare values for the streaming filter, from the threshold pair (key, idx).
@@ -1798,16 +1848,27 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
 }
 
 // --------------------------------------------------------------------------- list-merge kernel
-// One workgroup per (row, slice list) places that list's entries among the row's sorted slice
-// lists (at most kMaxListSlices).
-template <int DT, int WAVES>
+// One level of the list merge: a row's p.lists sorted lists are merged in groups of p.group
+// consecutive lists, each group into one sorted list of its k best (at p.dst, or the outputs
+// when the level has one group). Each workgroup places p.per_wg lists of one group; the
+// grid is rows x groups x ceil(group / per_wg), and workgroups past a short last group's
+// lists return at once.
+template <int DT, int WAVES, uint32_t MAXS>
 __global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(MergeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  const uint32_t S = static_cast<uint32_t>(p.entries / p.k);
-  const uint32_t row = blockIdx.x / S, list = blockIdx.x % S;
-  const uint32_t k = static_cast<uint32_t>(p.k);
-  merge_sorted_lists<DT, WAVES>(p.ws + static_cast<uint64_t>(row) * p.row_entries, S, k,
-                                reinterpret_cast<uint64_t*>(lds), p.out_vals, p.out_idx, row, list, list + 1u);
+  const uint32_t S = static_cast<uint32_t>(p.lists), G = static_cast<uint32_t>(p.group);
+  const uint32_t per = static_cast<uint32_t>(p.per_wg), k = static_cast<uint32_t>(p.k);
+  // grid: (workgroups per group, groups, rows of this launch)
+  const uint64_t row = static_cast<uint64_t>(p.row0) + blockIdx.z;
+  const uint32_t g = blockIdx.y, l0 = blockIdx.x * per;
+  const uint32_t first = g * G, gl = min(G, S - first);  // the group's lists
+  if (l0 >= gl) return;  // the same for the whole workgroup
+  const uint32_t pk = gl == G ? static_cast<uint32_t>(p.pk) : (k + gl - 1u) / gl;  // ceil(k / gl)
+  const uint2* src = p.ws + row * p.row_entries + static_cast<uint64_t>(first) * k;
+  uint2* pairs = p.dst ? p.dst + row * p.dst_row_entries + static_cast<uint64_t>(g) * k : nullptr;
+  const uint64_t at0 = p.dst ? 0u : row * k;
+  merge_lists_t<DT, WAVES, MAXS>(src, gl, k, pk, reinterpret_cast<uint64_t*>(lds), p.out_vals, p.out_idx, pairs, at0,
+                                 l0, min(l0 + per, gl));
 }
 
 // --------------------------------------------------------------------------- probes
@@ -1886,17 +1947,40 @@ hipError_t launch_select_dt(int shape, const SelectParams& p, int64_t rows, size
   }
 }
 
-template <int DT>
-hipError_t launch_merge_lists_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
-  auto kern = merge_lists_kernel<DT, 8>;
+// Rows per list-merge launch (the grid's z dimension).
+constexpr int64_t kMaxGridRows = 65535;
+
+// One instantiation per bound on the lists merged together.
+template <int DT, uint32_t MAXS>
+hipError_t launch_merge_lists_t(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
+  auto kern = merge_lists_kernel<DT, kListMergeWaves, MAXS>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  const int64_t S = p.entries / p.k;
-  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(rows * S)), dim3(8 * 64), lds, stream, p);
-  return hipGetLastError();
+  const int64_t G = p.group, wpg = (G + p.per_wg - 1) / p.per_wg, groups = (p.lists + G - 1) / G;
+  MergeParams q = p;
+  q.pk = (p.k + p.group - 1) / p.group;
+  for (int64_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
+    q.row0 = r0;
+    const int64_t nr = rows - r0 < kMaxGridRows ? rows - r0 : kMaxGridRows;
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(wpg), static_cast<uint32_t>(groups), static_cast<uint32_t>(nr)),
+                       dim3(kListMergeWaves * 64), lds, stream, q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int DT>
+hipError_t launch_merge_lists_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
+  const int32_t g = p.group < p.lists ? p.group : p.lists;
+  if (g <= 2) return launch_merge_lists_t<DT, 2>(p, rows, lds, stream);
+  if (g <= 4) return launch_merge_lists_t<DT, 4>(p, rows, lds, stream);
+  if (g <= 8) return launch_merge_lists_t<DT, 8>(p, rows, lds, stream);
+  static_assert(kMaxListGroup == 16, "instantiations cover groups up to kMaxListGroup");
+  return launch_merge_lists_t<DT, kMaxListGroup>(p, rows, lds, stream);
 }
 
 template <int DT>
@@ -1930,7 +2014,8 @@ hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int6
 }
 
 hipError_t launch_merge_lists(int dtype, const MergeParams& p, int64_t rows, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(p.entries) * 8;
+  const size_t lds =
+      static_cast<size_t>(p.group < p.lists ? p.group : p.lists) * static_cast<size_t>(p.k) * 8 + kMaxListGroup * 4;
   return dtype == DS_BF16 ? launch_merge_lists_dt<DS_BF16>(p, rows, lds, stream)
                           : launch_merge_lists_dt<DS_FP32>(p, rows, lds, stream);
 }
