@@ -5,9 +5,9 @@
 // beating T to an on-chip candidate buffer, a radix-select compaction back to k entries
 // whenever the buffer reaches k + B2 (which also raises T to the smallest survivor), and a
 // final compaction. The split-row path (design note, "Implementation", cluster paragraph)
-// runs the same method on slices of a row and merges the slices' survivors: up to 8 slices
-// store sorted lists that a list-merge kernel places by rank, more slices go through the
-// method again.
+// runs the same method on slices of a row and merges the slices' survivors: each slice
+// stores a sorted list, and a list-merge kernel places entries by rank, in levels of up to
+// 16 lists (or, when asked, the method runs again over all survivors).
 //
 // Order used everywhere: an element is the pair (value, index); larger value first,
 // +0 before -0, then smaller index first. On the device an element's value is replaced
