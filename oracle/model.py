@@ -32,6 +32,22 @@ here from its specification:
   round (L, R) -> (R, L ^ (lowbias32(R ^ key_r) & mask)), four rounds, value (L<<half)|R
   pi(i) = first value < m on the cycle i -> F(i) -> F(F(i)) ... (cycle walking); m = 1 -> 0.
 
+Two switchable departures of the GPU kernels from the design note are modelled too (both
+leave the result unchanged, only the counts):
+
+* grouped order: the Feistel bijection is drawn over ceil(m/G) groups of G consecutive
+  blocks, and the blocks of a group are read in turn (positions past the last block are
+  skipped);
+* presampled start: instead of "accept everything", the first block read, when it is
+  whole, sets T0 = the smallest over the workgroup's waves of each wave's j-th largest
+  lane maximum (j = ceil(k / waves)), with the low (key bits - 16) key bits cleared; every
+  element with key >= T0 is appended until the first compaction. A lane's maximum is over
+  its elements of that block (lane l of wave w holds, in every 16-byte chunk c of the block
+  with c mod waves = w, the elements at l*vec .. l*vec+vec-1; vec = 16 / element bytes),
+  and also over the second block read when the slice has fewer than 8 blocks and that
+  block is whole. Keys are the order-preserving unsigned images of the raw bits: sign bit
+  clear -> set the sign bit, sign bit set -> invert every bit.
+
 Slices (the split-row path): slice s of a row covers [s*Ls, min((s+1)*Ls, N)) for a slice
 length Ls that is a multiple of B; each slice runs the method on its own elements with its
 own block order (row, slice) and keeps its k best (or all, if fewer); the row's answer is
@@ -140,6 +156,51 @@ def block_order(family: str, m: int, seed: int = 0, row: int = 0, slice_: int = 
     raise ValueError(f"unknown block order family {family!r}")
 
 
+def grouped_order(m: int, group: int, seed: int, row: int = 0, slice_: int = 0) -> np.ndarray:
+    """Blocks in processing order when the random order is over groups of `group`
+    consecutive blocks: group g = feistel(i) contributes blocks g*group .. g*group+group-1."""
+    if group == 1:
+        return feistel_order(m, seed, row, slice_)
+    groups = feistel_order(-(-m // group), seed, row, slice_)
+    out = [int(g) * group + j for g in groups for j in range(group) if int(g) * group + j < m]
+    return np.asarray(out, np.int64)
+
+
+# ----------------------------------------------------------------------------- keys, presample
+def keys_of(row: np.ndarray) -> np.ndarray:
+    """Order-preserving unsigned keys of a row given as bf16 bits (uint16) or float32."""
+    if row.dtype == np.uint16:
+        b, sign, mask = row.astype(np.uint64), 0x8000, 0xFFFF
+    elif row.dtype == np.float32:
+        b, sign, mask = row.view(np.uint32).astype(np.uint64), 0x80000000, 0xFFFFFFFF
+    else:
+        raise ValueError("row must be uint16 (bf16 bits) or float32")
+    neg = (b & np.uint64(sign)) != 0
+    return np.where(neg, (~b) & np.uint64(mask), b | np.uint64(sign)).astype(np.uint64)
+
+
+@dataclasses.dataclass(frozen=True)
+class Presample:
+    """The kernel shape the presampled start depends on."""
+    waves: int
+    vec: int       # elements per lane per 16-byte chunk (8 bf16, 4 fp32)
+    key_bits: int  # 16 (bf16) or 32 (fp32)
+
+
+def presample_key(block_keys: List[np.ndarray], k: int, ps: Presample) -> int:
+    """T0 from whole blocks' keys (each array one block, in element order)."""
+    chunk = 64 * ps.vec
+    lane_max = np.zeros((ps.waves, 64), np.uint64)
+    for kb in block_keys:
+        o = np.arange(kb.size)
+        np.maximum.at(lane_max, ((o // chunk) % ps.waves, (o % chunk) // ps.vec), kb)
+    j = -(-k // ps.waves)
+    assert 1 <= j <= 64, "the presampled start needs k <= 64 * waves"
+    shift = np.uint64(ps.key_bits - 16)
+    per_wave = [(np.sort(lane_max[w])[::-1][j - 1] >> shift) << shift for w in range(ps.waves)]
+    return int(min(per_wave))
+
+
 # ----------------------------------------------------------------------------- the method
 @dataclasses.dataclass
 class RunStats:
@@ -161,12 +222,17 @@ def radix_select_topk(v: np.ndarray, pos: np.ndarray, j: np.ndarray, cand: np.nd
 
 
 def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B: int, B2: int,
-                     order: np.ndarray) -> Tuple[np.ndarray, RunStats]:
+                     order: np.ndarray, keys: Optional[np.ndarray] = None,
+                     presample: Optional[Presample] = None,
+                     second: Optional[int] = None) -> Tuple[np.ndarray, RunStats]:
     """DeepSelectTopk over the elements [lo, hi) of a row (indices stay row-relative).
 
     ``order`` lists the blocks of the range in processing order (block b covers
-    [lo + b*B, min(lo + (b+1)*B, hi))). Returns the kept positions (at most k, unordered)
-    and the run's counts.
+    [lo + b*B, min(lo + (b+1)*B, hi))). With ``presample`` (and the row's ``keys``) the run
+    starts from the presampled threshold when the first block read is whole; ``second`` is
+    the block at the second position of the order (None when that position is empty), which
+    the threshold also covers on ranges of fewer than 8 blocks. Returns the kept positions
+    (at most k, unordered) and the run's counts.
     """
     n = hi - lo
     assert n >= 1 and k >= 1 and B >= 1 and B2 >= 1
@@ -176,11 +242,24 @@ def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B
     jall = np.arange(v.size, dtype=np.int64)
     cand = np.zeros(0, np.int64)
     thr: Optional[Pair] = None  # None: the threshold is -inf, every element is accepted
+    t0: Optional[int] = None    # presampled start: keep key >= t0 until the first compaction
+
+    def whole(b: int) -> bool:
+        return lo + (b + 1) * B <= hi
+
+    if presample is not None and whole(int(order[0])):
+        firsts = [int(order[0])] + ([second] if m < 8 and second is not None and whole(second) else [])
+        t0 = presample_key([keys[lo + b * B:lo + (b + 1) * B] for b in firsts], k, presample)
     for b in order:
         blo, bhi = lo + int(b) * B, min(lo + (int(b) + 1) * B, hi)
         js = np.arange(blo, bhi, dtype=np.int64)
         st.reads[blo - lo:bhi - lo] += 1
-        keep = js if thr is None else js[_beats(v[js], pos[js], js, thr)]
+        if thr is not None:
+            keep = js[_beats(v[js], pos[js], js, thr)]
+        elif t0 is not None:
+            keep = js[keys[js] >= np.uint64(t0)]
+        else:
+            keep = js
         cand = np.concatenate([cand, keep])
         st.A += int(keep.size)
         st.max_len = max(st.max_len, int(cand.size))
@@ -202,10 +281,13 @@ def sort_output(v: np.ndarray, pos: np.ndarray, kept: np.ndarray) -> np.ndarray:
 
 
 def deepselect_row(row: np.ndarray, k: int, B: int, B2: int, family: str = "feistel", seed: int = 0,
-                   row_id: int = 0, slice_len: Optional[int] = None) -> Tuple[np.ndarray, List[RunStats]]:
+                   row_id: int = 0, slice_len: Optional[int] = None, group: int = 1,
+                   presample_waves: Optional[int] = None) -> Tuple[np.ndarray, List[RunStats]]:
     """DeepSelect on one row (bf16 bits or float32), optionally split into slices.
 
-    Returns the top-k indices in output order and the per-slice counts.
+    ``group`` > 1 draws the Feistel order over groups of blocks; ``presample_waves`` (the
+    workgroup's waves) turns on the presampled start. Returns the top-k indices in output
+    order and the per-slice counts.
     """
     v = widen(row)
     pos = (~np.signbit(v)).astype(np.int64)
@@ -215,12 +297,23 @@ def deepselect_row(row: np.ndarray, k: int, B: int, B2: int, family: str = "feis
     if slice_len is None:
         slice_len = -(-n // B) * B
     assert slice_len % B == 0 and slice_len >= B
+    keys, ps = None, None
+    if presample_waves is not None:
+        keys = keys_of(row)
+        bf16 = row.dtype == np.uint16
+        ps = Presample(presample_waves, 8 if bf16 else 4, 16 if bf16 else 32)
+    if group != 1 and family != "feistel":
+        raise ValueError("grouped orders are Feistel orders")
     stats = []
     kept_all = []
     for s, lo in enumerate(range(0, n, slice_len)):
         hi = min(lo + slice_len, n)
         m = -(-(hi - lo) // B)
-        kept, st = deepselect_range(v, pos, lo, hi, k, B, B2, block_order(family, m, seed, row_id, s))
+        order = grouped_order(m, group, seed, row_id, s) if group != 1 else block_order(family, m, seed, row_id, s)
+        # the second position of the order: the first group's second block (none past the end)
+        second = (int(order[1]) if m > 1 else None) if group == 1 else \
+            (int(order[0]) + 1 if int(order[0]) + 1 < m else None)
+        kept, st = deepselect_range(v, pos, lo, hi, k, B, B2, order, keys, ps, second)
         stats.append(st)
         kept_all.append(kept)
     union = np.concatenate(kept_all)

@@ -113,29 +113,40 @@ def test_fuzz():
             assert e.status == ts.DS_ERR_UNSUPPORTED and cfg is not None, str(e)
 
 
+@pytest.mark.parametrize("mode", ["design-note", "default"])
 @pytest.mark.parametrize("dtype,n,k,block,slack,slices", [
     (gen.BF16, 50000, 100, 1024, 333, 3),
     (gen.FP32, 129280, 512, 1024, 1024, 1),
     (gen.BF16, 262144, 512, 1024, 1024, 1),
     (gen.FP32, 70000, 64, 2048, 100, 4),
+    (gen.BF16, 131072, 512, 0, 0, 4),   # the indexer shape's plan: 4 blocks per slice
+    (gen.FP32, 129280, 512, 0, 0, 1),   # the sampler shape's plan: 16 blocks, groups of two
 ])
-def test_counters_match_model(dtype, n, k, block, slack, slices):
+def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
     """The kernel's A, R, W, max buffer length and read checksums equal the CPU model's under
-    the same Feistel block order, B, B2 and slicing (with the design note's start and order:
-    no presampled threshold, a random order of single blocks)."""
+    the same Feistel block order, B, B2 and slicing: with the design note's start and order
+    (no presampled threshold, a random order of single blocks) forced, and with the plan's
+    own presampled start and order groups."""
     x = gen.rows_family("normal", dtype, 17, 2, n)
     x[1] = gen.rows_family("ascending", dtype, 18, 1, n)[0]
-    cfg = {"block": block, "slack": slack, "slices": slices, "presample": ts.PRESAMPLE_OFF, "order_group": 1}
+    cfg = {"slices": slices}
+    if block:
+        cfg.update(block=block, slack=slack)
+    if mode == "design-note":
+        cfg.update(presample=ts.PRESAMPLE_OFF, order_group=1)
     seed = 99
     say(f"[gpu] counters: n={n} k={k} cfg={cfg}")
     gv, gi, (plan, st) = run_gpu(x, k, seed=seed, cfg=cfg, stats=True)
     wv, wi = otk.topk(x, k)
     assert_same(x, k, gv, gi, wv, wi, "counters-run")
+    pw = plan["waves"] if plan["presample"] == ts.PRESAMPLE_ON else None
+    if mode == "design-note":
+        assert pw is None and plan["order_group"] == 1
     for r in range(x.shape[0]):
         per = -(-n // plan["slices"])
         slice_len = -(-per // plan["block"]) * plan["block"]  # the planner's slice length
         _, mst = model.deepselect_row(x[r], k, plan["block"], plan["slack"], "feistel", seed=seed, row_id=r,
-                                      slice_len=slice_len)
+                                      slice_len=slice_len, group=plan["order_group"], presample_waves=pw)
         assert len(mst) == plan["slices"]
         for s, ms in enumerate(mst):
             g = st[r, s]

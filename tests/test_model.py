@@ -224,3 +224,99 @@ def test_expected_work_bound(shape):
             mean = float(np.mean(ws))
             half = 1.96 * float(np.std(ws)) / math.sqrt(len(ws))
             assert mean + half <= bound, (name, kind, fam, mean, half, bound)
+
+
+# ----------------------------------------------------------------------------- grouped order, presample
+def test_keys_follow_numeric_order():
+    """keys_of orders values as numbers do, with +0 above -0 (bf16 and fp32, specials too)."""
+    for dtype in (gen.BF16, gen.FP32):
+        x = np.concatenate([gen.rows_family(f, dtype, 61, 1, 4000)[0] for f in ("normal", "specials", "tiny", "neg")])
+        keys = model.keys_of(x).astype(np.int64)
+        v = model.widen(x)
+        pos = (~np.signbit(v)).astype(np.int64)
+        by_key = np.argsort(keys, kind="stable")
+        by_value = np.lexsort((pos, v))  # value ascending, -0 before +0
+        assert np.array_equal(keys[by_key], keys[by_value])
+        same = (v[:, None] == v[None, :]) & (pos[:, None] == pos[None, :])
+        assert np.array_equal(same[:200, :200], (keys[:200, None] == keys[None, :200]))
+    one, mone = np.array([0x3F80], np.uint16), np.array([0xBF80], np.uint16)  # bf16 +1.0, -1.0
+    assert int(model.keys_of(one)[0]) == 0xBF80 and int(model.keys_of(mone)[0]) == 0x407F
+    z = np.array([0.0, -0.0], np.float32)
+    assert model.keys_of(z).tolist() == [0x80000000, 0x7FFFFFFF]
+
+
+@pytest.mark.parametrize("m,group", [(1, 2), (7, 2), (8, 2), (16, 2), (13, 4), (5, 1)])
+def test_grouped_order_structure(m, group):
+    order = model.grouped_order(m, group, seed=9, row=3, slice_=1)
+    assert sorted(order.tolist()) == list(range(m))
+    groups = model.feistel_order(-(-m // group), 9, 3, 1)
+    want = [g * group + j for g in groups for j in range(group) if g * group + j < m]
+    assert order.tolist() == want
+    if group == 1:
+        assert order.tolist() == model.feistel_order(m, 9, 3, 1).tolist()
+
+
+def _brute_t0(blocks, k, waves, vec, bits):
+    """T0 by its definition, with an explicit search per wave: the largest value whose low
+    (bits - 16) bits are zero that at least ceil(k/waves) lane maxima reach."""
+    lane_max = {}
+    for kb in blocks:
+        for o, key in enumerate(kb.tolist()):
+            lane = ((o // (64 * vec)) % waves, (o % (64 * vec)) // vec)
+            lane_max[lane] = max(lane_max.get(lane, 0), key)
+    j = -(-k // waves)
+    out = []
+    for w in range(waves):
+        maxima = [lane_max.get((w, l), 0) for l in range(64)]
+        best = 0
+        for top16 in range(1 << 16):
+            v = top16 << (bits - 16)
+            if sum(mx >= v for mx in maxima) >= j:
+                best = v
+            else:
+                break
+        out.append(best)
+    return min(out)
+
+
+@pytest.mark.parametrize("dtype,waves,k,nblocks", [(gen.BF16, 2, 100, 1), (gen.BF16, 2, 128, 2),
+                                                    (gen.FP32, 4, 256, 1), (gen.FP32, 4, 7, 2)])
+@pytest.mark.parametrize("family", ["normal", "ties", "neg"])
+def test_presample_key(dtype, waves, k, nblocks, family):
+    """T0 equals its definition (a brute-force search per wave) and at least k of the
+    sampled elements reach it, so it never exceeds their k-th largest key."""
+    vec = 8 if dtype == gen.BF16 else 4
+    bits = 16 if dtype == gen.BF16 else 32
+    B = waves * 64 * vec
+    x = gen.rows_family(family, dtype, 63, 1, nblocks * B)[0]
+    keys = model.keys_of(x)
+    blocks = [keys[b * B:(b + 1) * B] for b in range(nblocks)]
+    t0 = model.presample_key(blocks, k, model.Presample(waves, vec, bits))
+    if family != "ties" or dtype == gen.BF16:  # the brute force walks 2^16 candidates at most
+        assert t0 == _brute_t0(blocks, k, waves, vec, bits)
+    assert int((keys >= np.uint64(t0)).sum()) >= k
+    assert t0 <= int(np.sort(keys)[::-1][k - 1])
+
+
+@pytest.mark.parametrize("family", ["normal", "ascending", "ties", "specials"])
+@pytest.mark.parametrize("dtype,n,k,B,slice_len,group", [
+    (gen.BF16, 20000, 100, 1024, None, 2),   # 20 blocks, one presampled block
+    (gen.BF16, 6000, 128, 1024, None, 1),    # 6 blocks: the first two presampled
+    (gen.FP32, 9000, 200, 1024, 4096, 2),    # slices of 4 blocks, groups of two
+    (gen.FP32, 3000, 50, 1024, None, 4),     # a short last group
+])
+def test_model_grouped_presampled_matches_oracle(family, dtype, n, k, B, slice_len, group):
+    """The grouped order and the presampled start keep the result exact and the design
+    note's invariants; on i.i.d. rows the presampled start appends fewer elements."""
+    waves = 2 if dtype == gen.BF16 else 4
+    x = gen.rows_family(family, dtype, 65, 2, n)
+    _, want = otk.topk(x, k)
+    for r in range(x.shape[0]):
+        got, stats = model.deepselect_row(x[r], k, B, 256, seed=r + 3, row_id=r, slice_len=slice_len, group=group,
+                                          presample_waves=waves)
+        assert got.tolist() == want[r].tolist()
+        for st in stats:
+            _check_invariants(st, n, k, B, 256)
+        if family == "normal":
+            _, plain = model.deepselect_row(x[r], k, B, 256, seed=r + 3, row_id=r, slice_len=slice_len, group=group)
+            assert sum(s.A for s in stats) < sum(s.A for s in plain)
