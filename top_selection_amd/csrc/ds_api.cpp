@@ -2,6 +2,7 @@
 // workspace cache of ds_topk, and dispatch to the HIP kernels. Validation is pure host
 // code and runs before any HIP call, so every error path works without a GPU.
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <unordered_map>
 
@@ -16,7 +17,12 @@ constexpr int64_t kMaxLdsBytes = 160 * 1024;    // LDS per workgroup on gfx950
 constexpr int64_t kMaxSliceBytes = 0x7FFFFF00;  // buffer offsets are 31-bit
 constexpr int kChunkBf16 = 512, kChunkFp32 = 256;
 constexpr int kMergeBlock = ds::kMergeShape.waves * ds::kMergeShape.cpw * 128;
-constexpr int kDefaultSlacks[] = {4096, 2048};  // B2 when not forced (at least k), largest that fits
+// B2 when not forced: the largest of these (and at least k) that fits in LDS and is at most
+// twice sqrt(k (k + B)). The design note's expected-work bound (1 + k/B2)(k + B + B2) H_m is
+// smallest at B2 = sqrt(k (k + B)); on MI355X a compaction costs more, relative to the appends
+// it saves, than the bound counts, and twice that measured best (4096 at k = 512, B = 8192;
+// 1024 at k = 32).
+constexpr int kDefaultSlacks[] = {4096, 2048, 1024, 512, 256};
 // default select shapes (indices into kSelectShapes), best first
 constexpr int kDefaultFp32[] = {8, 7, 2, 1};  // 16x2 (B=8192), 16x1 (4096), 4x2 (2048), 4x1 (1024)
 constexpr int kDefaultBf16[] = {7, 3, 1, 0};  // 16x1 (B=8192), 8x1 (4096), 4x1 (2048), 2x1 (1024)
@@ -100,7 +106,9 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   size_t lds = 0;
   auto fit = [&](int s) -> bool {
     const int b = kSelectShapes[s].waves * kSelectShapes[s].cpw * chunk;
+    const double cap = 2.0 * std::sqrt(static_cast<double>(k) * (static_cast<double>(k) + b));
     for (int want : kDefaultSlacks) {
+      if (!c.slack && want > cap && want != kDefaultSlacks[sizeof(kDefaultSlacks) / sizeof(int) - 1]) continue;
       int sl = c.slack ? c.slack : std::max(k, want);
       if (sl + b < sort_cap) {
         if (c.slack) return false;  // the final sort runs in the append region
