@@ -289,3 +289,21 @@ def test_list_merge_values_only_many_slices():
     assert plan["merge"] == ts.MERGE_LISTS and plan["block"] == 8192
     _check(x, 32, "values-only 256 slices", cfg=cfg, indices=False)
     _check(x, 32, "values+indices 256 slices", cfg=cfg)
+
+
+def test_list_merge_many_rows():
+    """More split rows than one list-merge launch covers (its grid holds at most 65535 rows
+    in z): rows on both sides of the boundary, the last rows and a random sample equal the
+    oracle."""
+    rows, n, k = 65535 + 101, 2048, 16
+    x = gen.rows_family("normal", gen.BF16, 71, rows, n)
+    cfg = {"slices": 2, "block": 1024}
+    plan = ts.ds_topk_plan(rows, n, k, gen.BF16, cfg)
+    assert plan["slices"] == 2 and plan["merge"] == ts.MERGE_LISTS
+    say(f"[gpu] many rows: rows={rows} n={n} k={k} cfg={cfg}")
+    gv, gi, _ = run_gpu(x, k, cfg=cfg)
+    rng = np.random.default_rng(5)
+    pick = sorted(set(range(8)) | set(range(65528, 65544)) | set(range(rows - 8, rows)) |
+                  set(rng.choice(rows, 40, replace=False).tolist()))
+    wv, wi = otk.topk(x[pick], k)
+    assert_same(x[pick], k, gv[pick], gi[pick], wv, wi, "many rows")
