@@ -1155,15 +1155,16 @@ __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_
 
 // --------------------------------------------------------------------------- slice merge
 
-// Merge of S sorted lists (S <= MAXS <= kMaxListGroup, k entries each, best first, as (key, index)
-// pairs at src[s * k + i]) into their k best, sorted: written to the outputs at at0 + rank,
-// or, with pairs, as pairs at pairs[rank]. The lists are loaded into LDS (lds: S * k 64-bit
-// words, then S 32-bit prefix lengths) as composites; an entry's place in the merged order is its position in its own
-// list plus, for every other list, the number of that list's entries that rank above it
-// (binary searches, all lists searched in the same step with clamped, always valid indices;
-// equal entries of earlier lists count as above). Padding (composite 0) ranks below every
-// element; it is placed only when the lists hold fewer than k elements together, as padding.
-// Places the entries of lists [l0, l1) (all lists are loaded and searched).
+// Merge of S sorted lists (S <= MAXS <= kMaxListGroup, k entries each, best first, as
+// (key, index) pairs at src[s * k + i]) into their k best, sorted: written to the outputs at
+// at0 + rank, or, with pairs, as pairs at pairs[rank]. The lists are loaded into LDS as
+// composites (lds: S * k 64-bit words, then S 32-bit prefix lengths); an entry's place in
+// the merged order is its position in its own list plus, for every other list, the number
+// of that list's entries that rank above it (binary searches, all lists searched in the
+// same step with clamped, always valid indices; equal entries of earlier lists count as
+// above). Padding (composite 0) ranks below every element; it is placed only when the lists
+// hold fewer than k elements together, as padding. Places the entries of lists [l0, l1)
+// (all lists are loaded and searched).
 template <int DT, int WAVES, uint32_t MAXS>
 __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint32_t k, uint32_t pk, uint64_t* lds,
                                               void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t at0,
