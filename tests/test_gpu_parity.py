@@ -127,7 +127,7 @@ def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
     the same Feistel block order, B, B2 and slicing: with the design note's start and order
     (no presampled threshold, a random order of single blocks) forced, and with the plan's
     own presampled start and order groups."""
-    x = gen.rows_family("normal", dtype, 17, 2, n)
+    x = gen.rows_family("normal", dtype, 17, 9, n)  # 8 rows dealt to the XCDs, 1 in plain order
     x[1] = gen.rows_family("ascending", dtype, 18, 1, n)[0]
     cfg = {"slices": slices}
     if block:
@@ -292,9 +292,9 @@ def test_list_merge_values_only_many_slices():
 
 
 def test_list_merge_many_rows():
-    """More split rows than one list-merge launch covers (its grid holds at most 65535 rows
-    in z): rows on both sides of the boundary, the last rows and a random sample equal the
-    oracle."""
+    """More split rows than one list-merge launch covers (65528 rows per launch, rows dealt to
+    the XCDs in eights and the last rows in plain order): rows on both sides of the launch
+    boundary, the last rows and a random sample equal the oracle."""
     rows, n, k = 65535 + 101, 2048, 16
     x = gen.rows_family("normal", gen.BF16, 71, rows, n)
     cfg = {"slices": 2, "block": 1024}
@@ -303,7 +303,7 @@ def test_list_merge_many_rows():
     say(f"[gpu] many rows: rows={rows} n={n} k={k} cfg={cfg}")
     gv, gi, _ = run_gpu(x, k, cfg=cfg)
     rng = np.random.default_rng(5)
-    pick = sorted(set(range(8)) | set(range(65528, 65544)) | set(range(rows - 8, rows)) |
+    pick = sorted(set(range(8)) | set(range(65520, 65544)) | set(range(rows - 12, rows)) |
                   set(rng.choice(rows, 40, replace=False).tolist()))
     wv, wi = otk.topk(x[pick], k)
     assert_same(x[pick], k, gv[pick], gi[pick], wv, wi, "many rows")

@@ -60,6 +60,22 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_
   return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0);
 }
 
+// Work item of workgroup `wg` when each unit (a row) has `per` workgroups and `units` units:
+// the units are dealt to the eight XCDs (workgroup i runs on XCD i mod 8) so that all
+// workgroups of a unit run on one XCD and share its L2; units past the last multiple of 8
+// follow in plain order. Returns the unit and the workgroup's index within it.
+__device__ __forceinline__ void xcd_unit(uint32_t wg, uint32_t per, uint32_t units, uint32_t& unit, uint32_t& sub) {
+  const uint32_t dealt = (units & ~7u) * per;
+  if (wg < dealt) {
+    const uint32_t j = wg >> 3;
+    unit = (wg & 7u) + 8u * (j / per);
+    sub = j % per;
+  } else {
+    unit = (units & ~7u) + (wg - dealt) / per;
+    sub = (wg - dealt) % per;
+  }
+}
+
 // The same LDS location as an LDS-address-space pointer: accesses through it are always LDS
 // instructions (a generic pointer the compiler cannot trace becomes a flat access, which also
 // counts as an outstanding global access and makes the compiler wait for every global load).
@@ -1716,8 +1732,10 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   __shared__ Scalars sc;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
-  const uint32_t row = blockIdx.x / static_cast<uint32_t>(p.slices);
-  const uint32_t slice = blockIdx.x % static_cast<uint32_t>(p.slices);
+  // a row's slices run on one XCD, where the merge of their lists reads them from L2
+  uint32_t row, slice;
+  xcd_unit(blockIdx.x, static_cast<uint32_t>(p.slices), gridDim.x / static_cast<uint32_t>(p.slices), row, slice);
+  const uint32_t wg_item = row * static_cast<uint32_t>(p.slices) + slice;  // (row, slice) in row-major order
   const uint32_t slice_lo = slice * static_cast<uint32_t>(p.slice_len);
   const uint32_t len = static_cast<uint32_t>(min(p.slice_len, p.n - static_cast<int64_t>(slice_lo)));
   const uint32_t m = (len + B - 1) / B;
@@ -1770,7 +1788,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
     }
     lds_sync();
     if (tid == 0) {
-      ds_stats* o = p.stats + blockIdx.x;
+      ds_stats* o = p.stats + wg_item;
       o->appended = sc.st_a;
       o->compactions = sc.st_r;
       o->work = sc.st_w;
@@ -1804,8 +1822,8 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   }
   if (stats && tid == 0) {
     const uint64_t t_end = wall_clock64();
-    p.stats[blockIdx.x].t_total_ns = (t_end - t_start) * 10;
-    p.stats[blockIdx.x].t_final_ns = (t_end - sc.st_tf) * 10;
+    p.stats[wg_item].t_total_ns = (t_end - t_start) * 10;
+    p.stats[wg_item].t_final_ns = (t_end - sc.st_tf) * 10;
   }
 }
 
@@ -1859,9 +1877,13 @@ __global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(MergeParams p) 
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const uint32_t S = static_cast<uint32_t>(p.lists), G = static_cast<uint32_t>(p.group);
   const uint32_t per = static_cast<uint32_t>(p.per_wg), k = static_cast<uint32_t>(p.k);
-  // grid: (workgroups per group, groups, rows of this launch)
-  const uint64_t row = static_cast<uint64_t>(p.row0) + blockIdx.z;
-  const uint32_t g = blockIdx.y, l0 = blockIdx.x * per;
+  // grid: (workgroups per group, groups, rows of this launch); a row's workgroups run on the
+  // XCD that ran its slices (row0 is a multiple of 8), whose L2 holds their lists
+  const uint32_t wpr = gridDim.x * gridDim.y;
+  uint32_t lrow, r;
+  xcd_unit(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), wpr, gridDim.z, lrow, r);
+  const uint64_t row = static_cast<uint64_t>(p.row0) + lrow;
+  const uint32_t g = r / gridDim.x, l0 = (r % gridDim.x) * per;
   const uint32_t first = g * G, gl = min(G, S - first);  // the group's lists
   if (l0 >= gl) return;  // the same for the whole workgroup
   const uint32_t pk = gl == G ? static_cast<uint32_t>(p.pk) : (k + gl - 1u) / gl;  // ceil(k / gl)
@@ -1948,8 +1970,8 @@ hipError_t launch_select_dt(int shape, const SelectParams& p, int64_t rows, size
   }
 }
 
-// Rows per list-merge launch (the grid's z dimension).
-constexpr int64_t kMaxGridRows = 65535;
+// Rows per list-merge launch (the grid's z dimension; a multiple of 8, see xcd_unit).
+constexpr int64_t kMaxGridRows = 65528;
 
 // One instantiation per bound on the lists merged together.
 template <int DT, uint32_t MAXS>
