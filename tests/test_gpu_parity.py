@@ -121,6 +121,8 @@ def test_fuzz():
     (gen.FP32, 70000, 64, 2048, 100, 4),
     (gen.BF16, 131072, 512, 0, 0, 4),   # the indexer shape's plan: 4 blocks per slice
     (gen.FP32, 129280, 512, 0, 0, 1),   # the sampler shape's plan: 16 blocks, groups of two
+    (gen.FP32, 200000, 32, 0, 0, 2),    # small k: blocks of 16384 (16 waves x 4 chunks)
+    (gen.BF16, 200000, 16, 0, 0, 1),    # small k, bf16: blocks of 16384 (16 waves x 2 chunks)
 ])
 def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
     """The kernel's A, R, W, max buffer length and read checksums equal the CPU model's under
@@ -281,12 +283,12 @@ def test_list_merge_levels(dtype, family, rows, n, k, slices, block):
 
 
 def test_list_merge_values_only_many_slices():
-    """A values-only giant row cut into 256 slices of two blocks: two list-merge levels with
-    sixteen lists per workgroup (k = 32)."""
+    """A values-only giant row cut into 256 slices: two list-merge levels with sixteen lists
+    per workgroup (k = 32)."""
     x = gen.WORKLOADS["c5_giant"].make(n=1 << 22)
     cfg = {"slices": 256}
     plan = ts.ds_topk_plan(1, 1 << 22, 32, gen.FP32, cfg)
-    assert plan["merge"] == ts.MERGE_LISTS and plan["block"] == 8192
+    assert plan["merge"] == ts.MERGE_LISTS and plan["slices"] == 256
     _check(x, 32, "values-only 256 slices", cfg=cfg, indices=False)
     _check(x, 32, "values+indices 256 slices", cfg=cfg)
 

@@ -67,7 +67,7 @@ struct Shape {
 
 // Select-kernel shapes built for each element type. The block size is
 // waves * cpw * 64 lanes * (16 / elem_bytes) elements.
-constexpr Shape kSelectShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}, {8, 2}, {4, 4}, {8, 4}, {16, 1}, {16, 2}};
+constexpr Shape kSelectShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}, {8, 2}, {4, 4}, {8, 4}, {16, 1}, {16, 2}, {16, 4}};
 constexpr int kNumSelectShapes = sizeof(kSelectShapes) / sizeof(kSelectShapes[0]);
 constexpr Shape kMergeShape = {16, 2};  // 16 waves x 2 chunks x 128 entries = 4096 entries per block
 

@@ -1966,6 +1966,7 @@ hipError_t launch_select_dt(int shape, const SelectParams& p, int64_t rows, size
     case 6: return launch_select_shape<DT, 8, 4>(p, rows, lds, s);
     case 7: return launch_select_shape<DT, 16, 1>(p, rows, lds, s);
     case 8: return launch_select_shape<DT, 16, 2>(p, rows, lds, s);
+    case 9: return launch_select_shape<DT, 16, 4>(p, rows, lds, s);
     default: return hipErrorInvalidValue;
   }
 }
