@@ -51,8 +51,9 @@ def source_digest() -> str:
     a comment keeps counter summaries taken on the same code valid."""
     import re
     h = hashlib.sha256()
-    for f in ("ds_kernels.hip", "ds_api.cpp", "ds_internal.h"):
-        with open(os.path.join(ROOT, "top_selection_amd", "csrc", f), encoding="utf-8") as fh:
+    csrc = os.path.join(ROOT, "top_selection_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)

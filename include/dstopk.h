@@ -50,7 +50,9 @@ extern "C" {
 #define DS_ERR_LAUNCH (-5)      /* the HIP runtime refused a launch or an allocation */
 #define DS_ERR_DEVICE (-6)      /* no usable gfx950 device, or a device query failed */
 
-#define DS_MAX_K 4096 /* the largest supported k (DeepSelect supports topk <= 4096) */
+/* The largest supported k: the DeepSelect library accepts top-k of at most 4096 and no more
+ * (TileLang tutorial chapter 37, "DeepSelect top-k", section 1.2, the constraint matrix). */
+#define DS_MAX_K 4096
 
 /*
  * Launch configuration. Zero in any field means "choose automatically".
@@ -88,6 +90,22 @@ extern "C" {
 #define DS_MERGE_AUTO 0
 #define DS_MERGE_LISTS 1
 #define DS_MERGE_SELECT 2
+/*
+ *   schedule   when the buffer is checked. DS_SCHEDULE_LOCKSTEP is the design note's schedule
+ *              ("Algorithm", the DeepSelectTopk pseudocode): every wave of the workgroup
+ *              filters its share of a block, a workgroup barrier follows, and then the buffer
+ *              is compacted if it holds at least k + B2 entries. DS_SCHEDULE_FREE (the
+ *              default; zero means it) drops the barrier after every block: each wave streams
+ *              its shares on its own, reserves buffer space with one atomic and checks the
+ *              length itself after every share; a wave that sees k + B2 or more stops at a
+ *              barrier and the waves compact together. A wave appends at most one more share
+ *              after the length crosses k + B2, so the buffer bound k + B2 + B of the design
+ *              note's notes still holds. The result is the same for both; only the counters
+ *              (which elements were appended with which threshold) differ.
+ */
+#define DS_SCHEDULE_AUTO 0
+#define DS_SCHEDULE_FREE 1
+#define DS_SCHEDULE_LOCKSTEP 2
 
 typedef struct ds_config {
   int32_t block;
@@ -97,11 +115,16 @@ typedef struct ds_config {
   int32_t presample;
   int32_t order_group;
   int32_t merge;
+  int32_t schedule;
 } ds_config;
 
 /*
  * Per-(row, slice) counters of one run, filled when ds_topk_ex gets a stats pointer.
- * Names follow the design note's analysis section.
+ * Names follow the design note's analysis section ("Expected Upper Bound on the Total
+ * Elements Processed by RadixSelectTopK": A, R, W). Under DS_SCHEDULE_LOCKSTEP every
+ * counter is a function of (x, k, B, B2, seed, slicing); under DS_SCHEDULE_FREE reads,
+ * index_sum and monotone are, while A, R, W and max_len depend on how the waves interleave
+ * (W = A + k*R, R*B2 <= A and max_len <= k + B2 + B - 1 hold for both).
  */
 typedef struct ds_stats {
   uint64_t appended;    /* A: elements appended to the candidate buffer */
@@ -123,21 +146,32 @@ typedef struct ds_stats {
 } ds_stats;
 
 /*
- * ds_topk -- top-k of every row.
+ * ds_topk -- top-k of every row (DeepSelect design note, "Algorithm": DeepSelectTopk, whose
+ * final RadixSelectTopK returns exactly the k largest; ties go to the smaller index, the
+ * convention of TileLang tutorial chapter 33's top-k gate reference).
  *   x          device, rows x row_stride elements of `dtype`; row r starts at
  *              x + r*row_stride elements. 16-byte aligned; row_stride*elem_bytes a
- *              multiple of 16 (DS_ERR_ALIGNMENT otherwise).
+ *              multiple of 16 (DS_ERR_ALIGNMENT otherwise): the scan reads 16-byte vectors.
+ *              The DeepSelect library has its own row-stride alignment contract (tutorial
+ *              chapter 37, section 1.2); 16 bytes is this build's.
  *   rows       >= 0; rows == 0 returns DS_OK and enqueues nothing.
  *   n          elements per row, 1 <= n <= 2^31 - 1; row_stride >= n.
- *   k          1 <= k <= min(DS_MAX_K, n).
- *   dtype      DS_BF16 or DS_FP32.
- *   seed       picks the block order only; it never changes the result.
+ *   k          1 <= k <= min(DS_MAX_K, n) (the pseudocode's "require 1 <= k <= N").
+ *   dtype      DS_BF16 (Lightning Indexer scores) or DS_FP32 (sampler logits): the two
+ *              input types of tutorial chapter 37, sections 1.1-1.2.
+ *   seed       picks the block order only; it never changes the result (design note: the
+ *              permutation is independent of x and only the cost is random).
  *   out_vals   device [rows, k] of `dtype` (bit patterns of the selected elements), or NULL.
  *   out_idx    device [rows, k] int32, or NULL (values only). Not both NULL.
  *   stream     hipStream_t as void*.
- * When the split path needs scratch memory, ds_topk takes it from a per-device cache that
- * grows on demand (hipMalloc on the calling thread, the first time a larger size is
- * needed) and lives until the library is unloaded. Use ds_topk_ex to pass it instead.
+ * When the split path needs scratch memory, ds_topk takes it from a cache that holds one
+ * buffer per (device, stream): calls on one stream share it (the stream orders them), calls
+ * on different streams never do. A cached buffer is never freed before the library is
+ * unloaded (when a stream needs more, its old buffer is kept aside), so a graph that
+ * captured a call keeps a valid buffer. Growing the cache calls hipMalloc on the calling
+ * thread; on a stream that is being captured it returns DS_ERR_WORKSPACE instead (capture
+ * a ds_topk_ex call with its own workspace, or make one uncaptured call of the same size on
+ * that stream first).
  */
 int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
             void* out_vals, int32_t* out_idx, void* stream);
@@ -145,31 +179,38 @@ int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, i
 /*
  * ds_topk_plan -- the configuration ds_topk / ds_topk_ex would use (cfg may force some
  * fields; NULL = all automatic). Writes it to *out. Host only, no device call except a
- * one-time query of the current device's compute-unit count.
+ * one-time query of the current device's compute-unit count. The parameters are the
+ * design note's B and B2 ("Algorithm") and the cluster split's parts per row
+ * ("Implementation", last paragraph).
  */
 int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, ds_config* out);
 
 /*
  * ds_topk_workspace_size -- bytes of device workspace ds_topk_ex needs for this call
- * (0 when the plan has one slice per row). Writes it to *bytes.
+ * (0 when the plan has one slice per row). Writes it to *bytes. The workspace holds each
+ * part's k survivors on their way to the merge, where the design note's cluster split
+ * ("Implementation", last paragraph) sends them to the first block of the cluster.
  */
 int ds_topk_workspace_size(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, size_t* bytes);
 
 /*
- * ds_topk_ex -- ds_topk with a caller workspace, a forced configuration and counters.
+ * ds_topk_ex -- ds_topk with a caller workspace, a forced configuration and counters
+ * (the same method: design note, "Algorithm"; the counters of its "Expected Upper Bound"
+ * section).
  *   workspace  device, >= ds_topk_workspace_size bytes, 16-byte aligned; may be NULL when
  *              that size is 0. Its contents on entry do not matter; it is overwritten.
  *              Calls that share a workspace must not overlap in time.
  *   cfg        NULL or fields to force (see ds_config).
  *   stats      NULL, or device [rows, slices] ds_stats filled by the select kernel.
- * Allocates nothing.
+ * Allocates nothing and never synchronises, so it can be captured in a graph.
  */
 int ds_topk_ex(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
                void* out_vals, int32_t* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
                ds_stats* stats, void* stream);
 
 /*
- * ds_topk_slices / ds_topk_merge -- ds_topk_ex as its two launches, for callers that
+ * ds_topk_slices / ds_topk_merge -- ds_topk_ex as its two launches (the per-part top-k and
+ * the merge of the design note's cluster split, "Implementation", last paragraph), for callers that
  * want to time or overlap them separately. ds_topk_slices runs the select kernel: with one
  * slice per row it writes the final outputs; otherwise it writes every slice's k survivors
  * to the workspace (sorted, for the list merge) and ds_topk_merge reduces each row's
@@ -185,17 +226,20 @@ int ds_topk_merge(int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void
                   void* workspace, size_t ws_bytes, const ds_config* cfg, void* stream);
 
 /*
- * ds_probe_read -- measurement aid, not part of top-k: streams `bytes` (a multiple of
+ * ds_probe_read -- measurement aid, not part of top-k (tutorial chapter 37, section 6.1: the
+ * method is judged by how close it comes to reading the input once; this is the plain read
+ * of the same bytes): streams `bytes` (a multiple of
  * 16, 16-byte aligned) from src with the same 16-byte loads the scan uses and writes
  * one 32-bit word per workgroup to sink (device, >= ds_probe_sink_words(bytes) words).
  */
 int ds_probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 int64_t ds_probe_sink_words(int64_t bytes);
 
-/* ds_probe_copy -- measurement aid: a plain 16-byte-vector copy of `bytes` (multiple of 16). */
+/* ds_probe_copy -- measurement aid: a plain 16-byte-vector copy of `bytes` (multiple of 16),
+ * whose known byte counts calibrate the HBM traffic counters. */
 int ds_probe_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
-/* ds_status_string -- a static, human-readable name for a status code. */
+/* ds_status_string -- a static, human-readable name for a status code (never NULL). */
 const char* ds_status_string(int status);
 
 #ifdef __cplusplus

@@ -170,3 +170,15 @@ def test_order_group_plan_field():
     with pytest.raises(ts.DSError) as e:
         ts.ds_topk_plan(4, 32768, 512, ts.BF16, {"order_group": 3, "slices": 1})
     assert e.value.status == ts.DS_ERR_INVALID_ARG
+
+
+def test_schedule_plan_field():
+    """The free-running schedule is the default; the lockstep schedule can be forced; other
+    values are rejected before any launch."""
+    base = {"slices": 2}
+    assert ts.ds_topk_plan(4, 100000, 64, ts.BF16, base)["schedule"] == ts.SCHEDULE_FREE
+    assert ts.ds_topk_plan(4, 100000, 64, ts.BF16, dict(base, schedule=ts.SCHEDULE_LOCKSTEP))["schedule"] == \
+        ts.SCHEDULE_LOCKSTEP
+    with pytest.raises(ts.DSError) as e:
+        ts.ds_topk_plan(4, 100000, 64, ts.BF16, dict(base, schedule=7))
+    assert e.value.status == ts.DS_ERR_INVALID_ARG

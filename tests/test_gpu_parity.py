@@ -17,9 +17,9 @@ from workloads import gen
 pytestmark = pytest.mark.gpu
 
 
-def _check(x, k, label, seed=1, cfg=None, values=True, indices=True, pad_to=0):
+def _check(x, k, label, seed=1, cfg=None, values=True, indices=True, pad_to=0, stats=False):
     say(f"[gpu] {label}: rows={x.shape[0]} n={x.shape[1]} k={k} dtype={x.dtype} cfg={cfg} seed={seed}")
-    gv, gi, _ = run_gpu(x, k, seed=seed, cfg=cfg, values=values, indices=indices, pad_to=pad_to)
+    gv, gi, _ = run_gpu(x, k, seed=seed, cfg=cfg, values=values, indices=indices, pad_to=pad_to, stats=stats)
     wv, wi = otk.topk(x, k)
     assert_same(x, k, gv, gi, wv if values else None, wi if indices else None, label)
 
@@ -113,7 +113,7 @@ def test_fuzz():
             assert e.status == ts.DS_ERR_UNSUPPORTED and cfg is not None, str(e)
 
 
-@pytest.mark.parametrize("mode", ["design-note", "default"])
+@pytest.mark.parametrize("mode", ["design-note", "default-lockstep", "free"])
 @pytest.mark.parametrize("dtype,n,k,block,slack,slices", [
     (gen.BF16, 50000, 100, 1024, 333, 3),
     (gen.FP32, 129280, 512, 1024, 1024, 1),
@@ -125,13 +125,16 @@ def test_fuzz():
     (gen.BF16, 200000, 16, 0, 0, 1),    # small k, bf16: blocks of 16384 (16 waves x 2 chunks)
 ])
 def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
-    """The kernel's A, R, W, max buffer length and read checksums equal the CPU model's under
-    the same Feistel block order, B, B2 and slicing: with the design note's start and order
-    (no presampled threshold, a random order of single blocks) forced, and with the plan's
-    own presampled start and order groups."""
+    """Under the lockstep schedule the kernel's A, R, W, max buffer length and read checksums
+    equal the CPU model's under the same Feistel block order, B, B2 and slicing: with the
+    design note's start and order (no presampled threshold, a random order of single
+    blocks) forced, and with the plan's own presampled start and order groups. Under the
+    free-running schedule the counters depend on how the waves interleave, so only what the
+    design note's notes and analysis fix is checked: every element read once, T
+    non-decreasing, W = A + k R, R B2 <= A and the buffer bound k + B2 + B - 1."""
     x = gen.rows_family("normal", dtype, 17, 9, n)  # 8 rows dealt to the XCDs, 1 in plain order
     x[1] = gen.rows_family("ascending", dtype, 18, 1, n)[0]
-    cfg = {"slices": slices}
+    cfg = {"slices": slices, "schedule": ts.SCHEDULE_FREE if mode == "free" else ts.SCHEDULE_LOCKSTEP}
     if block:
         cfg.update(block=block, slack=slack)
     if mode == "design-note":
@@ -144,13 +147,15 @@ def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
     pw = plan["waves"] if plan["presample"] == ts.PRESAMPLE_ON else None
     if mode == "design-note":
         assert pw is None and plan["order_group"] == 1
+    B, B2 = plan["block"], plan["slack"]
     for r in range(x.shape[0]):
         per = -(-n // plan["slices"])
-        slice_len = -(-per // plan["block"]) * plan["block"]  # the planner's slice length
-        _, mst = model.deepselect_row(x[r], k, plan["block"], plan["slack"], "feistel", seed=seed, row_id=r,
-                                      slice_len=slice_len, group=plan["order_group"], presample_waves=pw)
-        assert len(mst) == plan["slices"]
-        for s, ms in enumerate(mst):
+        slice_len = -(-per // B) * B  # the planner's slice length
+        if mode != "free":
+            _, mst = model.deepselect_row(x[r], k, B, B2, "feistel", seed=seed, row_id=r,
+                                          slice_len=slice_len, group=plan["order_group"], presample_waves=pw)
+            assert len(mst) == plan["slices"]
+        for s in range(plan["slices"]):
             g = st[r, s]
             lo = s * slice_len
             ln = min(slice_len, n - lo)
@@ -158,9 +163,11 @@ def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
             assert int(g["reads"]) == ln
             assert int(g["index_sum"]) == ln * lo + ln * (ln - 1) // 2
             assert int(g["monotone"]) == 1
-            assert (int(g["appended"]), int(g["compactions"]), int(g["work"]), int(g["max_len"])) == \
-                (ms.A, ms.R, ms.W, ms.max_len), (r, s)
-            assert int(g["max_len"]) <= k + plan["slack"] + plan["block"] - 1
+            a, rr, w, ml = int(g["appended"]), int(g["compactions"]), int(g["work"]), int(g["max_len"])
+            assert w == a + k * rr and rr * B2 <= a and ml <= k + B2 + B - 1
+            if mode != "free":
+                ms = mst[s]
+                assert (a, rr, w, ml) == (ms.A, ms.R, ms.W, ms.max_len), (r, s)
 
 
 @pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
@@ -309,3 +316,79 @@ def test_list_merge_many_rows():
                   set(rng.choice(rows, 40, replace=False).tolist()))
     wv, wi = otk.topk(x[pick], k)
     assert_same(x[pick], k, gv[pick], gi[pick], wv, wi, "many rows")
+
+
+def test_two_streams_share_nothing():
+    """ds_topk on two streams at once, both on split rows: each stream has its own cached
+    workspace, so both results equal the oracle's."""
+    import torch
+    from gpu_util import to_device, to_numpy_vals
+    xa = gen.WORKLOADS["c2_indexer"].make(rows=8)
+    xb = gen.rows_family("ascending", gen.BF16, 77, 8, 131072)
+    assert ts.ds_topk_plan(8, 131072, 512, gen.BF16)["slices"] > 1
+    da, db = to_device(xa), to_device(xb)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say(f"[gpu] two streams, round {rep}")
+        with torch.cuda.stream(sa):
+            va, ia = ts.ds_topk(da, 512, seed=rep, stream=sa)
+        with torch.cuda.stream(sb):
+            vb, ib = ts.ds_topk(db, 512, seed=rep + 10, stream=sb)
+        outs.append((va, ia, vb, ib))
+    torch.cuda.synchronize()
+    wa, wia = otk.topk(xa, 512)
+    wb, wib = otk.topk(xb, 512)
+    for va, ia, vb, ib in outs:
+        assert_same(xa, 512, to_numpy_vals(va), ia.cpu().numpy(), wa, wia, "stream a")
+        assert_same(xb, 512, to_numpy_vals(vb), ib.cpu().numpy(), wb, wib, "stream b")
+
+
+def test_cache_growth_refused_under_capture():
+    """Under stream capture ds_topk does not allocate: a call that would grow the stream's
+    cached workspace returns DS_ERR_WORKSPACE, and one that fits is captured and replays
+    correctly."""
+    import torch
+    from gpu_util import to_device, to_numpy_vals
+    s = torch.cuda.Stream()
+    small = gen.WORKLOADS["c2_indexer"].make(rows=2)
+    big = gen.WORKLOADS["c2_indexer"].make(rows=16)
+    ds, db = to_device(small), to_device(big)
+    with torch.cuda.stream(s):
+        ts.ds_topk(ds, 512, stream=s)  # the stream's cache now fits two rows
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    vals = torch.empty((2, 512), dtype=ds.dtype, device="cuda")
+    idx = torch.empty((2, 512), dtype=torch.int32, device="cuda")
+    with torch.cuda.graph(g, stream=s):
+        with pytest.raises(ts.DSError) as e:
+            ts.ds_topk(db, 512, stream=s)
+        ts.ds_topk(ds, 512, out_vals=vals, out_idx=idx, stream=s)
+    assert e.value.status == ts.DS_ERR_WORKSPACE
+    wv, wi = otk.topk(small, 512)
+    for rep in range(3):
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_same(small, 512, to_numpy_vals(vals), idx.cpu().numpy(), wv, wi, f"replay {rep}")
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+@pytest.mark.parametrize("schedule", [ts.SCHEDULE_FREE, ts.SCHEDULE_LOCKSTEP])
+def test_partial_block_first_without_threshold(dtype, schedule):
+    """All-negative rows whose first block read is the partial last block, with no threshold
+    yet (presample off): the zero padding the hardware returns past the row's end must never
+    be appended (a +0 would outrank every real element). Block orders are picked on the CPU
+    (the model's Feistel order is the kernel's) so that the partial block comes first."""
+    B = 16384
+    n = 5 * B + 3392
+    rows = 8
+    x = gen.rows_family("neg", dtype, 91, rows, n)
+    m = -(-n // B)
+    seed = next(s for s in range(1000)
+                if all(int(model.block_order("feistel", m, s, r, 0)[0]) == m - 1 for r in range(2)))
+    cfg = {"slices": 1, "block": B, "presample": ts.PRESAMPLE_OFF, "order_group": 1, "schedule": schedule}
+    _check(x, 64, f"partial-first seed={seed}", seed=seed, cfg=cfg)
+    _check(x, 64, f"partial-first stats seed={seed}", seed=seed, cfg=cfg, stats=True)

@@ -27,6 +27,7 @@ DS_ERR_DEVICE = -6
 DS_MAX_K = 4096
 PRESAMPLE_AUTO, PRESAMPLE_OFF, PRESAMPLE_ON = 0, 1, 2
 MERGE_AUTO, MERGE_LISTS, MERGE_SELECT = 0, 1, 2
+SCHEDULE_AUTO, SCHEDULE_FREE, SCHEDULE_LOCKSTEP = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdstopk.so")
@@ -42,7 +43,7 @@ class DSError(RuntimeError):
 class ds_config(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("slack", ctypes.c_int32), ("slices", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("presample", ctypes.c_int32), ("order_group", ctypes.c_int32),
-                ("merge", ctypes.c_int32)]
+                ("merge", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 STATS_FIELDS = ["appended", "compactions", "work", "max_len", "reads", "index_sum", "monotone", "slice_lo",
@@ -104,7 +105,7 @@ def _cfg(cfg: Optional[Dict[str, int]]):
         return None
     c = ds_config(int(cfg.get("block", 0)), int(cfg.get("slack", 0)), int(cfg.get("slices", 0)),
                   int(cfg.get("waves", 0)), int(cfg.get("presample", 0)), int(cfg.get("order_group", 0)),
-                  int(cfg.get("merge", 0)))
+                  int(cfg.get("merge", 0)), int(cfg.get("schedule", 0)))
     return ctypes.pointer(c)
 
 
@@ -114,7 +115,8 @@ def ds_topk_plan(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, 
     if st != DS_OK:
         raise DSError(st, "ds_topk_plan")
     return {"block": out.block, "slack": out.slack, "slices": out.slices, "waves": out.waves,
-            "presample": out.presample, "order_group": out.order_group, "merge": out.merge}
+            "presample": out.presample, "order_group": out.order_group, "merge": out.merge,
+            "schedule": out.schedule}
 
 
 def ds_topk_workspace_size(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, int]] = None) -> int:

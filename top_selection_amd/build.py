@@ -1,13 +1,19 @@
-"""Build libdstopk.so in place with hipcc for gfx950 (one shared library: kernels + C ABI)."""
+"""Build libdstopk.so in place with hipcc for gfx950 (one shared library: kernels + C ABI).
+
+The device code is instantiated by several translation units (the select kernels once per
+element type and counter mode, then the merge kernels and probes), which compile in
+parallel and link into the one library.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "ds_kernels.hip"), os.path.join(CSRC, "ds_api.cpp")]
+OBJDIR = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libdstopk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -16,26 +22,61 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # never let the compiler form packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# (object name, source, extra flags)
+UNITS = [("select_bf16", "ds_select.hip", ["-DDS_PART_DT=0", "-DDS_PART_STATS=0"]),
+         ("select_fp32", "ds_select.hip", ["-DDS_PART_DT=1", "-DDS_PART_STATS=0"]),
+         ("select_bf16_stats", "ds_select.hip", ["-DDS_PART_DT=0", "-DDS_PART_STATS=1"]),
+         ("select_fp32_stats", "ds_select.hip", ["-DDS_PART_DT=1", "-DDS_PART_STATS=1"]),
+         ("merge", "ds_merge.hip", []),
+         ("api", "ds_api.cpp", [])]
 
-def build(verbose: bool = False) -> str:
-    tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + SOURCES
-    if verbose:
-        print(" ".join(cmd), flush=True)
+NOISE = "packed-fp32-ops"
+
+
+def _run(cmd):
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    noise = "packed-fp32-ops"
-    msgs = [l for l in res.stdout.splitlines() if noise not in l and l.strip()]
-    if res.returncode != 0:
+    msgs = [l for l in res.stdout.splitlines() if NOISE not in l and l.strip()]
+    return res.returncode, msgs
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    tag = "%d" % os.getpid()
+    cmds = []
+    objs = []
+    for name, src, extra in UNITS:
+        obj = os.path.join(OBJDIR, f"{name}.{tag}.o")
+        objs.append(obj)
+        cmds.append([HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
+    jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    failed = False
+    for cmd, (rc, msgs) in zip(cmds, results):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if rc != 0:
+            failed = True
+            sys.stderr.write("\n".join(msgs) + "\n")
+        elif verbose and msgs:
+            print("\n".join(msgs))
+    if failed:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+        raise RuntimeError("hipcc failed")
+    tmp = OUT + ".tmp" + tag
+    rc, msgs = _run([HIPCC] + FLAGS + ["-shared", "-o", tmp] + objs)
+    for o in objs:
+        os.remove(o)
+    if rc != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
-    if verbose and msgs:
-        print("\n".join(msgs))
+        raise RuntimeError(f"hipcc link failed ({rc})")
     os.replace(tmp, OUT)
     return OUT
 

@@ -3,8 +3,11 @@
 // code and runs before any HIP call, so every error path works without a GPU.
 #include <algorithm>
 #include <cmath>
+#include <map>
 #include <mutex>
 #include <unordered_map>
+#include <utility>
+#include <vector>
 
 #include "ds_internal.h"
 
@@ -52,6 +55,7 @@ struct Plan {
   size_t lds;
   bool presample;   // the first whole block sets a presampled threshold
   int order_group;  // G: the random order is over groups of G consecutive blocks
+  bool lockstep;    // the design note's schedule: a barrier and the buffer check after every block
   // merge (slices > 1): DS_MERGE_LISTS (levels of the list-merge kernel over sorted slice
   // lists, group[l] lists merged together at level l) or DS_MERGE_SELECT (the merge kernel)
   int merge;
@@ -91,13 +95,15 @@ int check_basic(int64_t rows, int64_t n, int k, int dtype) {
 int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK) return st;
-  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0};
+  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0, 0};
   if (c.block < 0 || c.slack < 0 || c.slices < 0 || c.waves < 0) return DS_ERR_INVALID_ARG;
   if (c.presample != DS_PRESAMPLE_AUTO && c.presample != DS_PRESAMPLE_OFF && c.presample != DS_PRESAMPLE_ON)
     return DS_ERR_INVALID_ARG;
   if (c.order_group != 0 && c.order_group != 1 && c.order_group != 2 && c.order_group != 4)
     return DS_ERR_INVALID_ARG;
   if (c.merge != DS_MERGE_AUTO && c.merge != DS_MERGE_LISTS && c.merge != DS_MERGE_SELECT) return DS_ERR_INVALID_ARG;
+  if (c.schedule != DS_SCHEDULE_AUTO && c.schedule != DS_SCHEDULE_FREE && c.schedule != DS_SCHEDULE_LOCKSTEP)
+    return DS_ERR_INVALID_ARG;
   const int chunk = chunk_elems(dtype);
   const int eb = elem_bytes(dtype);
 
@@ -198,6 +204,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   // groups of two blocks pay off on long slices (consecutive loads in flight); short slices
   // keep single blocks, which randomise adversarial (sorted) slices better
   p.order_group = c.order_group ? c.order_group : ((slice_len + block - 1) / block >= 8 ? 2 : 1);
+  p.lockstep = c.schedule == DS_SCHEDULE_LOCKSTEP;
   if (slices > 1) {
     const int64_t entries = slices * static_cast<int64_t>(k);
     if (entries * 8 > kMaxSliceBytes) return DS_ERR_UNSUPPORTED;
@@ -273,6 +280,7 @@ int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t r
   sp.sorted_lists = pl.merge == DS_MERGE_LISTS ? 1 : 0;
   sp.presample = pl.presample ? 1 : 0;
   sp.group_shift = pl.order_group == 4 ? 2 : (pl.order_group == 2 ? 1 : 0);
+  sp.lockstep = pl.lockstep ? 1 : 0;
   return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }
 
@@ -338,25 +346,54 @@ int plan_with_workspace(int64_t rows, int64_t n, int k, int dtype, const ds_conf
   return DS_OK;
 }
 
-// Per-device workspace cache for ds_topk: grows on demand, freed at unload.
+// Workspace cache of ds_topk, one buffer per (device, stream): calls on one stream are
+// ordered by the stream, so they can share a buffer; calls on different streams never do.
+// A buffer that was handed out is never freed before unload (a graph captured on its
+// stream may still use it): when a stream needs more, the old buffer is retired and kept.
+// Growing calls hipMalloc, which is refused while the stream is being captured.
+struct WsBuf {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
 struct WsCache {
   std::mutex mu;
-  std::unordered_map<int, std::pair<void*, size_t>> bufs;
+  std::map<std::pair<int, uintptr_t>, WsBuf> bufs;
+  std::vector<std::pair<int, void*>> retired;
   ~WsCache() {
-    for (auto& kv : bufs) {
-      if (kv.second.first) {
-        int old = 0;
-        if (hipGetDevice(&old) == hipSuccess && hipSetDevice(kv.first) == hipSuccess) {
-          (void)hipFree(kv.second.first);
-          (void)hipSetDevice(old);
-        }
-      }
-    }
+    int old = 0;
+    if (hipGetDevice(&old) != hipSuccess) return;
+    auto release = [](int dev, void* p) {
+      if (p && hipSetDevice(dev) == hipSuccess) (void)hipFree(p);
+    };
+    for (auto& kv : bufs) release(kv.first.first, kv.second.ptr);
+    for (auto& r : retired) release(r.first, r.second);
+    (void)hipSetDevice(old);
   }
 };
 WsCache& ws_cache() {
-  static WsCache c;
-  return c;
+  static WsCache* c = new WsCache();  // never destroyed: the runtime may be gone at exit
+  return *c;
+}
+
+// The cached workspace of at least `bytes` for (current device, stream), or an error.
+int cached_workspace(size_t bytes, hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_DEVICE;
+  WsCache& c = ws_cache();
+  std::lock_guard<std::mutex> g(c.mu);
+  WsBuf& slot = c.bufs[{dev, reinterpret_cast<uintptr_t>(stream)}];
+  if (slot.bytes < bytes) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return DS_ERR_DEVICE;
+    if (cs != hipStreamCaptureStatusNone) return DS_ERR_WORKSPACE;  // no allocation under capture
+    void* ptr = nullptr;
+    if (hipMalloc(&ptr, bytes) != hipSuccess) return DS_ERR_LAUNCH;
+    if (slot.ptr) c.retired.emplace_back(dev, slot.ptr);
+    slot.ptr = ptr;
+    slot.bytes = bytes;
+  }
+  *out = slot.ptr;
+  return DS_OK;
 }
 
 }  // namespace
@@ -395,6 +432,7 @@ int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg
   out->presample = p.presample ? DS_PRESAMPLE_ON : DS_PRESAMPLE_OFF;
   out->order_group = p.order_group;
   out->merge = p.slices > 1 ? p.merge : DS_MERGE_AUTO;
+  out->schedule = p.lockstep ? DS_SCHEDULE_LOCKSTEP : DS_SCHEDULE_FREE;
   return DS_OK;
 }
 
@@ -460,23 +498,8 @@ int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, i
   if (st != DS_OK) return st;
   void* ws = nullptr;
   if (p.ws_bytes) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_DEVICE;
-    WsCache& c = ws_cache();
-    std::lock_guard<std::mutex> g(c.mu);
-    auto& slot = c.bufs[dev];
-    if (slot.second < p.ws_bytes) {
-      if (slot.first) {
-        (void)hipDeviceSynchronize();
-        (void)hipFree(slot.first);
-        slot = {nullptr, 0};
-      }
-      void* ptr = nullptr;
-      if (hipMalloc(&ptr, p.ws_bytes) != hipSuccess) return DS_ERR_LAUNCH;
-      slot = {ptr, p.ws_bytes};
-    }
-    ws = slot.first;
-    return run(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, nullptr, static_cast<hipStream_t>(stream));
+    st = cached_workspace(p.ws_bytes, static_cast<hipStream_t>(stream), &ws);
+    if (st != DS_OK) return st;
   }
   return run(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, nullptr, static_cast<hipStream_t>(stream));
 }

@@ -1,4 +1,6 @@
-// DeepSelect row-wise top-k: HIP kernels for gfx950 (CDNA4, 64-lane waves).
+#pragma once
+// DeepSelect row-wise top-k: HIP device code for gfx950 (CDNA4, 64-lane waves), shared by the
+// translation units that instantiate and launch it (ds_select.hip, ds_merge.hip).
 //
 // Method (DeepSelect design note, "Algorithm"): a threshold T, blocks of B elements read
 // once in a random order independent of the data, a filter that appends every element
@@ -37,6 +39,7 @@
 //    one wave ranks with lane reads. Survivors alternate between two k-entry sets, so
 //    nothing is copied back; appends always go to the region after the survivor set A. The
 //    final compaction can write its survivors sorted (a counting sort over its value bins).
+#include <atomic>
 #include <type_traits>
 
 #include "ds_internal.h"
@@ -337,7 +340,8 @@ constexpr uint32_t kListCap = 64;           // pivot-bin entries ranked with lan
 constexpr uint32_t kOrdCap = 1024;          // block-order table entries (longer streams compute it)
 
 struct Scalars {
-  uint32_t blk[3];             // entries appended by block i, at blk[i % 3]
+  uint32_t len;                // entries appended since the last compaction
+  uint32_t done;               // waves whose stream has ended (free-running schedule)
   uint32_t outpos;             // scatter cursor of the running compaction
   uint32_t listpos;            // pivot-list cursor of the running compaction
   uint32_t pub[6];             // bin scan result: bin, entries above it, entries in it, max key,
@@ -712,7 +716,7 @@ template <int WAVES, int DT, bool RAW>
 __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, bool fin, bool have_t,
                         uint32_t key_hi, uint32_t ilo, uint32_t ihi, Scalars& sc, uint32_t* hist2, uint32_t& hpar,
                         uint32_t& tkey, uint32_t& tidx, uint32_t& maxkey, uint32_t vlo_key, uint32_t vhi_key,
-                        bool vok, const OutSpec* so, bool& sorted) {
+                        bool vok, const OutSpec* so, bool& sorted, uint32_t* clear) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t n = sg.n0 + sg.n1;
@@ -920,6 +924,7 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
     }
     sorted = true;
   }
+  if (clear && tid == 0) *clear = 0;  // before the last barrier: no wave appends before it
   lds_sync();
   tkey = sc.pub[0];
   tidx = sc.pub[1];
@@ -1323,20 +1328,34 @@ struct BodyOut {
   bool sorted;           // the final compaction already wrote the sorted output
 };
 
+// Schedule. The design note checks the buffer once after each whole block ("lockstep":
+// a workgroup barrier after every block, then the check). By default the waves instead
+// stream independently: each wave filters its share of block after block, reserves buffer
+// space with one LDS atomic, and checks the buffer length itself (from the atomic's
+// return, or by reading it when it had no hits). A wave that sees the length at or past
+// k + B2 stops at a barrier; the other waves stop there at their next check, and a wave
+// that has no blocks left waits there. After the barrier every wave reads the same
+// length, and they compact together (or, once every wave is done, run the final
+// compaction). A wave appends at most one more share of a block after the length crosses
+// k + B2 (it checks after every share), so the buffer never exceeds k + B2 + B - 1 entries,
+// the design note's bound. The threshold only changes at compactions, so a wave always
+// filters with the workgroup's current threshold.
+//
 // D buffers of CPW chunks per wave are in flight: block i+D is loaded into the registers of
 // block i as soon as block i has been filtered. The loop body handles D blocks with D
 // separate buffers and has no exit, so the compiler sees which loads are the older ones and
 // waits only for those.
-template <int DT, int WAVES, int CPW, int D, bool MERGE>
+template <int DT, int WAVES, int CPW, int D, bool MERGE, bool STATS>
 __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amdgpu_buffer_rsrc_t rs, uint32_t len,
                                                 uint32_t idx_base, uint32_t k, uint32_t B2, const BlockOrder& ord,
-                                                uint32_t ilo, uint32_t ihi, bool stats, bool presample, uint32_t gshift,
-                                                const OutSpec* fso, BodyOut& out) {
+                                                uint32_t ilo, uint32_t ihi, bool lockstep, bool presample,
+                                                uint32_t gshift, const OutSpec* fso, BodyOut& out) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t IB = MERGE ? 8 : (DT == DS_BF16 ? 2 : 4);  // bytes per item
   constexpr uint32_t VEC = 16 / IB;                            // items per lane per chunk
   constexpr uint32_t CHUNK = 64 * VEC;
   constexpr uint32_t B = WAVES * CPW * CHUNK;
+  constexpr uint32_t SHARE = CPW * CHUNK;  // items of one block that one wave filters
   constexpr uint32_t key_hi = DT == DS_BF16 ? 0xFFFFu : 0xFFFFFFFFu;  // largest possible key
   static_assert(D >= 2 && D <= 4, "two to four buffers");
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
@@ -1357,10 +1376,10 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     return b < m ? b : m;
   };
 
-  // threshold state (uniform across the workgroup)
+  // threshold state (uniform across the workgroup; it changes only at compactions)
   uint32_t mode = 0, thr_s = ~0u, thr_n = ~0u;  // mode 0: accept everything (no threshold yet)
   uint32_t t_key = 0, t_idx = 0, maxkey = 0;
-  uint32_t nsurv = 0, napp = 0, hpar = 0, b3 = 0;
+  uint32_t nsurv = 0, hpar = 0;
   bool sur_a = false;  // survivors in set A (else set B)
   // key range of the entries appended before the first compaction (the select kernel tracks
   // it; the merge kernel does not)
@@ -1370,8 +1389,8 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   // block's largest key, the value-bin window of the first compaction
   bool presampled = false;
   uint32_t pre_hi = 0;
-  const bool st0 = stats && tid == 0;  // the thread that keeps the counters in sc.st_*
-  uint64_t t_mark = 0;
+  [[maybe_unused]] const bool st0 = STATS && tid == 0;  // the thread that keeps the counters in sc.st_*
+  [[maybe_unused]] uint64_t t_mark = 0;
   uint64_t my_reads = 0, my_jsum = 0;
 
   auto addr = [&](uint32_t bid, uint32_t t) -> uint32_t {
@@ -1388,7 +1407,10 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   }
 
   bool sorted = false;
-  auto compaction = [&](bool fin) {
+  // A compaction of the nsurv survivors and the napp entries appended since the last one.
+  // In-loop calls clear the append counter before their last barrier, so no wave can
+  // append before it is cleared.
+  auto compaction = [&](uint32_t napp, bool fin) {
     const Segs sg = nsurv ? make_segs(sur_a ? L.ck : L.bk, sur_a ? L.ci : L.bi, nsurv, L.ck + L.k4, L.ci + L.k4, napp)
                           : make_segs(nullptr, nullptr, 0u, L.ck, L.ci, napp);
     const bool to_a = nsurv != 0 && !sur_a;  // first compaction: entries start in A, go to B
@@ -1408,13 +1430,52 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
       }
       vok = range_ok;
     }
-    compact<WAVES, DT, !MERGE>(sg, to_a ? L.ck : L.bk, to_a ? L.ci : L.bi, k, fin, nsurv != 0, key_hi, ilo, ihi, sc,
-                               L.hist, hpar, t_key, t_idx, maxkey, vlo, vhi, vok, fin ? fso : nullptr, sorted);
-    if (st0) {
-      sc.st_a += napp;
-      sc.st_w += nsurv + napp;
+    if constexpr (STATS) {
+      if (st0) {
+        sc.st_a += napp;
+        sc.st_w += nsurv + napp;
+        sc.st_max = max(sc.st_max, static_cast<unsigned long long>(nsurv + napp));
+      }
     }
+    compact<WAVES, DT, !MERGE>(sg, to_a ? L.ck : L.bk, to_a ? L.ci : L.bi, k, fin, nsurv != 0, key_hi, ilo, ihi, sc,
+                               L.hist, hpar, t_key, t_idx, maxkey, vlo, vhi, vok, fin ? fso : nullptr, sorted,
+                               fin ? nullptr : &sc.len);
     sur_a = to_a;
+  };
+
+  // In-loop compaction (every wave calls it at the same barrier count), then the new filter.
+  auto in_loop = [&](uint32_t napp) {
+    [[maybe_unused]] const uint64_t prev_c = comp_of(t_key, t_idx);
+    [[maybe_unused]] const bool had_t = nsurv != 0;
+    if constexpr (STATS) {
+      if (st0) t_mark = wall_clock64();
+    }
+    compaction(napp, false);
+    if constexpr (STATS) {
+      if (st0) {
+        sc.st_tc += wall_clock64() - t_mark;
+        sc.st_r += 1;
+        if (had_t && comp_of(t_key, t_idx) < prev_c) sc.st_mono = 0;
+      }
+    }
+    nsurv = k;
+    if constexpr (!MERGE)
+      filter_thresholds<DT>(t_key, mode, thr_s, thr_n);
+    else
+      mode = 1;
+  };
+
+  // The stop of a free-running wave that saw the buffer at or past k + B2: one barrier, then
+  // the compaction every other wave joins (the length cannot shrink before it).
+  auto stop_and_compact = [&]() {
+    if constexpr (STATS) {
+      if (st0) t_mark = wall_clock64();
+    }
+    lds_sync();
+    if constexpr (STATS) {
+      if (st0) sc.st_ts += wall_clock64() - t_mark;
+    }
+    in_loop(sc.len);
   };
 
   // Threshold from the first (whole) block instead of "accept everything", from each lane's
@@ -1451,17 +1512,33 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     mode = 1;
   };
 
-  // Filter block `bid` (the i-th in the order) from `buf`, refill `buf` with block i+D, sync,
-  // and compact when the buffer is full.
+  // Reserves `cnt` buffer entries for this wave (one LDS atomic); returns the first slot
+  // (relative to the append region) and the length after this reservation in `seen`.
+  auto reserve = [&](uint32_t cnt, uint32_t& seen) -> uint32_t {
+    uint32_t pos = 0;
+    if (lane == 0) pos = atomicAdd(&sc.len, cnt);
+    pos = uni(pos);
+    seen = pos + cnt;
+    return pos;
+  };
+
+  // Filter block `bid` (the i-th in the order) from `buf`, refill `buf` with block i+D, and
+  // check the buffer.
   auto process = [&](u32x4(&bf)[CPW], uint32_t& bid_ref, uint32_t i) {
     const uint32_t bid = bid_ref;
     const uint32_t blk_lo = bid * B;
     // the id of block i+D, read now: read after the filter's LDS stores, its wait would also
     // wait for those stores and hold back the refill
     const uint32_t next_bid = bid_of(i + D);
-    const uint32_t abase = (nsurv ? L.k4 : 0u) + napp;  // append position of this block's first entry
-    const uint32_t nxt = (b3 == 2 ? 0u : b3 + 1u);
-    bool accept_all = false;  // every element of the (whole) block was appended
+    const uint32_t app0 = nsurv ? L.k4 : 0u;  // the append region
+    // The stream length as a value the optimizer cannot reason about: with the counters
+    // compiled in, clang (ROCm 7.2) dropped the length check of all but the last chunk of a
+    // share, so zero padding past the end was appended (measured); an empty asm on the
+    // uniform value keeps every check.
+    uint32_t len_opaque = len;
+    asm volatile("" : "+s"(len_opaque));
+    uint32_t seen = 0;                        // buffer length after this wave's last reservation
+    bool reserved = false;
     if constexpr (!MERGE) {
       uint32_t s[CPW][VEC];  // the block's scores (bf16: the element in bits 16-31)
 #pragma unroll
@@ -1477,7 +1554,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
           for (uint32_t q = 0; q < 4; ++q) s[t][q] = bf[t][q];
         }
       }
-      if (stats) {
+      if constexpr (STATS) {
 #pragma unroll
         for (uint32_t t = 0; t < CPW; ++t) {
           const uint32_t first = blk_lo + (wave + t * WAVES) * CHUNK + lane * VEC;
@@ -1490,7 +1567,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
         // each lane's maximum over its elements of this block and, on short streams (fewer
         // than 8 blocks) when it is a whole block too, of the second block read (already in
         // flight in buf[1]): a tighter T0 where the final compaction dominates; long streams
-        // do not wait for the second block (measured slower there)
+        // do not wait for it
         uint32_t lmax = 0;
 #pragma unroll
         for (uint32_t t = 0; t < CPW; ++t) {
@@ -1518,11 +1595,9 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
       const bool strict = idx_base + blk_lo > t_idx;
       const uint32_t thr = strict ? thr_s : thr_n;
       if (mode == 0 && blk_lo + B <= len) {
-        // accept everything: each wave stores its chunks (raw) contiguously, in wave order
-        constexpr uint32_t tot = CPW * CHUNK;
-        const uint32_t pos = abase + wave * tot;
-        accept_all = true;
-        if (tid == 0) sc.blk[nxt] = 0;
+        // accept everything: each wave stores its chunks (raw) contiguously
+        const uint32_t pos = app0 + reserve(SHARE, seen);
+        reserved = true;
         uint32_t kmn = ~0u, kmx = 0;
 #pragma unroll
         for (uint32_t t = 0; t < CPW; ++t) {
@@ -1576,11 +1651,9 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
 #pragma unroll
             for (uint32_t e = 0; e < VEC; ++e) h[e] = s[t][e] < thr;
           }
-          if (blk_lo + (wave + t * WAVES) * CHUNK + CHUNK > len) {  // the stream's tail chunk
-            const uint32_t nval = first >= len ? 0u : min(VEC, len - first);
+          // elements past the stream's end (the tail chunk, or no chunk at all) never hit
 #pragma unroll
-            for (uint32_t e = 0; e < VEC; ++e) h[e] = h[e] && e < nval;
-          }
+          for (uint32_t e = 0; e < VEC; ++e) h[e] = h[e] && first + e < len_opaque;
           if (mode == 0) {
 #pragma unroll
             for (uint32_t e = 0; e < VEC; ++e) {
@@ -1597,9 +1670,8 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
             tot += popc(mk[e]);
           }
           if (tot) {
-            uint32_t pos = 0;
-            if (lane == 0) pos = atomicAdd(&sc.blk[b3], tot);
-            pos = uni(pos) + abase;
+            uint32_t pos = app0 + reserve(tot, seen);
+            reserved = true;
             const uint32_t j0 = idx_base + first;
 #pragma unroll
             for (uint32_t e = 0; e < VEC; ++e) {
@@ -1614,7 +1686,6 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
             }
           }
         }
-        if (tid == 0) sc.blk[nxt] = 0;
         if (mode == 0) {
           rmin_w = min(rmin_w, wave_min32(kmn));
           rmax_w = max(rmax_w, wave_max32(kmx));
@@ -1642,16 +1713,14 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
         for (uint32_t e = 0; e < 2; ++e) {
           const uint32_t key = bf[t][2 * e], id = bf[t][2 * e + 1];
           const bool beats = mode == 0 || key > t_key || (key == t_key && id < t_idx);
-          h[t][e] = beats && first + e < len;
+          h[t][e] = beats && first + e < len_opaque;
           mk[t][e] = ballot(h[t][e]);
           tot += popc(mk[t][e]);
         }
       }
-      uint32_t pos = 0;
-      if (lane == 0 && tot) pos = atomicAdd(&sc.blk[b3], tot);
-      pos = uni(pos) + abase;
-      if (tid == 0) sc.blk[nxt] = 0;
       if (tot) {
+        uint32_t pos = app0 + reserve(tot, seen);
+        reserved = true;
 #pragma unroll
         for (uint32_t t = 0; t < CPW; ++t) {
 #pragma unroll
@@ -1674,28 +1743,27 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
 #pragma unroll
     for (uint32_t t = 0; t < CPW; ++t) bf[t] = load16(rs, addr(bid_ref, t));
 
-    if (st0) t_mark = wall_clock64();
-    lds_sync();
-    if (st0) sc.st_ts += wall_clock64() - t_mark;
-    napp += accept_all ? B : sc.blk[b3];
-    b3 = nxt;
-    if (st0) sc.st_max = max(sc.st_max, static_cast<unsigned long long>(nsurv + napp));
-    if (nsurv + napp >= k + B2) {
-      const uint64_t prev_c = comp_of(t_key, t_idx);
-      const bool had_t = nsurv != 0;
-      if (st0) t_mark = wall_clock64();
-      compaction(false);
-      if (st0) {
-        sc.st_tc += wall_clock64() - t_mark;
-        sc.st_r += 1;
-        if (had_t && comp_of(t_key, t_idx) < prev_c) sc.st_mono = 0;
+    if (lockstep) {
+      // the design note's schedule: every wave has appended its share of the block, then the
+      // check; a second barrier keeps the length still until every wave has read it
+      if constexpr (STATS) {
+        if (st0) t_mark = wall_clock64();
       }
-      nsurv = k;
-      napp = 0;
-      if constexpr (!MERGE)
-        filter_thresholds<DT>(t_key, mode, thr_s, thr_n);
+      lds_sync();
+      if constexpr (STATS) {
+        if (st0) sc.st_ts += wall_clock64() - t_mark;
+      }
+      const uint32_t napp = sc.len;
+      if constexpr (STATS) {
+        if (st0) sc.st_max = max(sc.st_max, static_cast<unsigned long long>(nsurv + napp));
+      }
+      if (nsurv + napp >= k + B2)
+        in_loop(napp);
       else
-        mode = 1;
+        lds_sync();
+    } else {
+      if (!reserved) seen = uni(__atomic_load_n(lds_ptr(&sc.len), __ATOMIC_RELAXED));
+      if (nsurv + seen >= k + B2) stop_and_compact();
     }
   };
 
@@ -1707,9 +1775,26 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     if constexpr (D >= 4) process(buf[3], bids[3], i + 3);
   }
 
+  // The end of this wave's stream. Free-running waves wait until every wave is done; a
+  // wave that stopped for a compaction meanwhile brings the others into it.
+  uint32_t napp;
+  if (lockstep) {
+    napp = sc.len;  // every append happened before the last barrier
+  } else {
+    if (lane == 0) atomicAdd(&sc.done, 1u);
+    for (;;) {
+      lds_sync();
+      napp = sc.len;
+      if (sc.done == WAVES) break;
+      in_loop(napp);
+    }
+  }
+
   // final compaction
-  if (st0) sc.st_tf = wall_clock64();
-  compaction(true);
+  if constexpr (STATS) {
+    if (st0) sc.st_tf = wall_clock64();
+  }
+  compaction(napp, true);
   out.fk = sur_a ? L.ck : L.bk;
   out.fi = sur_a ? L.ci : L.bi;
   out.reads = my_reads;
@@ -1717,12 +1802,12 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   out.sorted = sorted;
 }
 
-// Blocks in flight per wave (each CPW 16-byte chunks per lane): two for 16 waves (deeper
-// prefetch in 16-wave workgroups measured slower), four for smaller workgroups.
+// Blocks in flight per wave (each CPW 16-byte chunks per lane): two for 16 waves, four for
+// smaller workgroups.
 constexpr int depth_for(int waves) { return waves < 16 ? 4 : 2; }
 
 // --------------------------------------------------------------------------- select kernel
-template <int DT, int WAVES, int CPW>
+template <int DT, int WAVES, int CPW, bool STATS>
 __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t EB = DT == DS_BF16 ? 2 : 4;
@@ -1731,28 +1816,30 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   __shared__ Scalars sc;
 
-  const uint32_t tid = threadIdx.x, lane = tid & 63u;
+  const uint32_t tid = threadIdx.x;
   // a row's slices run on one XCD, where the merge of their lists reads them from L2
   uint32_t row, slice;
   xcd_unit(blockIdx.x, static_cast<uint32_t>(p.slices), gridDim.x / static_cast<uint32_t>(p.slices), row, slice);
-  const uint32_t wg_item = row * static_cast<uint32_t>(p.slices) + slice;  // (row, slice) in row-major order
   const uint32_t slice_lo = slice * static_cast<uint32_t>(p.slice_len);
   const uint32_t len = static_cast<uint32_t>(min(p.slice_len, p.n - static_cast<int64_t>(slice_lo)));
   const uint32_t m = (len + B - 1) / B;
   const uint32_t k = static_cast<uint32_t>(p.k);
   const uint32_t B2 = static_cast<uint32_t>(p.slack);
-  const bool stats = p.stats != nullptr;
-  const uint64_t t_start = stats ? wall_clock64() : 0;
+  [[maybe_unused]] uint64_t t_start = 0;
+  if constexpr (STATS) t_start = wall_clock64();
 
   const Lay L = lay_of(lds, k, B2, B);
   for (uint32_t i = 4u * tid; i < 2u * kBins; i += 4u * NT) *reinterpret_cast<uint4*>(L.hist + i) = make_uint4(0, 0, 0, 0);
   if (tid == 0) {
-    sc.blk[0] = sc.blk[1] = sc.blk[2] = 0;
-    sc.st_a = sc.st_r = sc.st_w = sc.st_max = sc.st_tc = sc.st_ts = sc.st_tf = 0;
-    sc.st_mono = 1;
+    sc.len = 0;
+    sc.done = 0;
     sc.st_p = 0;
-    sc.reads = 0;
-    sc.index_sum = 0;
+    if constexpr (STATS) {
+      sc.st_a = sc.st_r = sc.st_w = sc.st_max = sc.st_tc = sc.st_ts = sc.st_tf = 0;
+      sc.st_mono = 1;
+      sc.reads = 0;
+      sc.index_sum = 0;
+    }
   }
 
   const uint8_t* base = p.x + static_cast<uint64_t>(row) * p.row_stride_bytes + static_cast<uint64_t>(slice_lo) * EB;
@@ -1772,11 +1859,13 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   const bool own_sort = p.slices == 1 || p.sorted_lists;
 
   BodyOut bo;
-  deepselect_body<DT, WAVES, CPW, depth_for(WAVES), false>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
-                                                            slice_lo + len - 1u, stats, p.presample != 0, gshift,
-                                                            own_sort ? &fso : nullptr, bo);
+  deepselect_body<DT, WAVES, CPW, depth_for(WAVES), false, STATS>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
+                                                                   slice_lo + len - 1u, p.lockstep != 0,
+                                                                   p.presample != 0, gshift,
+                                                                   own_sort ? &fso : nullptr, bo);
 
-  if (stats) {
+  if constexpr (STATS) {
+    const uint32_t lane = tid & 63u;
     uint64_t my_reads = bo.reads, my_jsum = bo.jsum;
     for (uint32_t o = 32; o > 0; o >>= 1) {
       my_reads += __shfl_xor(my_reads, o);
@@ -1788,7 +1877,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
     }
     lds_sync();
     if (tid == 0) {
-      ds_stats* o = p.stats + wg_item;
+      ds_stats* o = p.stats + (row * static_cast<uint32_t>(p.slices) + slice);
       o->appended = sc.st_a;
       o->compactions = sc.st_r;
       o->work = sc.st_w;
@@ -1820,10 +1909,13 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k, nullptr,
                               nullptr, rws + slice * k, 0);
   }
-  if (stats && tid == 0) {
-    const uint64_t t_end = wall_clock64();
-    p.stats[wg_item].t_total_ns = (t_end - t_start) * 10;
-    p.stats[wg_item].t_final_ns = (t_end - sc.st_tf) * 10;
+  if constexpr (STATS) {
+    if (tid == 0) {
+      const uint64_t t_end = wall_clock64();
+      ds_stats* o = p.stats + (row * static_cast<uint32_t>(p.slices) + slice);
+      o->t_total_ns = (t_end - t_start) * 10;
+      o->t_final_ns = (t_end - sc.st_tf) * 10;
+    }
   }
 }
 
@@ -1847,7 +1939,8 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   const Lay L = lay_of(lds, k, B2, B);
   for (uint32_t i = 4u * tid; i < 2u * kBins; i += 4u * NT) *reinterpret_cast<uint4*>(L.hist + i) = make_uint4(0, 0, 0, 0);
   if (tid == 0) {
-    sc.blk[0] = sc.blk[1] = sc.blk[2] = 0;
+    sc.len = 0;
+    sc.done = 0;
     sc.st_p = 0;
   }
   const uint2* base = p.ws + static_cast<uint64_t>(row) * p.row_entries;  // rows padded to 16 bytes
@@ -1858,9 +1951,9 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
 
   const OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
   BodyOut bo;
-  deepselect_body<DT, WAVES, CPW, depth_for(WAVES), true>(L, sc, rs, len, 0u, k, B2, ord, 0u,
-                                                           static_cast<uint32_t>(p.n - 1), false, p.presample != 0, 0u,
-                                                           &fso, bo);
+  deepselect_body<DT, WAVES, CPW, depth_for(WAVES), true, false>(L, sc, rs, len, 0u, k, B2, ord, 0u,
+                                                                  static_cast<uint32_t>(p.n - 1), false,
+                                                                  p.presample != 0, 0u, &fso, bo);
   if (!bo.sorted)
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
                               p.out_vals, p.out_idx, nullptr, row);
@@ -1894,179 +1987,28 @@ __global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(MergeParams p) 
                                  l0, min(l0 + per, gl));
 }
 
-// --------------------------------------------------------------------------- probes
-constexpr uint32_t kProbeThreads = 256;
-constexpr uint32_t kProbeUnroll = 4;
-constexpr uint32_t kProbeTile = kProbeThreads * 16 * kProbeUnroll;  // bytes per workgroup step
-
-__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4* src, int64_t vecs, uint32_t* sink) {
-  uint32_t acc = 0;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kProbeThreads * kProbeUnroll;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kProbeThreads * kProbeUnroll + threadIdx.x; i < vecs;
-       i += stride) {
-    u32x4 r[kProbeUnroll];
-#pragma unroll
-    for (uint32_t u = 0; u < kProbeUnroll; ++u) {
-      const int64_t j = i + u * kProbeThreads;
-      r[u] = j < vecs ? src[j] : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (uint32_t u = 0; u < kProbeUnroll; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
-  }
-  for (uint32_t o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
-  __shared__ uint32_t part[kProbeThreads / 64];
-  if ((threadIdx.x & 63u) == 0) part[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t a = 0;
-    for (uint32_t w = 0; w < kProbeThreads / 64; ++w) a ^= part[w];
-    sink[blockIdx.x] = a;
-  }
-}
-
-__global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(u32x4* dst, const u32x4* src, int64_t vecs) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kProbeThreads * kProbeUnroll;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kProbeThreads * kProbeUnroll + threadIdx.x; i < vecs;
-       i += stride) {
-    u32x4 r[kProbeUnroll];
-#pragma unroll
-    for (uint32_t u = 0; u < kProbeUnroll; ++u) {
-      const int64_t j = i + u * kProbeThreads;
-      if (j < vecs) r[u] = src[j];
-    }
-#pragma unroll
-    for (uint32_t u = 0; u < kProbeUnroll; ++u) {
-      const int64_t j = i + u * kProbeThreads;
-      if (j < vecs) dst[j] = r[u];
+// Raises kernel KERN's dynamic-LDS limit to at least `lds` bytes on the current device. The
+// attribute is set only when a larger size than before is asked for on that device, so the
+// runtime call stays off the steady-state launch path.
+constexpr int kAttrDevices = 64;
+template <auto KERN>
+hipError_t allow_lds(size_t lds) {
+  static std::atomic<int> granted[kAttrDevices];  // zero-initialised: nothing granted yet
+  if (lds <= 65536) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kAttrDevices && granted[dev].load(std::memory_order_relaxed) >= static_cast<int>(lds))
+    return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(KERN), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(lds));
+  if (e == hipSuccess && dev >= 0 && dev < kAttrDevices) {
+    int cur = granted[dev].load(std::memory_order_relaxed);
+    while (cur < static_cast<int>(lds) && !granted[dev].compare_exchange_weak(cur, static_cast<int>(lds))) {
     }
   }
-}
-
-template <int DT, int W, int C>
-hipError_t launch_select_shape(const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream) {
-  auto kern = select_kernel<DT, W, C>;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(rows * p.slices)), dim3(W * 64), lds, stream, p);
-  return hipGetLastError();
-}
-
-template <int DT>
-hipError_t launch_select_dt(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t s) {
-  switch (shape) {
-    case 0: return launch_select_shape<DT, 2, 1>(p, rows, lds, s);
-    case 1: return launch_select_shape<DT, 4, 1>(p, rows, lds, s);
-    case 2: return launch_select_shape<DT, 4, 2>(p, rows, lds, s);
-    case 3: return launch_select_shape<DT, 8, 1>(p, rows, lds, s);
-    case 4: return launch_select_shape<DT, 8, 2>(p, rows, lds, s);
-    case 5: return launch_select_shape<DT, 4, 4>(p, rows, lds, s);
-    case 6: return launch_select_shape<DT, 8, 4>(p, rows, lds, s);
-    case 7: return launch_select_shape<DT, 16, 1>(p, rows, lds, s);
-    case 8: return launch_select_shape<DT, 16, 2>(p, rows, lds, s);
-    case 9: return launch_select_shape<DT, 16, 4>(p, rows, lds, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-// Rows per list-merge launch (the grid's z dimension; a multiple of 8, see xcd_unit).
-constexpr int64_t kMaxGridRows = 65528;
-
-// One instantiation per bound on the lists merged together.
-template <int DT, uint32_t MAXS>
-hipError_t launch_merge_lists_t(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
-  auto kern = merge_lists_kernel<DT, kListMergeWaves, MAXS>;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  const int64_t G = p.group, wpg = (G + p.per_wg - 1) / p.per_wg, groups = (p.lists + G - 1) / G;
-  MergeParams q = p;
-  q.pk = (p.k + p.group - 1) / p.group;
-  for (int64_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
-    q.row0 = r0;
-    const int64_t nr = rows - r0 < kMaxGridRows ? rows - r0 : kMaxGridRows;
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(wpg), static_cast<uint32_t>(groups), static_cast<uint32_t>(nr)),
-                       dim3(kListMergeWaves * 64), lds, stream, q);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-template <int DT>
-hipError_t launch_merge_lists_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
-  const int32_t g = p.group < p.lists ? p.group : p.lists;
-  if (g <= 2) return launch_merge_lists_t<DT, 2>(p, rows, lds, stream);
-  if (g <= 4) return launch_merge_lists_t<DT, 4>(p, rows, lds, stream);
-  if (g <= 8) return launch_merge_lists_t<DT, 8>(p, rows, lds, stream);
-  static_assert(kMaxListGroup == 16, "instantiations cover groups up to kMaxListGroup");
-  return launch_merge_lists_t<DT, kMaxListGroup>(p, rows, lds, stream);
-}
-
-template <int DT>
-hipError_t launch_merge_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
-  constexpr int W = kMergeShape.waves, C = kMergeShape.cpw;
-  auto kern = merge_kernel<DT, W, C>;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(rows)), dim3(W * 64), lds, stream, p);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace
-
-size_t select_scalars_bytes() { return sizeof(Scalars); }
-
-size_t select_lds_bytes(int k, int block, int slack, int waves) {
-  (void)waves;
-  const size_t k4 = round4(static_cast<uint32_t>(k)), pc = round4(static_cast<uint32_t>(slack + block));
-  return (2 * (k4 + pc) + 2 * k4 + 2 * kBins + kOrdCap) * 4 + sizeof(Scalars);
-}
-
-hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,
-                         hipStream_t stream) {
-  const size_t dyn = lds_bytes - sizeof(Scalars);
-  return dtype == DS_BF16 ? launch_select_dt<DS_BF16>(shape_index, p, rows, dyn, stream)
-                          : launch_select_dt<DS_FP32>(shape_index, p, rows, dyn, stream);
-}
-
-hipError_t launch_merge_lists(int dtype, const MergeParams& p, int64_t rows, hipStream_t stream) {
-  const size_t lds =
-      static_cast<size_t>(p.group < p.lists ? p.group : p.lists) * static_cast<size_t>(p.k) * 8 + kMaxListGroup * 4;
-  return dtype == DS_BF16 ? launch_merge_lists_dt<DS_BF16>(p, rows, lds, stream)
-                          : launch_merge_lists_dt<DS_FP32>(p, rows, lds, stream);
-}
-
-hipError_t launch_merge(int dtype, const MergeParams& p, int64_t rows, size_t lds_bytes, hipStream_t stream) {
-  const size_t dyn = lds_bytes - sizeof(Scalars);
-  return dtype == DS_BF16 ? launch_merge_dt<DS_BF16>(p, rows, dyn, stream)
-                          : launch_merge_dt<DS_FP32>(p, rows, dyn, stream);
-}
-
-int64_t probe_read_groups(int64_t bytes) {
-  int64_t g = (bytes + kProbeTile - 1) / kProbeTile;
-  return g < 1 ? 1 : (g > 4096 ? 4096 : g);
-}
-
-hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
-  const int64_t g = probe_read_groups(bytes);
-  hipLaunchKernelGGL(probe_read_kernel, dim3(static_cast<uint32_t>(g)), dim3(kProbeThreads), 0, stream,
-                     static_cast<const u32x4*>(src), bytes / 16, sink);
-  return hipGetLastError();
-}
-
-hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
-  const int64_t g = probe_read_groups(bytes);
-  hipLaunchKernelGGL(probe_copy_kernel, dim3(static_cast<uint32_t>(g)), dim3(kProbeThreads), 0, stream,
-                     static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), bytes / 16);
-  return hipGetLastError();
-}
-
 }  // namespace ds

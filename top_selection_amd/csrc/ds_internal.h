@@ -30,6 +30,7 @@ struct SelectParams {
   int32_t sorted_lists;      // slices > 1: store each slice's survivors sorted (for the list merge)
   int32_t presample;         // nonzero: the first whole block sets a presampled threshold
   int32_t group_shift;       // log2 of G: the block order is random over groups of G blocks
+  int32_t lockstep;          // nonzero: a barrier and the buffer check after every block
 };
 
 // The merge of split rows. The merge kernel: one workgroup per row runs DeepSelect over the
@@ -81,6 +82,13 @@ size_t select_scalars_bytes();
 constexpr uint32_t kMaxListGroup = 16;
 constexpr int64_t kListMergeLds = 128 * 1024;
 constexpr int kListMergeWaves = 8;
+
+// The select-kernel launcher of one element type and counter mode (one object each).
+#define DS_SELECT_PART_NAME(dt, st) launch_select_part_##dt##_##st
+hipError_t DS_SELECT_PART_NAME(0, 0)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream);
+hipError_t DS_SELECT_PART_NAME(0, 1)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream);
+hipError_t DS_SELECT_PART_NAME(1, 0)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream);
+hipError_t DS_SELECT_PART_NAME(1, 1)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream);
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,

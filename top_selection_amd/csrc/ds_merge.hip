@@ -1,0 +1,157 @@
+// Merge-kernel and list-merge instantiations, the probes, and the launch entry points the
+// C-ABI layer calls (the select kernels live in the ds_select.hip objects).
+#include "ds_device.h"
+
+namespace ds {
+namespace {
+
+// --------------------------------------------------------------------------- probes
+constexpr uint32_t kProbeThreads = 256;
+constexpr uint32_t kProbeUnroll = 4;
+constexpr uint32_t kProbeTile = kProbeThreads * 16 * kProbeUnroll;  // bytes per workgroup step
+
+__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4* src, int64_t vecs, uint32_t* sink) {
+  uint32_t acc = 0;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kProbeThreads * kProbeUnroll;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kProbeThreads * kProbeUnroll + threadIdx.x; i < vecs;
+       i += stride) {
+    u32x4 r[kProbeUnroll];
+#pragma unroll
+    for (uint32_t u = 0; u < kProbeUnroll; ++u) {
+      const int64_t j = i + u * kProbeThreads;
+      r[u] = j < vecs ? src[j] : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kProbeUnroll; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+  }
+  for (uint32_t o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  __shared__ uint32_t part[kProbeThreads / 64];
+  if ((threadIdx.x & 63u) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0;
+    for (uint32_t w = 0; w < kProbeThreads / 64; ++w) a ^= part[w];
+    sink[blockIdx.x] = a;
+  }
+}
+
+__global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(u32x4* dst, const u32x4* src, int64_t vecs) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kProbeThreads * kProbeUnroll;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kProbeThreads * kProbeUnroll + threadIdx.x; i < vecs;
+       i += stride) {
+    u32x4 r[kProbeUnroll];
+#pragma unroll
+    for (uint32_t u = 0; u < kProbeUnroll; ++u) {
+      const int64_t j = i + u * kProbeThreads;
+      if (j < vecs) r[u] = src[j];
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kProbeUnroll; ++u) {
+      const int64_t j = i + u * kProbeThreads;
+      if (j < vecs) dst[j] = r[u];
+    }
+  }
+}
+
+// Rows per list-merge launch (the grid's z dimension; a multiple of 8, see xcd_unit).
+constexpr int64_t kMaxGridRows = 65528;
+
+// One instantiation per bound on the lists merged together.
+template <int DT, uint32_t MAXS>
+hipError_t launch_merge_lists_t(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
+  auto kern = merge_lists_kernel<DT, kListMergeWaves, MAXS>;
+  {
+    const hipError_t e = allow_lds<merge_lists_kernel<DT, kListMergeWaves, MAXS>>(lds);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t G = p.group, wpg = (G + p.per_wg - 1) / p.per_wg, groups = (p.lists + G - 1) / G;
+  MergeParams q = p;
+  q.pk = (p.k + p.group - 1) / p.group;
+  for (int64_t r0 = 0; r0 < rows; r0 += kMaxGridRows) {
+    q.row0 = r0;
+    const int64_t nr = rows - r0 < kMaxGridRows ? rows - r0 : kMaxGridRows;
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(wpg), static_cast<uint32_t>(groups), static_cast<uint32_t>(nr)),
+                       dim3(kListMergeWaves * 64), lds, stream, q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int DT>
+hipError_t launch_merge_lists_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
+  const int32_t g = p.group < p.lists ? p.group : p.lists;
+  if (g <= 2) return launch_merge_lists_t<DT, 2>(p, rows, lds, stream);
+  if (g <= 4) return launch_merge_lists_t<DT, 4>(p, rows, lds, stream);
+  if (g <= 8) return launch_merge_lists_t<DT, 8>(p, rows, lds, stream);
+  static_assert(kMaxListGroup == 16, "instantiations cover groups up to kMaxListGroup");
+  return launch_merge_lists_t<DT, kMaxListGroup>(p, rows, lds, stream);
+}
+
+template <int DT>
+hipError_t launch_merge_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
+  constexpr int W = kMergeShape.waves, C = kMergeShape.cpw;
+  auto kern = merge_kernel<DT, W, C>;
+  {
+    const hipError_t e = allow_lds<merge_kernel<DT, W, C>>(lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(rows)), dim3(W * 64), lds, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t select_scalars_bytes() { return sizeof(Scalars); }
+
+size_t select_lds_bytes(int k, int block, int slack, int waves) {
+  (void)waves;
+  const size_t k4 = round4(static_cast<uint32_t>(k)), pc = round4(static_cast<uint32_t>(slack + block));
+  return (2 * (k4 + pc) + 2 * k4 + 2 * kBins + kOrdCap) * 4 + sizeof(Scalars);
+}
+
+// The counters are a separate instantiation (its own object), so the kernel that runs
+// without them carries no counter code.
+hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,
+                         hipStream_t stream) {
+  const size_t dyn = lds_bytes - sizeof(Scalars);
+  if (dtype == DS_BF16)
+    return p.stats ? DS_SELECT_PART_NAME(0, 1)(shape_index, p, rows, dyn, stream)
+                   : DS_SELECT_PART_NAME(0, 0)(shape_index, p, rows, dyn, stream);
+  return p.stats ? DS_SELECT_PART_NAME(1, 1)(shape_index, p, rows, dyn, stream)
+                 : DS_SELECT_PART_NAME(1, 0)(shape_index, p, rows, dyn, stream);
+}
+
+hipError_t launch_merge_lists(int dtype, const MergeParams& p, int64_t rows, hipStream_t stream) {
+  const size_t lds =
+      static_cast<size_t>(p.group < p.lists ? p.group : p.lists) * static_cast<size_t>(p.k) * 8 + kMaxListGroup * 4;
+  return dtype == DS_BF16 ? launch_merge_lists_dt<DS_BF16>(p, rows, lds, stream)
+                          : launch_merge_lists_dt<DS_FP32>(p, rows, lds, stream);
+}
+
+hipError_t launch_merge(int dtype, const MergeParams& p, int64_t rows, size_t lds_bytes, hipStream_t stream) {
+  const size_t dyn = lds_bytes - sizeof(Scalars);
+  return dtype == DS_BF16 ? launch_merge_dt<DS_BF16>(p, rows, dyn, stream)
+                          : launch_merge_dt<DS_FP32>(p, rows, dyn, stream);
+}
+
+int64_t probe_read_groups(int64_t bytes) {
+  int64_t g = (bytes + kProbeTile - 1) / kProbeTile;
+  return g < 1 ? 1 : (g > 4096 ? 4096 : g);
+}
+
+hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  const int64_t g = probe_read_groups(bytes);
+  hipLaunchKernelGGL(probe_read_kernel, dim3(static_cast<uint32_t>(g)), dim3(kProbeThreads), 0, stream,
+                     static_cast<const u32x4*>(src), bytes / 16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  const int64_t g = probe_read_groups(bytes);
+  hipLaunchKernelGGL(probe_copy_kernel, dim3(static_cast<uint32_t>(g)), dim3(kProbeThreads), 0, stream,
+                     static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), bytes / 16);
+  return hipGetLastError();
+}
+
+}  // namespace ds
