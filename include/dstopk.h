@@ -69,6 +69,8 @@ extern "C" {
  *              the block reach it), and the block only appends the elements that reach it.
  *              ON needs k <= 64 * waves and a whole first block; otherwise the plan falls
  *              back to OFF. Zero (auto) means ON. The result is the same either way.
+ *              The lanes' maxima are taken over every whole block among the first `depth`
+ *              blocks of the order (all of them are requested at the start).
  *   order_group  G in {1, 2, 4}: the random order is drawn over groups of G consecutive
  *              blocks, which are read in turn (G = 1 is the design note's order of single
  *              blocks; larger G keeps consecutive loads in flight, measured faster on
@@ -116,6 +118,7 @@ typedef struct ds_config {
   int32_t order_group;
   int32_t merge;
   int32_t schedule;
+  int32_t depth; /* output only (ds_topk_plan): blocks in flight per wave; zero on input */
 } ds_config;
 
 /*

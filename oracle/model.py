@@ -42,11 +42,13 @@ leave the result unchanged, only the counts):
   whole, sets T0 = the smallest over the workgroup's waves of each wave's j-th largest
   lane maximum (j = ceil(k / waves)), with the low (key bits - 16) key bits cleared; every
   element with key >= T0 is appended until the first compaction. A lane's maximum is over
-  its elements of that block (lane l of wave w holds, in every 16-byte chunk c of the block
-  with c mod waves = w, the elements at l*vec .. l*vec+vec-1; vec = 16 / element bytes),
-  and also over the second block read when the slice has fewer than 8 blocks and that
-  block is whole. Keys are the order-preserving unsigned images of the raw bits: sign bit
-  clear -> set the sign bit, sign bit set -> invert every bit.
+  its elements of every whole block among the first `depth` positions of the order (the
+  blocks the kernel has requested before it filters anything; lane l of wave w holds, in
+  every 16-byte chunk c of a block with c mod waves = w, the elements at l*vec ..
+  l*vec+vec-1; vec = 16 / element bytes). With groups of G blocks, position d is block
+  G*g(d // G) + d mod G of the group order g, and positions past the last block are empty.
+  Keys are the order-preserving unsigned images of the raw bits: sign bit clear -> set the
+  sign bit, sign bit set -> invert every bit.
 
 Slices (the split-row path): slice s of a row covers [s*Ls, min((s+1)*Ls, N)) for a slice
 length Ls that is a multiple of B; each slice runs the method on its own elements with its
@@ -224,15 +226,14 @@ def radix_select_topk(v: np.ndarray, pos: np.ndarray, j: np.ndarray, cand: np.nd
 def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B: int, B2: int,
                      order: np.ndarray, keys: Optional[np.ndarray] = None,
                      presample: Optional[Presample] = None,
-                     second: Optional[int] = None) -> Tuple[np.ndarray, RunStats]:
+                     firsts: Optional[List[int]] = None) -> Tuple[np.ndarray, RunStats]:
     """DeepSelectTopk over the elements [lo, hi) of a row (indices stay row-relative).
 
     ``order`` lists the blocks of the range in processing order (block b covers
     [lo + b*B, min(lo + (b+1)*B, hi))). With ``presample`` (and the row's ``keys``) the run
-    starts from the presampled threshold when the first block read is whole; ``second`` is
-    the block at the second position of the order (None when that position is empty), which
-    the threshold also covers on ranges of fewer than 8 blocks. Returns the kept positions
-    (at most k, unordered) and the run's counts.
+    starts from the presampled threshold when the first block read is whole; ``firsts`` are
+    the blocks at the first positions of the order whose whole blocks the threshold covers.
+    Returns the kept positions (at most k, unordered) and the run's counts.
     """
     n = hi - lo
     assert n >= 1 and k >= 1 and B >= 1 and B2 >= 1
@@ -248,8 +249,8 @@ def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B
         return lo + (b + 1) * B <= hi
 
     if presample is not None and whole(int(order[0])):
-        firsts = [int(order[0])] + ([second] if m < 8 and second is not None and whole(second) else [])
-        t0 = presample_key([keys[lo + b * B:lo + (b + 1) * B] for b in firsts], k, presample)
+        covered = [b for b in (firsts or [int(order[0])]) if whole(b)]
+        t0 = presample_key([keys[lo + b * B:lo + (b + 1) * B] for b in covered], k, presample)
     for b in order:
         blo, bhi = lo + int(b) * B, min(lo + (int(b) + 1) * B, hi)
         js = np.arange(blo, bhi, dtype=np.int64)
@@ -280,14 +281,30 @@ def sort_output(v: np.ndarray, pos: np.ndarray, kept: np.ndarray) -> np.ndarray:
     return kept[_order(v[kept], pos[kept], kept)]
 
 
+def first_positions(m: int, group: int, depth: int, seed: int, row_id: int, slice_: int,
+                    family: str = "feistel") -> List[int]:
+    """Blocks at the first ``depth`` positions of the order (empty positions left out)."""
+    if group == 1:
+        return [int(b) for b in block_order(family, m, seed, row_id, slice_)[:depth]]
+    g = feistel_order(-(-m // group), seed, row_id, slice_)
+    out = []
+    for d in range(min(depth, g.size * group)):
+        b = int(g[d // group]) * group + d % group
+        if b < m:
+            out.append(b)
+    return out
+
+
 def deepselect_row(row: np.ndarray, k: int, B: int, B2: int, family: str = "feistel", seed: int = 0,
                    row_id: int = 0, slice_len: Optional[int] = None, group: int = 1,
-                   presample_waves: Optional[int] = None) -> Tuple[np.ndarray, List[RunStats]]:
+                   presample_waves: Optional[int] = None,
+                   presample_depth: int = 4) -> Tuple[np.ndarray, List[RunStats]]:
     """DeepSelect on one row (bf16 bits or float32), optionally split into slices.
 
     ``group`` > 1 draws the Feistel order over groups of blocks; ``presample_waves`` (the
-    workgroup's waves) turns on the presampled start. Returns the top-k indices in output
-    order and the per-slice counts.
+    workgroup's waves) turns on the presampled start, over the whole blocks among the first
+    ``presample_depth`` positions of the order. Returns the top-k indices in output order
+    and the per-slice counts.
     """
     v = widen(row)
     pos = (~np.signbit(v)).astype(np.int64)
@@ -310,10 +327,8 @@ def deepselect_row(row: np.ndarray, k: int, B: int, B2: int, family: str = "feis
         hi = min(lo + slice_len, n)
         m = -(-(hi - lo) // B)
         order = grouped_order(m, group, seed, row_id, s) if group != 1 else block_order(family, m, seed, row_id, s)
-        # the second position of the order: the first group's second block (none past the end)
-        second = (int(order[1]) if m > 1 else None) if group == 1 else \
-            (int(order[0]) + 1 if int(order[0]) + 1 < m else None)
-        kept, st = deepselect_range(v, pos, lo, hi, k, B, B2, order, keys, ps, second)
+        firsts = first_positions(m, group, presample_depth, seed, row_id, s, family)
+        kept, st = deepselect_range(v, pos, lo, hi, k, B, B2, order, keys, ps, firsts)
         stats.append(st)
         kept_all.append(kept)
     union = np.concatenate(kept_all)

@@ -122,6 +122,7 @@ def test_merge_levels_rule():
 
 def test_merge_plan_field():
     assert ts.ds_topk_plan(8, 1 << 20, 512, ts.BF16, {"slices": 32})["merge"] == ts.MERGE_LISTS
+    assert ts.ds_topk_plan(8, 1 << 20, 512, ts.BF16, {"slices": 4})["merge"] == ts.MERGE_LISTS
     assert ts.ds_topk_plan(8, 1 << 20, 512, ts.BF16, {"slices": 32, "merge": ts.MERGE_SELECT})["merge"] == \
         ts.MERGE_SELECT
     assert ts.ds_topk_plan(8, 1 << 20, 512, ts.BF16, {"slices": 1, "merge": ts.MERGE_SELECT})["merge"] == 0

@@ -153,7 +153,8 @@ def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
         slice_len = -(-per // B) * B  # the planner's slice length
         if mode != "free":
             _, mst = model.deepselect_row(x[r], k, B, B2, "feistel", seed=seed, row_id=r,
-                                          slice_len=slice_len, group=plan["order_group"], presample_waves=pw)
+                                          slice_len=slice_len, group=plan["order_group"], presample_waves=pw,
+                                          presample_depth=plan["depth"])
             assert len(mst) == plan["slices"]
         for s in range(plan["slices"]):
             g = st[r, s]

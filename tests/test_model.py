@@ -299,13 +299,13 @@ def test_presample_key(dtype, waves, k, nblocks, family):
 
 
 @pytest.mark.parametrize("family", ["normal", "ascending", "ties", "specials"])
-@pytest.mark.parametrize("dtype,n,k,B,slice_len,group", [
-    (gen.BF16, 20000, 100, 1024, None, 2),   # 20 blocks, one presampled block
-    (gen.BF16, 6000, 128, 1024, None, 1),    # 6 blocks: the first two presampled
-    (gen.FP32, 9000, 200, 1024, 4096, 2),    # slices of 4 blocks, groups of two
-    (gen.FP32, 3000, 50, 1024, None, 4),     # a short last group
+@pytest.mark.parametrize("dtype,n,k,B,slice_len,group,depth", [
+    (gen.BF16, 20000, 100, 1024, None, 2, 4),   # 20 blocks, the first four presampled
+    (gen.BF16, 6000, 128, 1024, None, 1, 2),    # 6 blocks: the first two presampled
+    (gen.FP32, 9000, 200, 1024, 4096, 2, 4),    # slices of 4 blocks, groups of two
+    (gen.FP32, 3000, 50, 1024, None, 4, 4),     # a short last group
 ])
-def test_model_grouped_presampled_matches_oracle(family, dtype, n, k, B, slice_len, group):
+def test_model_grouped_presampled_matches_oracle(family, dtype, n, k, B, slice_len, group, depth):
     """The grouped order and the presampled start keep the result exact and the design
     note's invariants; on i.i.d. rows the presampled start appends fewer elements."""
     waves = 2 if dtype == gen.BF16 else 4
@@ -313,10 +313,22 @@ def test_model_grouped_presampled_matches_oracle(family, dtype, n, k, B, slice_l
     _, want = otk.topk(x, k)
     for r in range(x.shape[0]):
         got, stats = model.deepselect_row(x[r], k, B, 256, seed=r + 3, row_id=r, slice_len=slice_len, group=group,
-                                          presample_waves=waves)
+                                          presample_waves=waves, presample_depth=depth)
         assert got.tolist() == want[r].tolist()
         for st in stats:
             _check_invariants(st, n, k, B, 256)
         if family == "normal":
             _, plain = model.deepselect_row(x[r], k, B, 256, seed=r + 3, row_id=r, slice_len=slice_len, group=group)
             assert sum(s.A for s in stats) < sum(s.A for s in plain)
+
+
+@pytest.mark.parametrize("m,group,depth", [(6, 1, 4), (7, 2, 4), (5, 2, 4), (1, 2, 4), (9, 4, 2), (3, 4, 4)])
+def test_first_positions_follow_the_grouped_order(m, group, depth):
+    """The presampled blocks are the first positions of the processing order, the padding of
+    a short last group left out (the grouped order lists the same blocks in the same order)."""
+    firsts = model.first_positions(m, group, depth, 5, 1, 0)
+    order = model.grouped_order(m, group, 5, 1, 0) if group > 1 else model.feistel_order(m, 5, 1, 0)
+    assert firsts == [int(b) for b in order[:len(firsts)]]
+    assert len(firsts) <= depth and all(0 <= b < m for b in firsts)
+    if m >= depth * group:
+        assert len(firsts) == depth  # no padding among the first positions of a long order

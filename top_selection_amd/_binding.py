@@ -43,7 +43,8 @@ class DSError(RuntimeError):
 class ds_config(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("slack", ctypes.c_int32), ("slices", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("presample", ctypes.c_int32), ("order_group", ctypes.c_int32),
-                ("merge", ctypes.c_int32), ("schedule", ctypes.c_int32)]
+                ("merge", ctypes.c_int32), ("schedule", ctypes.c_int32),
+                ("depth", ctypes.c_int32)]
 
 
 STATS_FIELDS = ["appended", "compactions", "work", "max_len", "reads", "index_sum", "monotone", "slice_lo",
@@ -116,7 +117,7 @@ def ds_topk_plan(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, 
         raise DSError(st, "ds_topk_plan")
     return {"block": out.block, "slack": out.slack, "slices": out.slices, "waves": out.waves,
             "presample": out.presample, "order_group": out.order_group, "merge": out.merge,
-            "schedule": out.schedule}
+            "schedule": out.schedule, "depth": out.depth}
 
 
 def ds_topk_workspace_size(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, int]] = None) -> int:

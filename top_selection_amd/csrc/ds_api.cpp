@@ -95,7 +95,7 @@ int check_basic(int64_t rows, int64_t n, int k, int dtype) {
 int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK) return st;
-  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0, 0};
+  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (c.block < 0 || c.slack < 0 || c.slices < 0 || c.waves < 0) return DS_ERR_INVALID_ARG;
   if (c.presample != DS_PRESAMPLE_AUTO && c.presample != DS_PRESAMPLE_OFF && c.presample != DS_PRESAMPLE_ON)
     return DS_ERR_INVALID_ARG;
@@ -104,6 +104,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   if (c.merge != DS_MERGE_AUTO && c.merge != DS_MERGE_LISTS && c.merge != DS_MERGE_SELECT) return DS_ERR_INVALID_ARG;
   if (c.schedule != DS_SCHEDULE_AUTO && c.schedule != DS_SCHEDULE_FREE && c.schedule != DS_SCHEDULE_LOCKSTEP)
     return DS_ERR_INVALID_ARG;
+  if (c.depth != 0) return DS_ERR_INVALID_ARG;  // reported by the plan, never forced
   const int chunk = chunk_elems(dtype);
   const int eb = elem_bytes(dtype);
 
@@ -433,6 +434,7 @@ int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg
   out->order_group = p.order_group;
   out->merge = p.slices > 1 ? p.merge : DS_MERGE_AUTO;
   out->schedule = p.lockstep ? DS_SCHEDULE_LOCKSTEP : DS_SCHEDULE_FREE;
+  out->depth = ds::depth_for(kSelectShapes[p.shape].waves, kSelectShapes[p.shape].cpw);
   return DS_OK;
 }
 

@@ -362,26 +362,31 @@ __host__ __device__ constexpr uint32_t round4(uint32_t v) { return (v + 3u) & ~3
 
 // Candidate buffer in LDS (32-bit words, every array 16-byte aligned), k4 = round4(k),
 // pc = round4(B2 + B):
-//   ck[k4 + pc], ci[k4 + pc]  keys / indices: survivor set A in [0, k4), appended entries
+//   ck[k4 + pc + 64], ci[...] keys / indices: survivor set A in [0, k4), appended entries
 //                             from k4 on (before the first compaction appends start at 0,
-//                             so k + B2 + B entries fit)
+//                             so k + B2 + B entries fit), then 64 per-lane dummy slots
 //   bk[k4], bi[k4]            survivor set B
 //   hist[2 * kBins]           two histograms, used alternately
 //   ordt[kOrdCap]             the block order (block id of the i-th block read)
 // After the final compaction the append region (ck + k4, ci + k4: pc >= pow2(k) words
 // each) is the sort's exchange buffer.
+// Per-lane dummy slots after the append region of ck and ci: a lane whose element does not
+// hit writes there, so the append needs no exec-mask changes.
+constexpr uint32_t kDummySlots = 64;
+
 struct Lay {
   uint32_t *ck, *ci, *bk, *bi, *hist, *ordt;
-  uint32_t k4, pc;
+  uint32_t k4, pc, dummy;
 };
 
 __device__ __forceinline__ Lay lay_of(uint32_t* lds, uint32_t k, uint32_t B2, uint32_t B) {
   Lay l;
   l.k4 = round4(k);
   l.pc = round4(B2 + B);
+  l.dummy = l.k4 + l.pc;
   l.ck = lds;
-  l.ci = lds + (l.k4 + l.pc);
-  l.bk = lds + 2u * (l.k4 + l.pc);
+  l.ci = lds + (l.k4 + l.pc + kDummySlots);
+  l.bk = lds + 2u * (l.k4 + l.pc + kDummySlots);
   l.bi = l.bk + l.k4;
   l.hist = l.bi + l.k4;
   l.ordt = l.hist + 2u * kBins;
@@ -1367,9 +1372,12 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   // group order is a table for up to kOrdCap groups, computed on the fly beyond.
   const uint32_t ng = (m + (1u << gshift) - 1u) >> gshift, m_iter = ng << gshift;
   const bool tab = ng <= kOrdCap;
-  if (tab)
-    for (uint32_t i = tid; i < ng; i += NT) L.ordt[i] = ord.at(i);
-  lds_sync();
+  // block id of the i-th block read, from the permutation itself (direct) or its table
+  auto bid_direct = [&](uint32_t i) -> uint32_t {
+    if (i >= m_iter) return m;
+    const uint32_t b = (ord.at(i >> gshift) << gshift) | (i & ((1u << gshift) - 1u));
+    return b < m ? b : m;
+  };
   auto bid_of = [&](uint32_t i) -> uint32_t {
     if (i >= m_iter) return m;
     const uint32_t b = ((tab ? uni(L.ordt[i >> gshift]) : ord.at(i >> gshift)) << gshift) | (i & ((1u << gshift) - 1u));
@@ -1397,14 +1405,33 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     return bid < m ? (bid * B + (wave + t * WAVES) * CHUNK + lane * VEC) * IB : kNoLoad;
   };
 
+  // The first D blocks are requested before anything else, so their latency overlaps the
+  // set-up below (their ids come from the permutation directly, the rest from its table).
   u32x4 buf[D][CPW];
   uint32_t bids[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    bids[d] = bid_of(d);
+    bids[d] = bid_direct(d);
 #pragma unroll
     for (uint32_t t = 0; t < CPW; ++t) buf[d][t] = load16(rs, addr(bids[d], t));
   }
+
+  // workgroup state: histograms, counters, the order table
+  for (uint32_t i = 4u * tid; i < 2u * kBins; i += 4u * NT) *reinterpret_cast<uint4*>(L.hist + i) = make_uint4(0, 0, 0, 0);
+  if (tid == 0) {
+    sc.len = 0;
+    sc.done = 0;
+    sc.st_p = 0;
+    if constexpr (STATS) {
+      sc.st_a = sc.st_r = sc.st_w = sc.st_max = sc.st_tc = sc.st_ts = sc.st_tf = 0;
+      sc.st_mono = 1;
+      sc.reads = 0;
+      sc.index_sum = 0;
+    }
+  }
+  if (tab)
+    for (uint32_t i = tid; i < ng; i += NT) L.ordt[i] = ord.at(i);
+  lds_sync();
 
   bool sorted = false;
   // A compaction of the nsurv survivors and the napp entries appended since the last one.
@@ -1564,26 +1591,24 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
         }
       }
       if (presample && i == 0 && blk_lo + B <= len) {
-        // each lane's maximum over its elements of this block and, on short streams (fewer
-        // than 8 blocks) when it is a whole block too, of the second block read (already in
-        // flight in buf[1]): a tighter T0 where the final compaction dominates; long streams
-        // do not wait for it
+        // each lane's maximum over its elements of this block and of every other whole block
+        // already in flight (the next D - 1 of the order): all of them were requested at the
+        // start and arrive together, and more elements give a tighter T0
         uint32_t lmax = 0;
 #pragma unroll
         for (uint32_t t = 0; t < CPW; ++t) {
 #pragma unroll
           for (uint32_t q = 0; q < VEC; ++q) lmax = max(lmax, key_of_score<DT>(s[t][q]));
         }
-        if (m < 8 && bids[1] < m && bids[1] * B + B <= len) {
 #pragma unroll
-          for (uint32_t t = 0; t < CPW; ++t) {
+        for (int d = 1; d < D; ++d) {
+          if (bids[d] < m && bids[d] * B + B <= len) {
 #pragma unroll
-            for (uint32_t q = 0; q < 4; ++q) {
-              const uint32_t w = buf[1][t][q];
-              if constexpr (DT == DS_BF16) {
-                lmax = max(lmax, key_of_score<DT>(w << 16));
-                lmax = max(lmax, key_of_score<DT>(w));
-              } else {
+            for (uint32_t t = 0; t < CPW; ++t) {
+#pragma unroll
+              for (uint32_t q = 0; q < 4; ++q) {
+                const uint32_t w = buf[d][t][q];
+                if constexpr (DT == DS_BF16) lmax = max(lmax, key_of_score<DT>(w << 16));
                 lmax = max(lmax, key_of_score<DT>(w));
               }
             }
@@ -1639,10 +1664,13 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
         }
       } else {
         uint32_t kmn = ~0u, kmx = 0;  // key range of the hits while there is no threshold
-        // one reservation per chunk: only that chunk's hit masks are live. Hits are stored raw.
+        // one reservation per chunk: only that chunk's hit masks are live. Hits are stored raw;
+        // a lane without a hit in an element that some lane of the wave hit writes its dummy
+        // slot instead, so the stores need no exec-mask changes.
 #pragma unroll
         for (uint32_t t = 0; t < CPW; ++t) {
-          const uint32_t first = blk_lo + (wave + t * WAVES) * CHUNK + lane * VEC;
+          const uint32_t cfirst = blk_lo + (wave + t * WAVES) * CHUNK;  // the chunk's first element
+          const uint32_t first = cfirst + lane * VEC;
           bool h[VEC];
           if (mode == 1) {
 #pragma unroll
@@ -1651,9 +1679,10 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
 #pragma unroll
             for (uint32_t e = 0; e < VEC; ++e) h[e] = s[t][e] < thr;
           }
-          // elements past the stream's end (the tail chunk, or no chunk at all) never hit
+          if (cfirst + CHUNK > len_opaque) {  // the stream's tail chunk, or a chunk past its end
 #pragma unroll
-          for (uint32_t e = 0; e < VEC; ++e) h[e] = h[e] && first + e < len_opaque;
+            for (uint32_t e = 0; e < VEC; ++e) h[e] = h[e] && first + e < len_opaque;
+          }
           if (mode == 0) {
 #pragma unroll
             for (uint32_t e = 0; e < VEC; ++e) {
@@ -1676,11 +1705,9 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
 #pragma unroll
             for (uint32_t e = 0; e < VEC; ++e) {
               if (mk[e]) {
-                const uint32_t q = mbcnt(mk[e], pos);
-                if (h[e]) {
-                  L.ck[q] = s[t][e];
-                  L.ci[q] = j0 + e;
-                }
+                const uint32_t q = h[e] ? mbcnt(mk[e], pos) : L.dummy + lane;
+                L.ck[q] = s[t][e];
+                L.ci[q] = j0 + e;
                 pos += popc(mk[e]);
               }
             }
@@ -1802,10 +1829,6 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   out.sorted = sorted;
 }
 
-// Blocks in flight per wave (each CPW 16-byte chunks per lane): two for 16 waves, four for
-// smaller workgroups.
-constexpr int depth_for(int waves) { return waves < 16 ? 4 : 2; }
-
 // --------------------------------------------------------------------------- select kernel
 template <int DT, int WAVES, int CPW, bool STATS>
 __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
@@ -1829,18 +1852,6 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   if constexpr (STATS) t_start = wall_clock64();
 
   const Lay L = lay_of(lds, k, B2, B);
-  for (uint32_t i = 4u * tid; i < 2u * kBins; i += 4u * NT) *reinterpret_cast<uint4*>(L.hist + i) = make_uint4(0, 0, 0, 0);
-  if (tid == 0) {
-    sc.len = 0;
-    sc.done = 0;
-    sc.st_p = 0;
-    if constexpr (STATS) {
-      sc.st_a = sc.st_r = sc.st_w = sc.st_max = sc.st_tc = sc.st_ts = sc.st_tf = 0;
-      sc.st_mono = 1;
-      sc.reads = 0;
-      sc.index_sum = 0;
-    }
-  }
 
   const uint8_t* base = p.x + static_cast<uint64_t>(row) * p.row_stride_bytes + static_cast<uint64_t>(slice_lo) * EB;
   // Range = the slice rounded up to whole 16-byte chunks: the hardware checks whole dwords, so
@@ -1859,7 +1870,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   const bool own_sort = p.slices == 1 || p.sorted_lists;
 
   BodyOut bo;
-  deepselect_body<DT, WAVES, CPW, depth_for(WAVES), false, STATS>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
+  deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), false, STATS>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
                                                                    slice_lo + len - 1u, p.lockstep != 0,
                                                                    p.presample != 0, gshift,
                                                                    own_sort ? &fso : nullptr, bo);
@@ -1937,12 +1948,6 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   const uint32_t B2 = static_cast<uint32_t>(p.slack);
 
   const Lay L = lay_of(lds, k, B2, B);
-  for (uint32_t i = 4u * tid; i < 2u * kBins; i += 4u * NT) *reinterpret_cast<uint4*>(L.hist + i) = make_uint4(0, 0, 0, 0);
-  if (tid == 0) {
-    sc.len = 0;
-    sc.done = 0;
-    sc.st_p = 0;
-  }
   const uint2* base = p.ws + static_cast<uint64_t>(row) * p.row_entries;  // rows padded to 16 bytes
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint2*>(base), 0, static_cast<int>((len * 8u + 15u) & ~15u), kRsrcWord3);
@@ -1951,7 +1956,7 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
 
   const OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
   BodyOut bo;
-  deepselect_body<DT, WAVES, CPW, depth_for(WAVES), true, false>(L, sc, rs, len, 0u, k, B2, ord, 0u,
+  deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), true, false>(L, sc, rs, len, 0u, k, B2, ord, 0u,
                                                                   static_cast<uint32_t>(p.n - 1), false,
                                                                   p.presample != 0, 0u, &fso, bo);
   if (!bo.sorted)

@@ -72,6 +72,11 @@ constexpr Shape kSelectShapes[] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}, {8, 2}, {4, 4
 constexpr int kNumSelectShapes = sizeof(kSelectShapes) / sizeof(kSelectShapes[0]);
 constexpr Shape kMergeShape = {16, 2};  // 16 waves x 2 chunks x 128 entries = 4096 entries per block
 
+// Blocks in flight per wave in a select workgroup of `waves` waves with `cpw` 16-byte chunks
+// per wave per block: four (at most 16 VGPRs of loads), or two for four chunks. The presampled
+// start covers the whole blocks among the first depth_for blocks of the order.
+constexpr int depth_for(int waves, int cpw) { return (void)waves, cpw >= 4 ? 2 : 4; }
+
 // LDS bytes a select/merge workgroup needs, and the part of them that is not the dynamic
 // array (the per-workgroup scalars).
 size_t select_lds_bytes(int k, int block, int slack, int waves);

@@ -107,7 +107,7 @@ size_t select_scalars_bytes() { return sizeof(Scalars); }
 size_t select_lds_bytes(int k, int block, int slack, int waves) {
   (void)waves;
   const size_t k4 = round4(static_cast<uint32_t>(k)), pc = round4(static_cast<uint32_t>(slack + block));
-  return (2 * (k4 + pc) + 2 * k4 + 2 * kBins + kOrdCap) * 4 + sizeof(Scalars);
+  return (2 * (k4 + pc + kDummySlots) + 2 * k4 + 2 * kBins + kOrdCap) * 4 + sizeof(Scalars);
 }
 
 // The counters are a separate instantiation (its own object), so the kernel that runs
