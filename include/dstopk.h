@@ -229,6 +229,23 @@ int ds_topk_merge(int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void
                   void* workspace, size_t ws_bytes, const ds_config* cfg, void* stream);
 
 /*
+ * ds_topk_noalloc -- ds_topk for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, plan, kernels and result as ds_topk; the split rows' workspace is a
+ * library-owned device array of DS_NOALLOC_SCRATCH_BYTES on each GPU (reserved when the
+ * library's code is loaded on that GPU and held until the process ends) instead of the
+ * per-stream cache, so no call allocates, frees or synchronises. A call whose plan needs
+ * more workspace than that returns DS_ERR_WORKSPACE and enqueues nothing (use ds_topk_ex
+ * with a workspace of ds_topk_workspace_size bytes). All calls on one GPU share the one
+ * array, on every stream: calls that overlap in time on one GPU race and give wrong
+ * results, so order them (one stream, or events). Nothing in the array needs to start at
+ * any value; each call overwrites what it reads.
+ */
+#define DS_NOALLOC_SCRATCH_BYTES (8u << 20)
+int ds_topk_noalloc(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
+                    void* out_vals, int32_t* out_idx, void* stream);
+
+/*
  * ds_probe_read -- measurement aid, not part of top-k (tutorial chapter 37, section 6.1: the
  * method is judged by how close it comes to reading the input once; this is the plain read
  * of the same bytes): streams `bytes` (a multiple of

@@ -12,7 +12,8 @@ FAKE = 0x10000  # a 16-byte aligned address; never dereferenced by a rejected ca
 def test_exports_every_declared_symbol():
     names = ts.header_functions()
     assert {"ds_topk", "ds_topk_ex", "ds_topk_plan", "ds_topk_workspace_size", "ds_status_string",
-            "ds_probe_read", "ds_probe_copy", "ds_probe_sink_words", "ds_topk_slices", "ds_topk_merge"} <= set(names)
+            "ds_probe_read", "ds_probe_copy", "ds_probe_sink_words", "ds_topk_slices", "ds_topk_merge",
+            "ds_topk_noalloc"} <= set(names)
     lib = ts.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -25,8 +26,8 @@ def test_status_strings():
         assert ts.ds_status_string(code) == name
 
 
-def _call(x=FAKE, rows=4, n=1024, stride=None, k=8, dtype=ts.BF16, vals=FAKE, idx=FAKE):
-    return ts.lib().ds_topk(x, rows, n, n if stride is None else stride, k, dtype, 1, vals, idx, None)
+def _call(x=FAKE, rows=4, n=1024, stride=None, k=8, dtype=ts.BF16, vals=FAKE, idx=FAKE, entry="ds_topk"):
+    return getattr(ts.lib(), entry)(x, rows, n, n if stride is None else stride, k, dtype, 1, vals, idx, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -43,12 +44,21 @@ def _call(x=FAKE, rows=4, n=1024, stride=None, k=8, dtype=ts.BF16, vals=FAKE, id
     (dict(x=FAKE + 8), ts.DS_ERR_ALIGNMENT),
     (dict(n=1001, stride=1001), ts.DS_ERR_ALIGNMENT),        # 2002-byte rows
 ])
-def test_rejects_before_launch(kw, code):
-    assert _call(**kw) == code
+@pytest.mark.parametrize("entry", ["ds_topk", "ds_topk_noalloc"])
+def test_rejects_before_launch(kw, code, entry):
+    assert _call(entry=entry, **kw) == code
 
 
-def test_empty_rows_is_a_no_op():
-    assert _call(rows=0) == ts.DS_OK
+@pytest.mark.parametrize("entry", ["ds_topk", "ds_topk_noalloc"])
+def test_empty_rows_is_a_no_op(entry):
+    assert _call(rows=0, entry=entry) == ts.DS_OK
+
+
+def test_noalloc_limit_matches_header():
+    import re
+    text = open(ts._binding.HEADER_PATH).read()
+    m = re.search(r"#define DS_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ts.DS_NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_rejected_without_touching_device():

@@ -25,6 +25,7 @@ DS_ERR_WORKSPACE = -4
 DS_ERR_LAUNCH = -5
 DS_ERR_DEVICE = -6
 DS_MAX_K = 4096
+DS_NOALLOC_SCRATCH_BYTES = 8 << 20
 PRESAMPLE_AUTO, PRESAMPLE_OFF, PRESAMPLE_ON = 0, 1, 2
 MERGE_AUTO, MERGE_LISTS, MERGE_SELECT = 0, 1, 2
 SCHEDULE_AUTO, SCHEDULE_FREE, SCHEDULE_LOCKSTEP = 0, 1, 2
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
             L.ds_topk.restype = ci
             L.ds_topk_ex.argtypes = [vp, i64, i64, i64, ci, ci, u64, vp, vp, vp, ctypes.c_size_t, cfgp, vp, vp]
             L.ds_topk_ex.restype = ci
+            L.ds_topk_noalloc.argtypes = [vp, i64, i64, i64, ci, ci, u64, vp, vp, vp]
+            L.ds_topk_noalloc.restype = ci
             L.ds_topk_slices.argtypes = [vp, i64, i64, i64, ci, ci, u64, vp, vp, vp, ctypes.c_size_t, cfgp, vp,
                                          vp]
             L.ds_topk_slices.restype = ci
@@ -184,6 +187,20 @@ def ds_topk(x, k: int, seed: int = 0, values: bool = True, indices: bool = True,
                        out_idx.data_ptr() if out_idx is not None else None, _stream_handle(stream))
     if st != DS_OK:
         raise DSError(st, "ds_topk")
+    return out_vals, out_idx
+
+
+def ds_topk_noalloc(x, k: int, seed: int = 0, values: bool = True, indices: bool = True, out_vals=None,
+                    out_idx=None, stream=None) -> Tuple[Optional[object], Optional[object]]:
+    """ds_topk whose workspace is the library's fixed per-GPU device array (no device
+    allocation by the library; outputs not given are allocated here by torch). Raises
+    DSError(DS_ERR_WORKSPACE) when the plan needs more than DS_NOALLOC_SCRATCH_BYTES."""
+    rows, n, rs, dt, out_vals, out_idx = _prep(x, k, values, indices, out_vals, out_idx)
+    st = lib().ds_topk_noalloc(x.data_ptr() if rows else None, rows, n, rs, k, dt, seed & 0xFFFFFFFFFFFFFFFF,
+                               out_vals.data_ptr() if out_vals is not None else None,
+                               out_idx.data_ptr() if out_idx is not None else None, _stream_handle(stream))
+    if st != DS_OK:
+        raise DSError(st, "ds_topk_noalloc")
     return out_vals, out_idx
 
 

@@ -33,6 +33,7 @@ UNITS = [("select_bf16", "ds_select.hip", ["-DDS_PART_DT=0", "-DDS_PART_STATS=0"
          ("select_bf16_stats", "ds_select.hip", ["-DDS_PART_DT=0", "-DDS_PART_STATS=1"]),
          ("select_fp32_stats", "ds_select.hip", ["-DDS_PART_DT=1", "-DDS_PART_STATS=1"]),
          ("merge", "ds_merge.hip", []),
+         ("noalloc", "ds_noalloc.hip", []),
          ("api", "ds_api.cpp", [])]
 
 NOISE = "packed-fp32-ops"

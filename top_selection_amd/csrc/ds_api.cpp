@@ -399,6 +399,27 @@ int cached_workspace(size_t bytes, hipStream_t stream, void** out) {
 
 }  // namespace
 
+namespace ds {
+
+int topk_auto(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
+              void* out_vals, int32_t* out_idx, void* stream, WorkspaceSource get_ws) {
+  int st = check_call(x, rows, n, row_stride, k, dtype, out_vals, out_idx);
+  if (st != DS_OK || rows == 0) return st;
+  const int cus = device_cu_count();
+  if (cus <= 0) return DS_ERR_DEVICE;
+  Plan p;
+  st = make_plan(rows, n, k, dtype, nullptr, cus, &p);
+  if (st != DS_OK) return st;
+  void* ws = nullptr;
+  if (p.ws_bytes) {
+    st = get_ws(p.ws_bytes, stream, &ws);
+    if (st != DS_OK) return st;
+  }
+  return run(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, nullptr, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace ds
+
 extern "C" {
 
 const char* ds_status_string(int status) {
@@ -491,19 +512,10 @@ int ds_topk_merge(int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void
 
 int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
             void* out_vals, int32_t* out_idx, void* stream) {
-  int st = check_call(x, rows, n, row_stride, k, dtype, out_vals, out_idx);
-  if (st != DS_OK || rows == 0) return st;
-  const int cus = device_cu_count();
-  if (cus <= 0) return DS_ERR_DEVICE;
-  Plan p;
-  st = make_plan(rows, n, k, dtype, nullptr, cus, &p);
-  if (st != DS_OK) return st;
-  void* ws = nullptr;
-  if (p.ws_bytes) {
-    st = cached_workspace(p.ws_bytes, static_cast<hipStream_t>(stream), &ws);
-    if (st != DS_OK) return st;
-  }
-  return run(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, nullptr, static_cast<hipStream_t>(stream));
+  return ds::topk_auto(x, rows, n, row_stride, k, dtype, seed, out_vals, out_idx, stream,
+                       [](size_t bytes, void* s, void** out) {
+                         return cached_workspace(bytes, static_cast<hipStream_t>(s), out);
+                       });
 }
 
 int64_t ds_probe_sink_words(int64_t bytes) { return bytes <= 0 ? 0 : ds::probe_read_groups(bytes); }

@@ -88,6 +88,13 @@ constexpr uint32_t kMaxListGroup = 16;
 constexpr int64_t kListMergeLds = 128 * 1024;
 constexpr int kListMergeWaves = 8;
 
+// ds_topk's body (argument checks, the automatic plan, the launches) with the split rows'
+// workspace taken from `get_ws(bytes, stream, &ptr)` (a status code; called only when the
+// plan needs a workspace, before anything is enqueued).
+using WorkspaceSource = int (*)(size_t bytes, void* stream, void** out);
+int topk_auto(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
+              void* out_vals, int32_t* out_idx, void* stream, WorkspaceSource get_ws);
+
 // The select-kernel launcher of one element type and counter mode (one object each).
 #define DS_SELECT_PART_NAME(dt, st) launch_select_part_##dt##_##st
 hipError_t DS_SELECT_PART_NAME(0, 0)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream);
