@@ -17,11 +17,20 @@ from workloads import gen
 pytestmark = pytest.mark.gpu
 
 
-def _check(x, k, label, seed=1, cfg=None, values=True, indices=True, pad_to=0, stats=False):
+def _check(x, k, label, seed=1, cfg=None, values=True, indices=True, pad_to=0, stats=False, want=None):
     say(f"[gpu] {label}: rows={x.shape[0]} n={x.shape[1]} k={k} dtype={x.dtype} cfg={cfg} seed={seed}")
     gv, gi, _ = run_gpu(x, k, seed=seed, cfg=cfg, values=values, indices=indices, pad_to=pad_to, stats=stats)
-    wv, wi = otk.topk(x, k)
+    wv, wi = otk.topk(x, k) if want is None else want
     assert_same(x, k, gv, gi, wv if values else None, wi if indices else None, label)
+
+
+SEEDS = (1, 2, 3)  # block-order seeds: the result must not depend on the order (design note, "Algorithm")
+
+
+def _check_seeds(x, k, label, **kw):
+    want = otk.topk(x, k)
+    for seed in SEEDS:
+        _check(x, k, f"{label} seed={seed}", seed=seed, want=want, **kw)
 
 
 def test_smoke_small():
@@ -52,7 +61,7 @@ def test_c3_sampler_rows(slices):
 @pytest.mark.parametrize("k", [512, 4096])
 def test_c4_long_full(k):
     x = gen.WORKLOADS["c4_long"].make()
-    _check(x, k, f"c4 k={k}")
+    _check_seeds(x, k, f"c4 k={k}")
 
 
 def test_c5_reduced():
@@ -65,13 +74,13 @@ def test_c5_reduced():
 def test_full_size_bench_shapes(name):
     w = gen.WORKLOADS[name]
     x = w.make()
-    _check(x, w.ks[0], f"{name}-full")
+    _check_seeds(x, w.ks[0], f"{name}-full")
 
 
 def test_c5_full_size():
     w = gen.WORKLOADS["c5_giant"]
     x = w.make()
-    _check(x, 32, "c5-full", indices=False)
+    _check_seeds(x, 32, "c5-full", indices=False)
 
 
 FAMILIES = ["normal", "ascending", "descending", "constant", "ties", "specials", "tiny", "neg"]

@@ -226,6 +226,56 @@ def test_expected_work_bound(shape):
             assert mean + half <= bound, (name, kind, fam, mean, half, bound)
 
 
+# The plans the library ships for the workloads (one slice each): (name, slice length, k, B,
+# B2, G, presample waves or None, blocks covered by the presample, rows, seeds). A grouped
+# order reads G consecutive blocks in turn, so the bound's analysis applies to super-blocks of
+# G*B elements: m = ceil(N / (G*B)) and L = k + G*B + B2.
+SHIPPED_PLANS = [
+    ("indexer_slice", 32768, 512, 8192, 4096, 1, 16, 4, ("indexer", "ascending"), 60),
+    ("sampler_row", 129280, 512, 8192, 4096, 2, 16, 4, ("sampler", "sampler_ascending"), 30),
+    ("long_k4096_slice", 32768, 4096, 4096, 4096, 2, None, 4, ("normal", "ascending"), 60),
+    ("giant_slice", 1 << 20, 32, 16384, 1024, 2, 16, 2, ("grid", "grid_ascending"), 80),
+]
+
+
+def _shipped_row(kind, n):
+    if kind == "sampler_ascending":
+        return np.sort(gen.rows_sampler_f32(80, 1, n)[0])
+    if kind == "grid_ascending":
+        return np.sort(gen.rows_grid_f32(82, 1, n)[0])
+    return _bound_row(kind, n)
+
+
+def grouped_bound(n, k, B, B2, G):
+    """The boxed bound with the block replaced by a group of G blocks."""
+    m = -(-n // (G * B))
+    return (1.0 + k / B2) * (k + G * B + B2) * model.harmonic(m)
+
+
+def test_grouped_bound_reduces_to_the_boxed_bound():
+    for n, k, B, B2 in [(32768, 512, 1024, 1024), (1 << 20, 4096, 4096, 4096), (129280, 512, 8192, 4096)]:
+        assert grouped_bound(n, k, B, B2, 1) == model.expected_work_bound(n, k, B, B2)
+
+
+@pytest.mark.parametrize("plan", SHIPPED_PLANS, ids=[p[0] for p in SHIPPED_PLANS])
+def test_expected_work_bound_at_shipped_plans(plan):
+    """Mean W over block-order seeds (95% upper confidence) stays under the bound at the plans
+    the library runs: its B and B2, its order groups and its presampled start."""
+    name, n, k, B, B2, G, waves, depth, kinds, seeds = plan
+    bound = grouped_bound(n, k, B, B2, G)
+    for kind in kinds:
+        row = _shipped_row(kind, n)
+        ws = []
+        for s in range(seeds):
+            _, st = model.deepselect_row(row, k, B, B2, "feistel", seed=s + 1, row_id=s % 5, group=G,
+                                         presample_waves=waves, presample_depth=depth)
+            assert len(st) == 1
+            ws.append(st[0].W)
+        mean = float(np.mean(ws))
+        half = 1.96 * float(np.std(ws)) / math.sqrt(len(ws))
+        assert mean + half <= bound, (name, kind, mean, half, bound)
+
+
 # ----------------------------------------------------------------------------- grouped order, presample
 def test_keys_follow_numeric_order():
     """keys_of orders values as numbers do, with +0 above -0 (bf16 and fp32, specials too)."""

@@ -39,6 +39,28 @@ def test_exhaustive_alphabet_vs_brute(dtype, n):
             assert np.array_equal(vals[r], x[r, want])
 
 
+def test_batch_brute_agrees_with_row_brute():
+    """The vectorised rank count against the per-row one, on every 4-element alphabet row."""
+    rows = np.array(list(itertools.product(ALPHABET, repeat=4)), np.float64)
+    order = brute.brute_order_batch(rows)
+    for r in range(0, rows.shape[0], 7):
+        assert order[r].tolist() == brute.brute_topk(list(rows[r]), 4)
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+@pytest.mark.parametrize("n", [5, 6, 7])
+def test_exhaustive_alphabet_vs_batch_brute(dtype, n):
+    """Every row of n <= 7 elements over the 7-value alphabet (signed zeros, infinities,
+    ties), every k: the oracle's output equals the rank count's."""
+    rows = np.array(list(itertools.product(ALPHABET, repeat=n)), np.float32)
+    x = _as_dtype(rows, dtype)
+    order = np.concatenate([brute.brute_order_batch(_widen(x[i:i + 65536])) for i in range(0, x.shape[0], 65536)])
+    for k in range(1, n + 1):
+        vals, idx = otk.topk(x, k)
+        assert np.array_equal(idx, order[:, :k]), k
+        assert np.array_equal(vals, np.take_along_axis(x, order[:, :k], axis=1)), k
+
+
 @pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
 def test_random_tiny_ties_vs_brute(dtype):
     g = np.random.default_rng(7)
