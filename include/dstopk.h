@@ -119,7 +119,21 @@ typedef struct ds_config {
   int32_t merge;
   int32_t schedule;
   int32_t depth; /* output only (ds_topk_plan): blocks in flight per wave; zero on input */
+  int32_t output;
 } ds_config;
+/*
+ *   output     flags for the outputs' form (zero: sorted, int32 indices).
+ *              DS_OUTPUT_UNSORTED: each row's k outputs are its top k in an unspecified
+ *              order (tutorial chapter 37, sections 5.1 and 5.2(4): the Ascend kernel leaves
+ *              its output unsorted and sorts only the k results, at the end, when asked).
+ *              The single-slice path then skips the final sort (the survivors of the final
+ *              compaction are written as they stand) and so does the merge kernel
+ *              (DS_MERGE_SELECT); the list merge still writes sorted rows.
+ *              DS_OUTPUT_INDEX_INT64: out_idx is [rows, k] int64 (TileKernels chapter 33,
+ *              section 4.7: the gate's indices are int64, converted exactly from int32).
+ */
+#define DS_OUTPUT_UNSORTED 1
+#define DS_OUTPUT_INDEX_INT64 2
 
 /*
  * Per-(row, slice) counters of one run, filled when ds_topk_ex gets a stats pointer.
@@ -203,12 +217,21 @@ int ds_topk_workspace_size(int64_t rows, int64_t n, int k, int dtype, const ds_c
  *   workspace  device, >= ds_topk_workspace_size bytes, 16-byte aligned; may be NULL when
  *              that size is 0. Its contents on entry do not matter; it is overwritten.
  *              Calls that share a workspace must not overlap in time.
+ *   lens       NULL, or device [rows] int32: ragged rows (tutorial chapter 37, section 5.2(1):
+ *              the Ascend kernel takes each row's valid length; a DSA indexer query sees
+ *              its own context length, section 1.1). Row r is its first
+ *              min(max(lens[r], 0), n) elements; n (the longest row) sets the plan. When a
+ *              row holds fewer than k elements, its outputs past them are padding: index -1
+ *              and the value bit pattern of all ones (a NaN, never an input). The values are
+ *              read on the device only.
+ *   out_idx    as in ds_topk, or [rows, k] int64 when cfg->output has DS_OUTPUT_INDEX_INT64
+ *              (8-byte aligned).
  *   cfg        NULL or fields to force (see ds_config).
  *   stats      NULL, or device [rows, slices] ds_stats filled by the select kernel.
  * Allocates nothing and never synchronises, so it can be captured in a graph.
  */
-int ds_topk_ex(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
-               void* out_vals, int32_t* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
+int ds_topk_ex(const void* x, const int32_t* lens, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype,
+               uint64_t seed, void* out_vals, void* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
                ds_stats* stats, void* stream);
 
 /*
@@ -219,14 +242,14 @@ int ds_topk_ex(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k
  * to the workspace (sorted, for the list merge) and ds_topk_merge reduces each row's
  * survivors to the sorted top-k (one launch per list-merge level, or one merge-kernel
  * launch; nothing when the plan has one slice). Both take the same arguments as
- * ds_topk_ex (merge ignores x, row_stride and stats) and must be given the same rows, n, k,
- * dtype, seed, cfg and workspace; the pair then equals one ds_topk_ex call.
+ * ds_topk_ex (merge ignores x, row_stride and stats) and must be given the same lens, rows,
+ * n, k, dtype, seed, cfg and workspace; the pair then equals one ds_topk_ex call.
  */
-int ds_topk_slices(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
-                   void* out_vals, int32_t* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
-                   ds_stats* stats, void* stream);
-int ds_topk_merge(int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void* out_vals, int32_t* out_idx,
-                  void* workspace, size_t ws_bytes, const ds_config* cfg, void* stream);
+int ds_topk_slices(const void* x, const int32_t* lens, int64_t rows, int64_t n, int64_t row_stride, int k,
+                   int dtype, uint64_t seed, void* out_vals, void* out_idx, void* workspace, size_t ws_bytes,
+                   const ds_config* cfg, ds_stats* stats, void* stream);
+int ds_topk_merge(const int32_t* lens, int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void* out_vals,
+                  void* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg, void* stream);
 
 /*
  * ds_topk_noalloc -- ds_topk for callers that cannot allocate device memory: code being

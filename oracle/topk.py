@@ -71,3 +71,30 @@ def topk(x: np.ndarray, k: int, values: bool = True, indices: bool = True,
     if rc != 0:
         raise ValueError(f"oracle_topk rejected the arguments (rows={rows}, n={n}, k={k})")
     return vals, idx
+
+
+def padding_value(dtype) -> np.ndarray:
+    """The value bit pattern of an output position past a short row's length: all ones (a
+    NaN, which no input holds), as a 0-d array of the input's dtype."""
+    return np.array(0xFFFF, np.uint16) if np.dtype(dtype) == np.uint16 else np.array(0xFFFFFFFF, np.uint32).view(np.float32)
+
+
+def topk_ragged(x: np.ndarray, lens: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k of ragged rows: row r is x[r, :L] with L = min(max(lens[r], 0), n) (a per-row
+    valid length, TileLang tutorial chapter 37, section 5.2(1)). A row of L < k elements
+    gives its L top elements in order, then k - L padding positions (index -1, value bits
+    all ones). Rows of one length are passed to ``topk`` together."""
+    rows, n = x.shape
+    L = np.clip(np.asarray(lens, np.int64), 0, n)
+    vals = np.empty((rows, k), x.dtype)
+    vals[...] = padding_value(x.dtype)
+    idx = np.full((rows, k), -1, np.int32)
+    for length in np.unique(L):
+        kk = min(k, int(length))
+        if kk == 0:
+            continue
+        sel = np.nonzero(L == length)[0]
+        v, i = topk(x[sel, :int(length)], kk)
+        vals[sel, :kk] = v
+        idx[sel, :kk] = i
+    return vals, idx

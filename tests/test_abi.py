@@ -63,7 +63,7 @@ def test_noalloc_limit_matches_header():
 
 def test_workspace_rejected_without_touching_device():
     cfg = ts._binding.ds_config(0, 0, 4, 0)
-    st = ts.lib().ds_topk_ex(FAKE, 2, 65536, 65536, 64, ts.BF16, 0, FAKE, FAKE, None, 0, ctypes.byref(cfg), None,
+    st = ts.lib().ds_topk_ex(FAKE, None, 2, 65536, 65536, 64, ts.BF16, 0, FAKE, FAKE, None, 0, ctypes.byref(cfg), None,
                              None)
     assert st == ts.DS_ERR_WORKSPACE
 
@@ -192,4 +192,13 @@ def test_schedule_plan_field():
         ts.SCHEDULE_LOCKSTEP
     with pytest.raises(ts.DSError) as e:
         ts.ds_topk_plan(4, 100000, 64, ts.BF16, dict(base, schedule=7))
+    assert e.value.status == ts.DS_ERR_INVALID_ARG
+
+
+def test_output_flags_in_plan():
+    base = {"slices": 2}
+    for flags in (0, ts.OUTPUT_UNSORTED, ts.OUTPUT_INDEX_INT64, ts.OUTPUT_UNSORTED | ts.OUTPUT_INDEX_INT64):
+        assert ts.ds_topk_plan(4, 65536, 64, ts.BF16, dict(base, output=flags))["output"] == flags
+    with pytest.raises(ts.DSError) as e:
+        ts.ds_topk_plan(4, 65536, 64, ts.BF16, dict(base, output=4))
     assert e.value.status == ts.DS_ERR_INVALID_ARG

@@ -1,0 +1,173 @@
+"""Ragged rows (a valid length per row) and the output variants (unsorted rows, int64
+indices) of the HIP path, through the C ABI, against the oracle (tolerance 0).
+
+Ragged rows follow the per-row valid length of the Ascend kernel (TileLang tutorial chapter
+37, section 5.2(1)); unsorted output is that kernel's default and int64 indices are the
+TileKernels gate's (chapter 33, section 4.7). An unsorted row is compared as a set: its
+indices sorted ascending equal the oracle's sorted ascending, and every value is the input
+element at its index.
+"""
+import numpy as np
+import pytest
+
+import top_selection_amd as ts
+from gpu_util import assert_same, say, to_device, to_numpy_vals
+from oracle import topk as otk
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _lens(rows, n, k, B, seed, special=True):
+    """Random lengths in [0, n] with the boundary cases first: empty, one element, around k,
+    around the block and slice sizes, the full row, and out-of-range values that clamp."""
+    g = np.random.default_rng(seed)
+    lens = g.integers(0, n + 1, size=rows)
+    if special:
+        sp = [0, 1, k - 1, k, k + 1, B - 1, B, B + 1, n - 1, n, -5, n + 7]
+        sp = [v for v in sp if -5 <= v <= n + 7][:rows]
+        lens[:len(sp)] = sp
+    return lens.astype(np.int32)
+
+
+def _run(x, k, cfg=None, lens=None, seed=1, stats=False):
+    import torch
+    rows, n = x.shape
+    dt = gen.BF16 if x.dtype == np.uint16 else gen.FP32
+    plan = ts.ds_topk_plan(rows, n, k, dt, cfg)
+    wsb = ts.ds_topk_workspace_size(rows, n, k, dt, cfg)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+    xd = to_device(x)
+    ld = torch.from_numpy(lens).cuda() if lens is not None else None
+    sb = ts.stats_buffer(rows, plan["slices"], "cuda") if stats else None
+    say(f"[gpu] variants: rows={rows} n={n} k={k} dtype={x.dtype} cfg={cfg} plan={plan} lens={'yes' if lens is not None else 'no'}")
+    v, i = ts.ds_topk_ex(xd, k, seed=seed, workspace=ws, cfg=cfg, stats=sb, lens=ld)
+    torch.cuda.synchronize()
+    st = ts.decode_stats(sb).reshape(rows, plan["slices"]) if stats else None
+    return to_numpy_vals(v), i.cpu().numpy(), plan, st
+
+
+RAGGED = [
+    ("indexer-auto", "c2", gen.BF16, 64, 131072, 512, None),
+    ("indexer-merge-select", "c2", gen.BF16, 64, 131072, 512, {"merge": ts.MERGE_SELECT}),
+    ("bf16-one-slice", "normal", gen.BF16, 24, 20000, 64, {"slices": 1}),
+    ("fp32-two-slices", "sampler", gen.FP32, 16, 129280, 512, {"slices": 2}),
+    ("fp32-many-slices-k4096", "normal", gen.FP32, 14, 1 << 20, 4096, {"slices": 32}),
+    ("bf16-small-block", "ties", gen.BF16, 20, 70001, 100, {"block": 1024, "slices": 5}),
+]
+
+
+def _make(kind, dtype, rows, n, seed):
+    if kind == "c2":
+        return gen.WORKLOADS["c2_indexer"].make(rows=rows)
+    if kind == "sampler":
+        return gen.rows_sampler_f32(seed, rows, n)
+    return gen.rows_family(kind, dtype, seed, rows, n)
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
+def test_ragged_rows(case):
+    label, kind, dtype, rows, n, k, cfg = case
+    x = _make(kind, dtype, rows, n, 61)
+    plan = ts.ds_topk_plan(rows, n, k, dtype, cfg)
+    lens = _lens(rows, n, k, plan["block"], 62)
+    want = otk.topk_ragged(x, lens, k)
+    for seed in (1, 2):
+        gv, gi, plan, _ = _run(x, k, cfg, lens, seed=seed)
+        assert_same(x, k, gv, gi, want[0], want[1], f"ragged {label} seed={seed}")
+
+
+def test_ragged_rows_with_counters():
+    """The counting kernel on ragged rows: the same outputs, and a slice past its row's end
+    reads nothing and appends nothing."""
+    rows, n, k = 12, 65536, 256
+    x = gen.rows_family("normal", gen.BF16, 63, rows, n)
+    cfg = {"slices": 4, "block": 4096}
+    lens = _lens(rows, n, k, 4096, 64)
+    gv, gi, plan, st = _run(x, k, cfg, lens, stats=True)
+    wv, wi = otk.topk_ragged(x, lens, k)
+    assert_same(x, k, gv, gi, wv, wi, "ragged counters")
+    slice_len = n // plan["slices"]
+    for r in range(rows):
+        L = min(max(int(lens[r]), 0), n)
+        for s in range(plan["slices"]):
+            want_len = min(max(L - s * slice_len, 0), slice_len)
+            assert st[r, s]["slice_len"] == want_len
+            assert st[r, s]["reads"] == want_len
+            if want_len == 0:
+                assert st[r, s]["appended"] == 0 and st[r, s]["work"] == 0
+
+
+def test_ragged_full_lengths_equal_unragged():
+    x = gen.WORKLOADS["c2_indexer"].make(rows=8)
+    lens = np.full(8, x.shape[1], np.int32)
+    a = _run(x, 512, None, lens)
+    b = _run(x, 512, None, None)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[0], b[0])
+
+
+def _assert_same_set(x, k, gv, gi, want_idx, label):
+    if x.dtype == np.uint16:
+        xv = x
+    else:
+        xv = x.view(np.uint32)
+    got = np.sort(gi.astype(np.int64), axis=1)
+    assert np.array_equal(got, np.sort(want_idx.astype(np.int64), axis=1)), f"{label}: index sets differ"
+    vals = gv.view(xv.dtype)
+    assert np.array_equal(vals, np.take_along_axis(xv, gi.astype(np.int64), axis=1)), f"{label}: values off their indices"
+
+
+OUTPUTS = [
+    ("sampler-one-slice", "sampler", gen.FP32, 32, 129280, 512, {}),
+    ("indexer-lists", "c2", gen.BF16, 16, 131072, 512, {}),
+    ("indexer-merge-select", "c2", gen.BF16, 16, 131072, 512, {"merge": ts.MERGE_SELECT}),
+    ("k1", "normal", gen.BF16, 8, 40000, 1, {"slices": 1}),
+    ("ties-k4096", "ties", gen.FP32, 4, 300000, 4096, {"slices": 1}),
+]
+
+
+@pytest.mark.parametrize("case", OUTPUTS, ids=[c[0] for c in OUTPUTS])
+@pytest.mark.parametrize("flags", [ts.OUTPUT_UNSORTED, ts.OUTPUT_INDEX_INT64,
+                                   ts.OUTPUT_UNSORTED | ts.OUTPUT_INDEX_INT64])
+def test_output_variants(case, flags):
+    label, kind, dtype, rows, n, k, cfg = case
+    x = _make(kind, dtype, rows, n, 65)
+    cfg = dict(cfg, output=flags)
+    plan = ts.ds_topk_plan(rows, n, k, dtype, cfg)
+    assert plan["output"] == flags
+    gv, gi, _, _ = _run(x, k, cfg)
+    assert gi.dtype == (np.int64 if flags & ts.OUTPUT_INDEX_INT64 else np.int32)
+    wv, wi = otk.topk(x, k)
+    if flags & ts.OUTPUT_UNSORTED:
+        _assert_same_set(x, k, gv, gi, wi, f"{label} flags={flags}")
+    else:
+        assert_same(x, k, gv, gi, wv, wi.astype(gi.dtype), f"{label} flags={flags}")
+
+
+def test_ragged_int64_padding_reads_minus_one():
+    rows, n, k = 6, 5000, 300
+    x = gen.rows_family("normal", gen.FP32, 66, rows, n)
+    lens = np.array([0, 1, 299, 300, 301, 5000], np.int32)
+    gv, gi, _, _ = _run(x, k, {"slices": 1, "output": ts.OUTPUT_INDEX_INT64}, lens)
+    wv, wi = otk.topk_ragged(x, lens, k)
+    assert gi.dtype == np.int64
+    assert_same(x, k, gv, gi, wv, wi.astype(np.int64), "ragged int64")
+
+
+@pytest.mark.parametrize("merge", [ts.MERGE_LISTS, ts.MERGE_SELECT])
+def test_ragged_two_launches(merge):
+    """ds_topk_slices then ds_topk_merge with the same lengths equal one ds_topk_ex call."""
+    import torch
+    rows, n, k = 10, 100000, 700
+    x = gen.rows_family("normal", gen.BF16, 67, rows, n)
+    cfg = {"slices": 4, "merge": merge}
+    lens = _lens(rows, n, k, ts.ds_topk_plan(rows, n, k, gen.BF16, cfg)["block"], 68)
+    xd, ld = to_device(x), torch.from_numpy(lens).cuda()
+    ws = torch.empty(ts.ds_topk_workspace_size(rows, n, k, gen.BF16, cfg), dtype=torch.uint8, device="cuda")
+    vals = torch.empty((rows, k), dtype=xd.dtype, device="cuda")
+    idx = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    ts.ds_topk_slices(xd, k, seed=3, workspace=ws, cfg=cfg, out_vals=vals, out_idx=idx, lens=ld)
+    ts.ds_topk_merge(rows, n, k, gen.BF16, seed=3, workspace=ws, cfg=cfg, out_vals=vals, out_idx=idx, lens=ld)
+    torch.cuda.synchronize()
+    wv, wi = otk.topk_ragged(x, lens, k)
+    assert_same(x, k, to_numpy_vals(vals), idx.cpu().numpy(), wv, wi, f"ragged two launches merge={merge}")

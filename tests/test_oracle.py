@@ -139,3 +139,33 @@ def test_values_only_and_rejects():
         otk.topk(x, 101)
     with pytest.raises(ValueError):
         otk.topk(x, 0)
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+def test_ragged_rows_vs_brute(dtype):
+    """Ragged rows: each row's first L elements against the rank count with k' = min(k, L);
+    the positions past a short row's length are padding (index -1, value bits all ones)."""
+    g = np.random.default_rng(11)
+    rows, n, k = 40, 30, 9
+    vals = np.array(ALPHABET + [0.5, -0.5, 3.0], np.float32)[g.integers(0, 10, size=(rows, n))]
+    x = _as_dtype(vals, dtype)
+    lens = g.integers(-3, n + 4, size=rows)
+    lens[:4] = [0, 1, k, n]
+    v, i = otk.topk_ragged(x, lens, k)
+    pad = otk.padding_value(x.dtype)
+    for r in range(rows):
+        L = min(max(int(lens[r]), 0), n)
+        kk = min(k, L)
+        want = brute.brute_topk(list(_widen(x)[r, :L]), kk) if kk else []
+        assert i[r, :kk].tolist() == want
+        assert np.array_equal(v[r, :kk], x[r, want])
+        assert (i[r, kk:] == -1).all()
+        assert (v[r, kk:].view(pad.dtype) == pad).all() if dtype == gen.BF16 else \
+            (v[r, kk:].view(np.uint32) == 0xFFFFFFFF).all()
+
+
+def test_ragged_full_lengths_equal_plain_topk():
+    x = gen.rows_family("normal", gen.FP32, 12, 6, 5000)
+    v, i = otk.topk_ragged(x, np.full(6, 5000), 100)
+    wv, wi = otk.topk(x, 100)
+    assert np.array_equal(i, wi) and np.array_equal(v.view(np.uint32), wv.view(np.uint32))

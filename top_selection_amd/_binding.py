@@ -29,6 +29,7 @@ DS_NOALLOC_SCRATCH_BYTES = 8 << 20
 PRESAMPLE_AUTO, PRESAMPLE_OFF, PRESAMPLE_ON = 0, 1, 2
 MERGE_AUTO, MERGE_LISTS, MERGE_SELECT = 0, 1, 2
 SCHEDULE_AUTO, SCHEDULE_FREE, SCHEDULE_LOCKSTEP = 0, 1, 2
+OUTPUT_UNSORTED, OUTPUT_INDEX_INT64 = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdstopk.so")
@@ -45,7 +46,7 @@ class ds_config(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("slack", ctypes.c_int32), ("slices", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("presample", ctypes.c_int32), ("order_group", ctypes.c_int32),
                 ("merge", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("depth", ctypes.c_int32)]
+                ("depth", ctypes.c_int32), ("output", ctypes.c_int32)]
 
 
 STATS_FIELDS = ["appended", "compactions", "work", "max_len", "reads", "index_sum", "monotone", "slice_lo",
@@ -68,14 +69,14 @@ def lib() -> ctypes.CDLL:
             cfgp = ctypes.POINTER(ds_config)
             L.ds_topk.argtypes = [vp, i64, i64, i64, ci, ci, u64, vp, vp, vp]
             L.ds_topk.restype = ci
-            L.ds_topk_ex.argtypes = [vp, i64, i64, i64, ci, ci, u64, vp, vp, vp, ctypes.c_size_t, cfgp, vp, vp]
+            L.ds_topk_ex.argtypes = [vp, vp, i64, i64, i64, ci, ci, u64, vp, vp, vp, ctypes.c_size_t, cfgp, vp, vp]
             L.ds_topk_ex.restype = ci
             L.ds_topk_noalloc.argtypes = [vp, i64, i64, i64, ci, ci, u64, vp, vp, vp]
             L.ds_topk_noalloc.restype = ci
-            L.ds_topk_slices.argtypes = [vp, i64, i64, i64, ci, ci, u64, vp, vp, vp, ctypes.c_size_t, cfgp, vp,
-                                         vp]
+            L.ds_topk_slices.argtypes = [vp, vp, i64, i64, i64, ci, ci, u64, vp, vp, vp, ctypes.c_size_t, cfgp,
+                                         vp, vp]
             L.ds_topk_slices.restype = ci
-            L.ds_topk_merge.argtypes = [i64, i64, ci, ci, u64, vp, vp, vp, ctypes.c_size_t, cfgp, vp]
+            L.ds_topk_merge.argtypes = [vp, i64, i64, ci, ci, u64, vp, vp, vp, ctypes.c_size_t, cfgp, vp]
             L.ds_topk_merge.restype = ci
             L.ds_topk_plan.argtypes = [i64, i64, ci, ci, cfgp, cfgp]
             L.ds_topk_plan.restype = ci
@@ -109,7 +110,7 @@ def _cfg(cfg: Optional[Dict[str, int]]):
         return None
     c = ds_config(int(cfg.get("block", 0)), int(cfg.get("slack", 0)), int(cfg.get("slices", 0)),
                   int(cfg.get("waves", 0)), int(cfg.get("presample", 0)), int(cfg.get("order_group", 0)),
-                  int(cfg.get("merge", 0)), int(cfg.get("schedule", 0)))
+                  int(cfg.get("merge", 0)), int(cfg.get("schedule", 0)), 0, int(cfg.get("output", 0)))
     return ctypes.pointer(c)
 
 
@@ -120,7 +121,7 @@ def ds_topk_plan(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, 
         raise DSError(st, "ds_topk_plan")
     return {"block": out.block, "slack": out.slack, "slices": out.slices, "waves": out.waves,
             "presample": out.presample, "order_group": out.order_group, "merge": out.merge,
-            "schedule": out.schedule, "depth": out.depth}
+            "schedule": out.schedule, "depth": out.depth, "output": out.output}
 
 
 def ds_topk_workspace_size(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, int]] = None) -> int:
@@ -152,7 +153,7 @@ def _stream_handle(stream) -> Optional[int]:
     return s.cuda_stream
 
 
-def _prep(x, k: int, values: bool, indices: bool, out_vals, out_idx):
+def _prep(x, k: int, values: bool, indices: bool, out_vals, out_idx, idx64: bool = False):
     torch = _torch()
     if x.dim() != 2:
         raise ValueError("x must be 2-D [rows, N]")
@@ -164,11 +165,12 @@ def _prep(x, k: int, values: bool, indices: bool, out_vals, out_idx):
     dt = dtype_code(x)
     if values and out_vals is None:
         out_vals = torch.empty((rows, k), dtype=x.dtype, device=x.device)
+    idt = torch.int64 if idx64 else torch.int32
     if indices and out_idx is None:
-        out_idx = torch.empty((rows, k), dtype=torch.int32, device=x.device)
-    for o, want in ((out_vals, x.dtype), (out_idx, torch.int32)):
+        out_idx = torch.empty((rows, k), dtype=idt, device=x.device)
+    for o, want in ((out_vals, x.dtype), (out_idx, idt)):
         if o is not None and (o.dtype != want or not o.is_contiguous() or tuple(o.shape) != (rows, k)):
-            raise ValueError("outputs must be contiguous [rows, k] of the input dtype / int32")
+            raise ValueError("outputs must be contiguous [rows, k] of the input dtype / the index type")
     row_stride = x.stride(0) if rows > 0 else n
     return rows, n, row_stride, dt, out_vals, out_idx
 
@@ -204,14 +206,30 @@ def ds_topk_noalloc(x, k: int, seed: int = 0, values: bool = True, indices: bool
     return out_vals, out_idx
 
 
+def _idx64(cfg) -> bool:
+    return bool(cfg and int(cfg.get("output", 0)) & OUTPUT_INDEX_INT64)
+
+
+def _lens_ptr(lens, rows: int):
+    if lens is None:
+        return None
+    torch = _torch()
+    if not lens.is_cuda or lens.dtype != torch.int32 or not lens.is_contiguous() or lens.numel() != rows:
+        raise ValueError("lens must be a contiguous device int32 tensor of one length per row")
+    return lens.data_ptr()
+
+
 def ds_topk_ex(x, k: int, seed: int = 0, workspace=None, cfg: Optional[Dict[str, int]] = None, stats=None,
-               values: bool = True, indices: bool = True, out_vals=None, out_idx=None, stream=None):
-    """ds_topk with a caller workspace (a device tensor), forced config and optional stats
-    (a device uint8 tensor of rows*slices*128 bytes). Allocates nothing itself."""
-    rows, n, rs, dt, out_vals, out_idx = _prep(x, k, values, indices, out_vals, out_idx)
+               values: bool = True, indices: bool = True, out_vals=None, out_idx=None, stream=None, lens=None):
+    """ds_topk with a caller workspace (a device tensor), forced config (including the output
+    flags), optional stats (a device uint8 tensor of rows*slices*128 bytes) and optional
+    per-row lengths (a device int32 tensor [rows]). Allocates nothing itself beyond the
+    outputs it is not given."""
+    rows, n, rs, dt, out_vals, out_idx = _prep(x, k, values, indices, out_vals, out_idx, _idx64(cfg))
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
-    st = lib().ds_topk_ex(x.data_ptr() if rows else None, rows, n, rs, k, dt, seed & 0xFFFFFFFFFFFFFFFF,
+    st = lib().ds_topk_ex(x.data_ptr() if rows else None, _lens_ptr(lens, rows), rows, n, rs, k, dt,
+                          seed & 0xFFFFFFFFFFFFFFFF,
                           out_vals.data_ptr() if out_vals is not None else None,
                           out_idx.data_ptr() if out_idx is not None else None, ws_ptr, ws_bytes, _cfg(cfg),
                           stats.data_ptr() if stats is not None else None, _stream_handle(stream))
@@ -221,12 +239,13 @@ def ds_topk_ex(x, k: int, seed: int = 0, workspace=None, cfg: Optional[Dict[str,
 
 
 def ds_topk_slices(x, k: int, seed: int = 0, workspace=None, cfg: Optional[Dict[str, int]] = None, stats=None,
-                   out_vals=None, out_idx=None, values: bool = True, indices: bool = True, stream=None):
+                   out_vals=None, out_idx=None, values: bool = True, indices: bool = True, stream=None, lens=None):
     """First launch of ds_topk_ex (the select kernel); returns the outputs it may fill."""
-    rows, n, rs, dt, out_vals, out_idx = _prep(x, k, values, indices, out_vals, out_idx)
+    rows, n, rs, dt, out_vals, out_idx = _prep(x, k, values, indices, out_vals, out_idx, _idx64(cfg))
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
-    st = lib().ds_topk_slices(x.data_ptr() if rows else None, rows, n, rs, k, dt, seed & 0xFFFFFFFFFFFFFFFF,
+    st = lib().ds_topk_slices(x.data_ptr() if rows else None, _lens_ptr(lens, rows), rows, n, rs, k, dt,
+                              seed & 0xFFFFFFFFFFFFFFFF,
                               out_vals.data_ptr() if out_vals is not None else None,
                               out_idx.data_ptr() if out_idx is not None else None, ws_ptr, ws_bytes, _cfg(cfg),
                               stats.data_ptr() if stats is not None else None, _stream_handle(stream))
@@ -236,11 +255,11 @@ def ds_topk_slices(x, k: int, seed: int = 0, workspace=None, cfg: Optional[Dict[
 
 
 def ds_topk_merge(rows: int, n: int, k: int, dtype: int, seed: int = 0, workspace=None,
-                  cfg: Optional[Dict[str, int]] = None, out_vals=None, out_idx=None, stream=None):
+                  cfg: Optional[Dict[str, int]] = None, out_vals=None, out_idx=None, stream=None, lens=None):
     """Second launch of ds_topk_ex (the merge kernel) into the given output tensors."""
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
-    st = lib().ds_topk_merge(rows, n, k, dtype, seed & 0xFFFFFFFFFFFFFFFF,
+    st = lib().ds_topk_merge(_lens_ptr(lens, rows), rows, n, k, dtype, seed & 0xFFFFFFFFFFFFFFFF,
                              out_vals.data_ptr() if out_vals is not None else None,
                              out_idx.data_ptr() if out_idx is not None else None, ws_ptr, ws_bytes, _cfg(cfg),
                              _stream_handle(stream))

@@ -56,6 +56,8 @@ struct Plan {
   bool presample;   // the first whole block sets a presampled threshold
   int order_group;  // G: the random order is over groups of G consecutive blocks
   bool lockstep;    // the design note's schedule: a barrier and the buffer check after every block
+  bool unsorted;    // the outputs may hold the top k in any order (DS_OUTPUT_UNSORTED)
+  bool idx64;       // int64 output indices (DS_OUTPUT_INDEX_INT64)
   // merge (slices > 1): DS_MERGE_LISTS (levels of the list-merge kernel over sorted slice
   // lists, group[l] lists merged together at level l) or DS_MERGE_SELECT (the merge kernel)
   int merge;
@@ -95,7 +97,7 @@ int check_basic(int64_t rows, int64_t n, int k, int dtype) {
 int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK) return st;
-  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0, 0, 0};
+  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (c.block < 0 || c.slack < 0 || c.slices < 0 || c.waves < 0) return DS_ERR_INVALID_ARG;
   if (c.presample != DS_PRESAMPLE_AUTO && c.presample != DS_PRESAMPLE_OFF && c.presample != DS_PRESAMPLE_ON)
     return DS_ERR_INVALID_ARG;
@@ -105,6 +107,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   if (c.schedule != DS_SCHEDULE_AUTO && c.schedule != DS_SCHEDULE_FREE && c.schedule != DS_SCHEDULE_LOCKSTEP)
     return DS_ERR_INVALID_ARG;
   if (c.depth != 0) return DS_ERR_INVALID_ARG;  // reported by the plan, never forced
+  if ((c.output & ~(DS_OUTPUT_UNSORTED | DS_OUTPUT_INDEX_INT64)) != 0) return DS_ERR_INVALID_ARG;
   const int chunk = chunk_elems(dtype);
   const int eb = elem_bytes(dtype);
 
@@ -206,6 +209,8 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   // keep single blocks, which randomise adversarial (sorted) slices better
   p.order_group = c.order_group ? c.order_group : ((slice_len + block - 1) / block >= 8 ? 2 : 1);
   p.lockstep = c.schedule == DS_SCHEDULE_LOCKSTEP;
+  p.unsorted = (c.output & DS_OUTPUT_UNSORTED) != 0;
+  p.idx64 = (c.output & DS_OUTPUT_INDEX_INT64) != 0;
   if (slices > 1) {
     const int64_t entries = slices * static_cast<int64_t>(k);
     if (entries * 8 > kMaxSliceBytes) return DS_ERR_UNSUPPORTED;
@@ -248,7 +253,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
 }
 
 int check_call(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, const void* out_vals,
-               const int32_t* out_idx) {
+               const void* out_idx) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK) return st;
   if (row_stride < n) return DS_ERR_INVALID_ARG;
@@ -260,13 +265,14 @@ int check_call(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k
   return DS_OK;
 }
 
-int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, uint64_t seed,
-               void* out_vals, int32_t* out_idx, void* ws, ds_stats* stats, hipStream_t stream) {
+int run_select(const Plan& pl, const void* x, const int32_t* lens, int64_t rows, int64_t n, int64_t row_stride, int k,
+               uint64_t seed, void* out_vals, void* out_idx, void* ws, ds_stats* stats, hipStream_t stream) {
   (void)hipGetLastError();  // clear a stale error so a launch failure is reported as ours
   ds::SelectParams sp{};
   sp.x = static_cast<const uint8_t*>(x);
   sp.row_stride_bytes = row_stride * elem_bytes(pl.dtype);
   sp.n = n;
+  sp.lens = lens;
   sp.slice_len = pl.slice_len;
   sp.slices = pl.slices;
   sp.k = k;
@@ -276,17 +282,18 @@ int run_select(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t r
   sp.ws = static_cast<uint2*>(ws);
   sp.ws_row_entries = pl.ws_row_a;
   sp.out_vals = out_vals;
-  sp.out_idx = out_idx;
+  sp.out_idx = ds::IdxOut{out_idx, pl.idx64 ? 1 : 0};
   sp.stats = stats;
   sp.sorted_lists = pl.merge == DS_MERGE_LISTS ? 1 : 0;
   sp.presample = pl.presample ? 1 : 0;
   sp.group_shift = pl.order_group == 4 ? 2 : (pl.order_group == 2 ? 1 : 0);
   sp.lockstep = pl.lockstep ? 1 : 0;
+  sp.unsorted = pl.unsorted && pl.slices == 1 ? 1 : 0;
   return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }
 
-int run_merge(const Plan& pl, int64_t rows, int64_t n, int k, uint64_t seed, void* out_vals, int32_t* out_idx,
-              void* ws, hipStream_t stream) {
+int run_merge(const Plan& pl, const int32_t* lens, int64_t rows, int64_t n, int k, uint64_t seed, void* out_vals,
+              void* out_idx, void* ws, hipStream_t stream) {
   if (pl.slices <= 1) return DS_OK;
   (void)hipGetLastError();
   ds::MergeParams mp{};
@@ -294,12 +301,15 @@ int run_merge(const Plan& pl, int64_t rows, int64_t n, int k, uint64_t seed, voi
   mp.entries = static_cast<int64_t>(pl.slices) * k;
   mp.row_entries = (mp.entries + 1) & ~int64_t(1);
   mp.n = n;
+  mp.lens = lens;
+  mp.slice_len = pl.slice_len;
   mp.k = k;
   mp.slack = pl.mslack;
   mp.sort_cap = pl.sort_cap;
   mp.seed = seed;
   mp.out_vals = out_vals;
-  mp.out_idx = out_idx;
+  mp.out_idx = ds::IdxOut{out_idx, pl.idx64 ? 1 : 0};
+  mp.unsorted = pl.unsorted ? 1 : 0;
   mp.presample = pl.presample && k <= 64 * ds::kMergeShape.waves ? 1 : 0;
   if (pl.merge == DS_MERGE_SELECT)
     return ds::launch_merge(pl.dtype, mp, rows, pl.mlds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
@@ -323,11 +333,11 @@ int run_merge(const Plan& pl, int64_t rows, int64_t n, int k, uint64_t seed, voi
   return DS_OK;
 }
 
-int run(const Plan& pl, const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, uint64_t seed,
-        void* out_vals, int32_t* out_idx, void* ws, ds_stats* stats, hipStream_t stream) {
-  int st = run_select(pl, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, stats, stream);
+int run(const Plan& pl, const void* x, const int32_t* lens, int64_t rows, int64_t n, int64_t row_stride, int k,
+        uint64_t seed, void* out_vals, void* out_idx, void* ws, ds_stats* stats, hipStream_t stream) {
+  int st = run_select(pl, x, lens, rows, n, row_stride, k, seed, out_vals, out_idx, ws, stats, stream);
   if (st != DS_OK) return st;
-  return run_merge(pl, rows, n, k, seed, out_vals, out_idx, ws, stream);
+  return run_merge(pl, lens, rows, n, k, seed, out_vals, out_idx, ws, stream);
 }
 
 // Plan a call that brings its own workspace; validates the workspace against the plan.
@@ -415,7 +425,8 @@ int topk_auto(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k,
     st = get_ws(p.ws_bytes, stream, &ws);
     if (st != DS_OK) return st;
   }
-  return run(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, ws, nullptr, static_cast<hipStream_t>(stream));
+  return run(p, x, nullptr, rows, n, row_stride, k, seed, out_vals, out_idx, ws, nullptr,
+             static_cast<hipStream_t>(stream));
 }
 
 }  // namespace ds
@@ -456,6 +467,7 @@ int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg
   out->merge = p.slices > 1 ? p.merge : DS_MERGE_AUTO;
   out->schedule = p.lockstep ? DS_SCHEDULE_LOCKSTEP : DS_SCHEDULE_FREE;
   out->depth = ds::depth_for(kSelectShapes[p.shape].waves, kSelectShapes[p.shape].cpw);
+  out->output = (p.unsorted ? DS_OUTPUT_UNSORTED : 0) | (p.idx64 ? DS_OUTPUT_INDEX_INT64 : 0);
   return DS_OK;
 }
 
@@ -475,39 +487,39 @@ int ds_topk_workspace_size(int64_t rows, int64_t n, int k, int dtype, const ds_c
   return DS_OK;
 }
 
-int ds_topk_ex(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
-               void* out_vals, int32_t* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
+int ds_topk_ex(const void* x, const int32_t* lens, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype,
+               uint64_t seed, void* out_vals, void* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
                ds_stats* stats, void* stream) {
   int st = check_call(x, rows, n, row_stride, k, dtype, out_vals, out_idx);
   if (st != DS_OK || rows == 0) return st;
   Plan p;
   st = plan_with_workspace(rows, n, k, dtype, cfg, workspace, ws_bytes, &p);
   if (st != DS_OK) return st;
-  return run(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, workspace, stats,
+  return run(p, x, lens, rows, n, row_stride, k, seed, out_vals, out_idx, workspace, stats,
              static_cast<hipStream_t>(stream));
 }
 
-int ds_topk_slices(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,
-                   void* out_vals, int32_t* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg,
-                   ds_stats* stats, void* stream) {
+int ds_topk_slices(const void* x, const int32_t* lens, int64_t rows, int64_t n, int64_t row_stride, int k,
+                   int dtype, uint64_t seed, void* out_vals, void* out_idx, void* workspace, size_t ws_bytes,
+                   const ds_config* cfg, ds_stats* stats, void* stream) {
   int st = check_call(x, rows, n, row_stride, k, dtype, out_vals, out_idx);
   if (st != DS_OK || rows == 0) return st;
   Plan p;
   st = plan_with_workspace(rows, n, k, dtype, cfg, workspace, ws_bytes, &p);
   if (st != DS_OK) return st;
-  return run_select(p, x, rows, n, row_stride, k, seed, out_vals, out_idx, workspace, stats,
+  return run_select(p, x, lens, rows, n, row_stride, k, seed, out_vals, out_idx, workspace, stats,
                     static_cast<hipStream_t>(stream));
 }
 
-int ds_topk_merge(int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void* out_vals, int32_t* out_idx,
-                  void* workspace, size_t ws_bytes, const ds_config* cfg, void* stream) {
+int ds_topk_merge(const int32_t* lens, int64_t rows, int64_t n, int k, int dtype, uint64_t seed, void* out_vals,
+                  void* out_idx, void* workspace, size_t ws_bytes, const ds_config* cfg, void* stream) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK || rows == 0) return st;
   if (!out_vals && !out_idx) return DS_ERR_INVALID_ARG;
   Plan p;
   st = plan_with_workspace(rows, n, k, dtype, cfg, workspace, ws_bytes, &p);
   if (st != DS_OK) return st;
-  return run_merge(p, rows, n, k, seed, out_vals, out_idx, workspace, static_cast<hipStream_t>(stream));
+  return run_merge(p, lens, rows, n, k, seed, out_vals, out_idx, workspace, static_cast<hipStream_t>(stream));
 }
 
 int ds_topk(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, uint64_t seed,

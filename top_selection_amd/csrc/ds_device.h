@@ -601,7 +601,7 @@ __device__ __forceinline__ void ties_all(const Segs& sg, uint32_t tid, uint32_t 
 // Stores entry c (a composite) at position `at` of the outputs, or, with pairs, as a (key,
 // index) pair at pairs[at].
 template <int DT>
-__device__ __forceinline__ void store_out(void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t at, uint64_t c) {
+__device__ __forceinline__ void store_out(void* out_vals, IdxOut out_idx, uint2* pairs, uint64_t at, uint64_t c) {
   const uint32_t key = static_cast<uint32_t>(c >> 32), id = ~static_cast<uint32_t>(c);
   if (pairs) {
     pairs[at] = make_uint2(key, id);
@@ -613,14 +613,19 @@ __device__ __forceinline__ void store_out(void* out_vals, int32_t* out_idx, uint
     else
       static_cast<uint32_t*>(out_vals)[at] = raw_of_key<DT>(key);
   }
-  if (out_idx) out_idx[at] = static_cast<int32_t>(id);
+  if (out_idx.p) {
+    if (out_idx.wide)  // sign-extended: padding (index ~0) reads -1 in either width
+      static_cast<int64_t*>(out_idx.p)[at] = static_cast<int64_t>(static_cast<int32_t>(id));
+    else
+      static_cast<int32_t*>(out_idx.p)[at] = static_cast<int32_t>(id);
+  }
 }
 
 // Where a final compaction may write its survivors directly, sorted: row `row` of the
 // outputs, or pairs[row * k ...] when pairs is set.
 struct OutSpec {
   void* vals;
-  int32_t* idx;
+  IdxOut idx;
   uint2* pairs;
   uint64_t row;
 };
@@ -1002,7 +1007,7 @@ constexpr int bitonic_barriers() {
 // (fk, fi) and hold 2^LOGT words each.
 template <int DT, int WAVES, uint32_t LOGT>
 __device__ __forceinline__ void sort_store_t(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi, uint32_t k,
-                             void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t row) {
+                             void* out_vals, IdxOut out_idx, uint2* pairs, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64, TOTAL = 1u << LOGT;
   constexpr uint32_t TH = TOTAL > NT ? NT : TOTAL;
   constexpr int E = static_cast<int>(TOTAL / TH);
@@ -1030,7 +1035,7 @@ __device__ __forceinline__ void sort_store_t(const uint32_t* fk, const uint32_t*
 // (a power of two >= k) composites held as (xk, xi) halves, best first, and stores the first k.
 template <int DT, int WAVES>
 __device__ __forceinline__ void sort_store_lds(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi, uint32_t k,
-                               uint32_t cap, void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t row) {
+                               uint32_t cap, void* out_vals, IdxOut out_idx, uint2* pairs, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < cap; i += NT) {
@@ -1086,7 +1091,7 @@ __device__ __forceinline__ uint64_t wave_sort64(uint64_t v, uint32_t lane) {
 
 template <int DT, int WAVES, uint32_t RUNS>
 __device__ __forceinline__ void sort_runs_store(const uint32_t* fk, const uint32_t* fi, uint64_t* xs, uint32_t k,
-                                                void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t row) {
+                                                void* out_vals, IdxOut out_idx, uint2* pairs, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64, N = 64 * RUNS;
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   if constexpr (RUNS == 1) {
@@ -1139,7 +1144,7 @@ __device__ __forceinline__ void sort_runs_store(const uint32_t* fk, const uint32
 // with pairs, to pairs[row * k ...].
 template <int DT, int WAVES>
 __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_t* fi, uint32_t* xk, uint32_t* xi,
-                                               uint64_t* xs, uint32_t k, void* out_vals, int32_t* out_idx,
+                                               uint64_t* xs, uint32_t k, void* out_vals, IdxOut out_idx,
                                                uint2* pairs, uint64_t row) {
   constexpr uint32_t NT = WAVES * 64;
   if (k <= 64u * kMaxRuns) {
@@ -1193,7 +1198,7 @@ __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_
 // (all lists are loaded and searched).
 template <int DT, int WAVES, uint32_t MAXS>
 __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint32_t k, uint32_t pk, uint64_t* lds,
-                                              void* out_vals, int32_t* out_idx, uint2* pairs, uint64_t at0,
+                                              void* out_vals, IdxOut out_idx, uint2* pairs, uint64_t at0,
                                               uint32_t l0, uint32_t l1) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x, total = S * k;
@@ -1844,12 +1849,40 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   uint32_t row, slice;
   xcd_unit(blockIdx.x, static_cast<uint32_t>(p.slices), gridDim.x / static_cast<uint32_t>(p.slices), row, slice);
   const uint32_t slice_lo = slice * static_cast<uint32_t>(p.slice_len);
-  const uint32_t len = static_cast<uint32_t>(min(p.slice_len, p.n - static_cast<int64_t>(slice_lo)));
+  int64_t n_row = p.n;  // this row's length
+  if (p.lens) {
+    const int64_t l = p.lens[row];
+    n_row = l < 0 ? 0 : (l < n_row ? l : n_row);
+  }
+  const int64_t rest = n_row - static_cast<int64_t>(slice_lo);
+  const uint32_t len = rest <= 0 ? 0u : static_cast<uint32_t>(min(p.slice_len, rest));
   const uint32_t m = (len + B - 1) / B;
   const uint32_t k = static_cast<uint32_t>(p.k);
   const uint32_t B2 = static_cast<uint32_t>(p.slack);
   [[maybe_unused]] uint64_t t_start = 0;
   if constexpr (STATS) t_start = wall_clock64();
+
+  if (len == 0) {
+    // a slice past its row's end (ragged rows): its k entries are all padding, which ranks
+    // below every element (the row's outputs past its length read index -1)
+    if (p.slices == 1) {
+      for (uint32_t i = tid; i < k; i += NT) store_out<DT>(p.out_vals, p.out_idx, nullptr, static_cast<uint64_t>(row) * k + i, 0ull);
+    } else {
+      uint2* const dst = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + static_cast<uint64_t>(slice) * k;
+      for (uint32_t i = tid; i < k; i += NT) dst[i] = make_uint2(0u, kSentinelIdx);
+    }
+    if constexpr (STATS) {
+      if (tid == 0) {
+        ds_stats* o = p.stats + (row * static_cast<uint32_t>(p.slices) + slice);
+        *o = ds_stats{};
+        o->monotone = 1;
+        o->slice_lo = slice_lo;
+        o->block = B;
+        o->slack = B2;
+      }
+    }
+    return;
+  }
 
   const Lay L = lay_of(lds, k, B2, B);
 
@@ -1866,7 +1899,8 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   // the final compaction writes the sorted output itself when it can: the row's outputs, or
   // the slice's sorted list for the list merge
   OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
-  if (p.slices > 1) fso = OutSpec{nullptr, nullptr, p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + slice * k, 0};
+  if (p.slices > 1)
+    fso = OutSpec{nullptr, IdxOut{nullptr, 0}, p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + slice * k, 0};
   const bool own_sort = p.slices == 1 || p.sorted_lists;
 
   BodyOut bo;
@@ -1908,6 +1942,10 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
 
   if (bo.sorted) {
     // done by the final compaction
+  } else if (p.slices == 1 && p.unsorted) {
+    // the k survivors as the final compaction left them (no sort)
+    for (uint32_t i = tid; i < k; i += NT)
+      store_out<DT>(p.out_vals, p.out_idx, nullptr, static_cast<uint64_t>(row) * k + i, comp_of(bo.fk[i], bo.fi[i]));
   } else if (p.slices == 1) {
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
                               p.out_vals, p.out_idx, nullptr, row);
@@ -1918,7 +1956,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
     // the list-merge kernel merges the slices' sorted lists
     uint2* const rws = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries;
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k, nullptr,
-                              nullptr, rws + slice * k, 0);
+                              IdxOut{nullptr, 0}, rws + slice * k, 0);
   }
   if constexpr (STATS) {
     if (tid == 0) {
@@ -1951,6 +1989,37 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   const uint2* base = p.ws + static_cast<uint64_t>(row) * p.row_entries;  // rows padded to 16 bytes
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint2*>(base), 0, static_cast<int>((len * 8u + 15u) & ~15u), kRsrcWord3);
+  if (p.lens) {
+    // A ragged row shorter than k: every one of its elements survived in its slice (the
+    // first entries of each slice's list, the rest padding), so they are gathered, padded
+    // to k and sorted, without a selection.
+    const int64_t l = p.lens[row];
+    const int64_t n_row = l < 0 ? 0 : (l < p.n ? l : p.n);
+    if (n_row < static_cast<int64_t>(k)) {
+      const uint32_t S = len / k;
+      uint32_t at = 0;
+      for (uint32_t s = 0; s < S; ++s) {
+        const int64_t rest = n_row - static_cast<int64_t>(s) * p.slice_len;
+        if (rest <= 0) break;  // slices are consecutive ranges: the rest are empty
+        const uint32_t ls = static_cast<uint32_t>(rest < p.slice_len ? rest : p.slice_len);  // < k
+        for (uint32_t i = tid; i < ls; i += NT) {
+          const uint2 e = base[static_cast<uint64_t>(s) * k + i];
+          L.ck[at + i] = e.x;
+          L.ci[at + i] = e.y;
+        }
+        at += ls;
+      }
+      for (uint32_t i = at + tid; i < k; i += NT) {
+        L.ck[i] = 0u;
+        L.ci[i] = kSentinelIdx;
+      }
+      lds_sync();
+      sort_and_store<DT, WAVES>(L.ck, L.ci, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
+                                p.out_vals, p.out_idx, nullptr, row);
+      return;
+    }
+  }
+
   BlockOrder ord;
   ord.init(p.seed, row, 0x7FFFFFFFu, m);
 
@@ -1959,9 +2028,14 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), true, false>(L, sc, rs, len, 0u, k, B2, ord, 0u,
                                                                   static_cast<uint32_t>(p.n - 1), false,
                                                                   p.presample != 0, 0u, &fso, bo);
-  if (!bo.sorted)
+  if (bo.sorted) return;
+  if (p.unsorted) {
+    for (uint32_t i = tid; i < k; i += NT)
+      store_out<DT>(p.out_vals, p.out_idx, nullptr, static_cast<uint64_t>(row) * k + i, comp_of(bo.fk[i], bo.fi[i]));
+  } else {
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
                               p.out_vals, p.out_idx, nullptr, row);
+  }
 }
 
 // --------------------------------------------------------------------------- list-merge kernel

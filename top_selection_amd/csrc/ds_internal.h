@@ -10,12 +10,19 @@
 
 namespace ds {
 
+// An index output, [rows][k] int32, or int64 when `wide` (NULL: no index output).
+struct IdxOut {
+  void* p;
+  int32_t wide;
+};
+
 // One workgroup runs DeepSelect over one slice [slice*slice_len, min(n, (slice+1)*slice_len))
 // of one row. Candidates live in LDS as (key, index) pairs.
 struct SelectParams {
   const uint8_t* x;          // row 0, slice 0
   int64_t row_stride_bytes;  // bytes between rows
-  int64_t n;                 // elements per row
+  int64_t n;                 // elements per row (the longest row when lens is set)
+  const int32_t* lens;       // NULL, or row r holds min(max(lens[r], 0), n) elements
   int64_t slice_len;         // elements per slice, a multiple of the block size
   int32_t slices;            // workgroups per row
   int32_t k;
@@ -24,13 +31,14 @@ struct SelectParams {
   uint64_t seed;
   uint2* ws;                 // slices > 1: survivors, row r at ws + r*ws_row_entries, slice s at +s*k
   int64_t ws_row_entries;    // slices*k rounded up to even (16-byte rows)
-  void* out_vals;            // slices == 1: sorted output values [rows][k]
-  int32_t* out_idx;          // slices == 1: sorted output indices [rows][k]
+  void* out_vals;            // slices == 1: output values [rows][k]
+  IdxOut out_idx;            // slices == 1: output indices [rows][k]
   ds_stats* stats;           // NULL or [rows][slices]
   int32_t sorted_lists;      // slices > 1: store each slice's survivors sorted (for the list merge)
   int32_t presample;         // nonzero: the first whole block sets a presampled threshold
   int32_t group_shift;       // log2 of G: the block order is random over groups of G blocks
   int32_t lockstep;          // nonzero: a barrier and the buffer check after every block
+  int32_t unsorted;          // slices == 1: the k survivors may be written in any order
 };
 
 // The merge of split rows. The merge kernel: one workgroup per row runs DeepSelect over the
@@ -44,13 +52,16 @@ struct MergeParams {
   int64_t entries;     // slices * k
   int64_t row_entries; // entries rounded up to even (16-byte rows)
   int64_t n;           // row length (indices lie in [0, n))
+  const int32_t* lens; // NULL, or ragged rows as in SelectParams
+  int64_t slice_len;   // elements per slice
   int32_t k;
   int32_t slack;
   int32_t sort_cap;
   uint64_t seed;
   void* out_vals;
-  int32_t* out_idx;
+  IdxOut out_idx;
   int32_t presample;   // nonzero: the first whole block sets a presampled threshold
+  int32_t unsorted;    // merge kernel: the k survivors may be written in any order
   uint2* dst;
   int64_t dst_row_entries;
   int32_t lists;
