@@ -128,6 +128,37 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
     def select_only(src):
         ts.ds_topk_slices(src, k, seed=seed, workspace=ws, out_vals=vals, out_idx=idx, indices=idx is not None)
 
+    def per_call_times(get_src):
+        """Each step's own duration: K steps in one graph with an event recorded between
+        consecutive steps (event record nodes); eager launches between events if the graph
+        cannot hold such nodes. Returns (list of us, method)."""
+        try:
+            evs = [torch.cuda.Event(enable_timing=True, external=True) for _ in range(steps + 1)]
+            gs = torch.cuda.Stream()
+            gs.wait_stream(stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                evs[0].record(gs)
+                for i in range(steps):
+                    step(get_src(i))
+                    evs[i + 1].record(gs)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps)]
+            return us, "one HIP graph of K steps with an event record node between consecutive steps"
+        except Exception as e:  # noqa: BLE001 (the fallback names the reason)
+            log(f"[bench] graph events unavailable ({e}); timing eager steps")
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            torch.cuda.synchronize()
+            evs[0].record(stream)
+            for i in range(steps):
+                step(get_src(i))
+                evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+            return [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps)], "eager steps between events"
+
     def graph_timed(get_src, fn=step):
         """K steps (or K launches of fn) captured into one graph, replayed once between two
         events; returns ms per step."""
@@ -162,6 +193,11 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
     # the select kernel alone, back to back in a graph: its average duration per launch
     ms_select = graph_timed(lambda i: pool[i % copies], select_only)
     log(f"[bench] {w.name} select kernel (graph, cold): {ms_select * 1e3:.2f} us/launch")
+    # the read ceiling: the probe streams the same bytes with the scan's loads, same pool
+    sink = torch.empty(int(ts.lib().ds_probe_sink_words(in_bytes)), dtype=torch.int32, device="cuda")
+    ms_probe = graph_timed(lambda i: pool[i % copies], lambda src: ts.ds_probe_read(src, sink=sink))
+    log(f"[bench] {w.name} probe read (graph, cold): {ms_probe * 1e3:.2f} us/read")
+    per_call = per_call_times(lambda i: pool[i % copies])
 
     parity = None
     if verify:
@@ -178,10 +214,21 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
     del pool
     return dict(x=x, plan=plan, copies=copies, ms_cold=ms_graph, ms_eager=ms_cold, sel_cold=ms_select, sel_eager=sel_cold,
                 ms_warm=ms_graph_warm, ms_warm_eager=ms_warm, sel_warm=sel_warm, in_bytes=in_bytes, parity=parity,
-                ws_bytes=wsb)
+                ws_bytes=wsb, ms_probe=ms_probe, per_call=per_call)
+
+
+def percentiles(us_method):
+    import numpy as np
+    us, method = us_method
+    a = np.asarray(us)
+    return {"p10": round(float(np.percentile(a, 10)), 3), "p50": round(float(np.percentile(a, 50)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3), "unit": "us", "calls": int(a.size), "method": method}
 
 
 CALIB_BYTES = 256 * 2 ** 20  # calibration copy: reads and writes exactly this many bytes
+
+# the other workloads timed on every run: (workload, k, timed steps at most)
+SECONDARY = [("c3_sampler", 512, 100), ("c4_long", 512, 100), ("c4_long", 4096, 50), ("c5_giant", 32, 50)]
 
 
 def counter_pass(ts, torch, w, k, launches, pool_mib):
@@ -279,6 +326,60 @@ def write_counters(workload, fetch_dir, write_dir, command):
     log(f"[bench] wrote {path}: {total:.0f} B per launch ({total / algo:.3f} x algorithmic)")
 
 
+SQ_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_ANY",
+               "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES"]
+
+
+def write_sq(workload, k, folder, command):
+    """Summary of one rocprofv3 --pmc run of the SQ counters over the select kernel."""
+    from workloads import gen
+    w = gen.WORKLOADS[workload]
+    vals = {c: read_counter_csv(folder, c)["select"] for c in SQ_COUNTERS}
+    missing = [c for c, (v, _) in vals.items() if v is None]
+    if missing:
+        raise SystemExit(f"counter tables lack {missing} for the select kernel")
+    m = {c: v for c, (v, _) in vals.items()}
+    elems = w.rows * w.n
+    lines = [
+        f"# select_kernel SQ counters, {workload} (k = {k})",
+        "",
+        f"Workload: {w.description}. Elements per launch: {elems}.",
+        "",
+        "Command (rocprofv3 on one MI355X, one --pmc run; R is the repository path):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| counter | mean per select dispatch | dispatches |",
+        "|---|---|---|",
+    ]
+    for c in SQ_COUNTERS:
+        lines.append(f"| {c} | {m[c]:.0f} | {vals[c][1]} |")
+    lines += [
+        "",
+        "Derived (per dispatch):",
+        "",
+        f"- VALU wave-instructions per 64 elements (each lane's VALU instructions per element it holds): "
+        f"{m['SQ_INSTS_VALU'] / (elems / 64.0):.2f}",
+        f"- SALU instructions per 64 elements: {m['SQ_INSTS_SALU'] / (elems / 64.0):.2f}; LDS instructions per 64 "
+        f"elements: {m['SQ_INSTS_LDS'] / (elems / 64.0):.2f}",
+        f"- LDS bank-conflict cycles per LDS instruction: {m['SQ_LDS_BANK_CONFLICT'] / max(m['SQ_INSTS_LDS'], 1):.3f}",
+        f"- waves resident on average (SQ_WAVE_CYCLES / SQ_BUSY_CYCLES): "
+        f"{m['SQ_WAVE_CYCLES'] / max(m['SQ_BUSY_CYCLES'], 1):.2f}",
+        f"- share of wave cycles spent waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES): "
+        f"{m['SQ_WAIT_ANY'] / max(m['SQ_WAVE_CYCLES'], 1):.3f}",
+        f"- waves per dispatch (SQ_WAVES): {m['SQ_WAVES']:.0f}",
+        "",
+        f"source={source_digest()}",
+        "",
+    ]
+    path = os.path.join(ROOT, "profiles", f"select_kernel_{workload}_k{k}_sq.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    log(f"[bench] wrote {path}")
+
+
 def write_trace(workload, trace_dir, command):
     """Summary of a rocprofv3 --kernel-trace --stats run of bench.py into profiles/."""
     import csv
@@ -318,9 +419,27 @@ def write_trace(workload, trace_dir, command):
     log(f"[bench] wrote {path}")
 
 
+def cpu_identity():
+    """(model name, sockets) of the host from /proc/cpuinfo."""
+    model, sockets = "unknown", set()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key == "model name" and model == "unknown":
+                    model = val.strip()
+                elif key == "physical id":
+                    sockets.add(val.strip())
+    except OSError:
+        pass
+    return model, max(1, len(sockets))
+
+
 def cpu_baseline(w, k, x, seconds):
     from oracle import topk as otk
     threads = otk.hw_threads()
+    model, sockets = cpu_identity()
     reps, t0 = 0, time.perf_counter()
     while True:
         otk.topk(x, k, indices=not w.values_only, threads=threads)
@@ -329,7 +448,8 @@ def cpu_baseline(w, k, x, seconds):
         if el >= seconds:
             break
     gbs = w.input_bytes() * reps / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": model,
+            "sockets": sockets, "host_cpus_visible": os.cpu_count(),
             "sample": f"{reps} full passes of the {w.name} batch ({w.rows} rows x {w.n}) in {el:.1f} s: "
                       f"C++ full sort per row, rows spread over {threads} threads"}
 
@@ -351,6 +471,8 @@ def main() -> int:
                     help="summarise two rocprofv3 --pmc output folders into profiles/ (no GPU needed)")
     ap.add_argument("--write-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
                     help="summarise a rocprofv3 --kernel-trace --stats output folder into profiles/ (no GPU needed)")
+    ap.add_argument("--write-sq", nargs=2, metavar=("PMC_DIR", "COMMAND"),
+                    help="summarise a rocprofv3 --pmc run of the SQ counters into profiles/ (no GPU needed)")
     args = ap.parse_args()
 
     if args.write_counters:
@@ -358,6 +480,10 @@ def main() -> int:
         return 0
     if args.write_trace:
         write_trace(args.workload, *args.write_trace)
+        return 0
+    if args.write_sq:
+        from workloads import gen as _gen
+        write_sq(args.workload, args.k or _gen.WORKLOADS[args.workload].ks[0], *args.write_sq)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -408,6 +534,13 @@ def main() -> int:
         "pages_style_gbs": round((r["in_bytes"] + w.rows * k * (w.elem_bytes + (0 if w.values_only else 4)))
                                  / (r["ms_cold"] * 1e-3) / 1e9, 2),
         "parity": r["parity"],
+        "probe": {"us_per_read": round(r["ms_probe"] * 1e3, 3),
+                  "gbs": round(r["in_bytes"] / (r["ms_probe"] * 1e-3) / 1e9, 2),
+                  "note": "ds_probe_read of the same bytes from the same pool (the scan's 16-byte loads, nothing "
+                          "else), K reads in one HIP graph: the read ceiling this input size reaches"},
+        "pct_of_probe": round(100.0 * r["ms_probe"] / r["ms_cold"], 2),
+        "select_pct_of_probe": round(100.0 * r["ms_probe"] / r["sel_cold"], 2),
+        "per_call": percentiles(r["per_call"]),
         "roofline": {"bound": "hbm", "kernel": "select_kernel", "achieved": round(sel_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(sel_gbs / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(r["sel_cold"] * 1e3, 3),
@@ -417,16 +550,21 @@ def main() -> int:
     }
     if not args.no_secondary:
         sec = {}
-        for name in ("c3_sampler",):
-            if name == w.name:
+        for name, sk, nsteps in SECONDARY:
+            if name == w.name and sk == k:
                 continue
             sw = gen.WORKLOADS[name]
-            s = time_workload(ts, torch, sw, sw.ks[0], max(20, args.steps // 2), args.warmup, args.pool_mib)
+            s = time_workload(ts, torch, sw, sk, min(nsteps, args.steps), args.warmup, args.pool_mib)
             sv = s["in_bytes"] / (s["ms_cold"] * 1e-3) / 1e9
-            sec[name] = {"value": round(sv, 2), "unit": "GB/s", "pct_of_hbm_peak": round(100 * sv / HBM_PEAK_GBS, 2),
-                         "ms_per_step": round(s["ms_cold"], 6), "select_us": round(s["sel_cold"] * 1e3, 3),
-                         "warm_value": round(s["in_bytes"] / (s["ms_warm"] * 1e-3) / 1e9, 2),
-                         "plan": s["plan"], "parity": s["parity"]}
+            ssel = s["in_bytes"] / (s["sel_cold"] * 1e-3) / 1e9
+            sec[f"{name}_k{sk}"] = {
+                "value": round(sv, 2), "unit": "GB/s", "pct_of_hbm_peak": round(100 * sv / HBM_PEAK_GBS, 2),
+                "k": sk, "ms_per_step": round(s["ms_cold"], 6), "select_us": round(s["sel_cold"] * 1e3, 3),
+                "select_frac_of_hbm_peak": round(ssel / HBM_PEAK_GBS, 4),
+                "probe_us": round(s["ms_probe"] * 1e3, 3), "pct_of_probe": round(100.0 * s["ms_probe"] / s["ms_cold"], 2),
+                "per_call": percentiles(s["per_call"]),
+                "warm_value": round(s["in_bytes"] / (s["ms_warm"] * 1e-3) / 1e9, 2),
+                "plan": s["plan"], "parity": s["parity"], "input_pool_copies": s["copies"]}
         out["secondary"] = sec
     if not args.no_cpu:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
