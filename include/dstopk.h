@@ -120,6 +120,7 @@ typedef struct ds_config {
   int32_t schedule;
   int32_t depth; /* output only (ds_topk_plan): blocks in flight per wave; zero on input */
   int32_t output;
+  int32_t warmup;
 } ds_config;
 /*
  *   output     flags for the outputs' form (zero: sorted, int32 indices).
@@ -134,6 +135,15 @@ typedef struct ds_config {
  */
 #define DS_OUTPUT_UNSORTED 1
 #define DS_OUTPUT_INDEX_INT64 2
+/*
+ *   warmup     w >= 0 blocks of warm-up window (tutorial chapter 37, section 5.2(1): the
+ *              first shuffled pages are radix-selected to set the threshold before the
+ *              steady stream; the CUDA side's init window does the same). The first w blocks
+ *              of each slice's order are appended unfiltered and checked after every block;
+ *              after the w-th, a buffer of more than k entries is compacted, so T becomes
+ *              the k-th best of the window. Then the schedule continues as planned. A
+ *              window turns the presampled start off. Zero (default): no window.
+ */
 
 /*
  * Per-(row, slice) counters of one run, filled when ds_topk_ex gets a stats pointer.

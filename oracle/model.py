@@ -226,13 +226,16 @@ def radix_select_topk(v: np.ndarray, pos: np.ndarray, j: np.ndarray, cand: np.nd
 def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B: int, B2: int,
                      order: np.ndarray, keys: Optional[np.ndarray] = None,
                      presample: Optional[Presample] = None,
-                     firsts: Optional[List[int]] = None) -> Tuple[np.ndarray, RunStats]:
+                     firsts: Optional[List[int]] = None, warmup: int = 0) -> Tuple[np.ndarray, RunStats]:
     """DeepSelectTopk over the elements [lo, hi) of a row (indices stay row-relative).
 
     ``order`` lists the blocks of the range in processing order (block b covers
     [lo + b*B, min(lo + (b+1)*B, hi))). With ``presample`` (and the row's ``keys``) the run
     starts from the presampled threshold when the first block read is whole; ``firsts`` are
     the blocks at the first positions of the order whose whole blocks the threshold covers.
+    With ``warmup`` = w > 0 (the warm-up window of TileLang tutorial chapter 37, section
+    5.2(1)) the buffer is also compacted right after the w-th block of the order when it
+    holds more than k entries, so that T is the k-th best of the window's elements.
     Returns the kept positions (at most k, unordered) and the run's counts.
     """
     n = hi - lo
@@ -251,7 +254,7 @@ def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B
     if presample is not None and whole(int(order[0])):
         covered = [b for b in (firsts or [int(order[0])]) if whole(b)]
         t0 = presample_key([keys[lo + b * B:lo + (b + 1) * B] for b in covered], k, presample)
-    for b in order:
+    for position, b in enumerate(order):
         blo, bhi = lo + int(b) * B, min(lo + (int(b) + 1) * B, hi)
         js = np.arange(blo, bhi, dtype=np.int64)
         st.reads[blo - lo:bhi - lo] += 1
@@ -264,7 +267,7 @@ def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B
         cand = np.concatenate([cand, keep])
         st.A += int(keep.size)
         st.max_len = max(st.max_len, int(cand.size))
-        if cand.size >= k + B2:
+        if cand.size >= k + B2 or (warmup > 0 and position + 1 == warmup and cand.size > k):
             st.W += int(cand.size)
             st.R += 1
             st.call_sizes.append(int(cand.size))
@@ -298,13 +301,14 @@ def first_positions(m: int, group: int, depth: int, seed: int, row_id: int, slic
 def deepselect_row(row: np.ndarray, k: int, B: int, B2: int, family: str = "feistel", seed: int = 0,
                    row_id: int = 0, slice_len: Optional[int] = None, group: int = 1,
                    presample_waves: Optional[int] = None,
-                   presample_depth: int = 4) -> Tuple[np.ndarray, List[RunStats]]:
+                   presample_depth: int = 4, warmup: int = 0) -> Tuple[np.ndarray, List[RunStats]]:
     """DeepSelect on one row (bf16 bits or float32), optionally split into slices.
 
     ``group`` > 1 draws the Feistel order over groups of blocks; ``presample_waves`` (the
     workgroup's waves) turns on the presampled start, over the whole blocks among the first
-    ``presample_depth`` positions of the order. Returns the top-k indices in output order
-    and the per-slice counts.
+    ``presample_depth`` positions of the order; ``warmup`` > 0 adds the warm-up window's
+    compaction after that many blocks. Returns the top-k indices in output order and the
+    per-slice counts.
     """
     v = widen(row)
     pos = (~np.signbit(v)).astype(np.int64)
@@ -328,7 +332,7 @@ def deepselect_row(row: np.ndarray, k: int, B: int, B2: int, family: str = "feis
         m = -(-(hi - lo) // B)
         order = grouped_order(m, group, seed, row_id, s) if group != 1 else block_order(family, m, seed, row_id, s)
         firsts = first_positions(m, group, presample_depth, seed, row_id, s, family)
-        kept, st = deepselect_range(v, pos, lo, hi, k, B, B2, order, keys, ps, firsts)
+        kept, st = deepselect_range(v, pos, lo, hi, k, B, B2, order, keys, ps, firsts, warmup)
         stats.append(st)
         kept_all.append(kept)
     union = np.concatenate(kept_all)

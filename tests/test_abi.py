@@ -202,3 +202,12 @@ def test_output_flags_in_plan():
     with pytest.raises(ts.DSError) as e:
         ts.ds_topk_plan(4, 65536, 64, ts.BF16, dict(base, output=4))
     assert e.value.status == ts.DS_ERR_INVALID_ARG
+
+
+def test_warmup_in_plan():
+    p = ts.ds_topk_plan(4, 65536, 64, ts.BF16, {"slices": 2, "warmup": 3})
+    assert p["warmup"] == 3 and p["presample"] == ts.PRESAMPLE_OFF
+    assert ts.ds_topk_plan(4, 65536, 64, ts.BF16, {"slices": 2})["warmup"] == 0
+    with pytest.raises(ts.DSError) as e:
+        ts.ds_topk_plan(4, 65536, 64, ts.BF16, {"slices": 2, "warmup": -1})
+    assert e.value.status == ts.DS_ERR_INVALID_ARG

@@ -122,7 +122,7 @@ def test_fuzz():
             assert e.status == ts.DS_ERR_UNSUPPORTED and cfg is not None, str(e)
 
 
-@pytest.mark.parametrize("mode", ["design-note", "default-lockstep", "free"])
+@pytest.mark.parametrize("mode", ["design-note", "default-lockstep", "free", "warm-up", "warm-up-free"])
 @pytest.mark.parametrize("dtype,n,k,block,slack,slices", [
     (gen.BF16, 50000, 100, 1024, 333, 3),
     (gen.FP32, 129280, 512, 1024, 1024, 1),
@@ -140,10 +140,15 @@ def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
     blocks) forced, and with the plan's own presampled start and order groups. Under the
     free-running schedule the counters depend on how the waves interleave, so only what the
     design note's notes and analysis fix is checked: every element read once, T
-    non-decreasing, W = A + k R, R B2 <= A and the buffer bound k + B2 + B - 1."""
+    non-decreasing, W = A + k R, R B2 <= A and the buffer bound k + B2 + B - 1. With a
+    warm-up window of two blocks (its forced compaction may come before k + B2 entries, so
+    R B2 <= A is not claimed) the lockstep counters again equal the model's."""
     x = gen.rows_family("normal", dtype, 17, 9, n)  # 8 rows dealt to the XCDs, 1 in plain order
     x[1] = gen.rows_family("ascending", dtype, 18, 1, n)[0]
-    cfg = {"slices": slices, "schedule": ts.SCHEDULE_FREE if mode == "free" else ts.SCHEDULE_LOCKSTEP}
+    free = mode in ("free", "warm-up-free")
+    cfg = {"slices": slices, "schedule": ts.SCHEDULE_FREE if free else ts.SCHEDULE_LOCKSTEP}
+    if mode.startswith("warm-up"):
+        cfg["warmup"] = 2
     if block:
         cfg.update(block=block, slack=slack)
     if mode == "design-note":
@@ -156,14 +161,16 @@ def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
     pw = plan["waves"] if plan["presample"] == ts.PRESAMPLE_ON else None
     if mode == "design-note":
         assert pw is None and plan["order_group"] == 1
+    warm = plan["warmup"]
+    assert warm == (2 if mode.startswith("warm-up") else 0) and (pw is None or not warm)
     B, B2 = plan["block"], plan["slack"]
     for r in range(x.shape[0]):
         per = -(-n // plan["slices"])
         slice_len = -(-per // B) * B  # the planner's slice length
-        if mode != "free":
+        if not free:
             _, mst = model.deepselect_row(x[r], k, B, B2, "feistel", seed=seed, row_id=r,
                                           slice_len=slice_len, group=plan["order_group"], presample_waves=pw,
-                                          presample_depth=plan["depth"])
+                                          presample_depth=plan["depth"], warmup=warm)
             assert len(mst) == plan["slices"]
         for s in range(plan["slices"]):
             g = st[r, s]
@@ -174,8 +181,9 @@ def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
             assert int(g["index_sum"]) == ln * lo + ln * (ln - 1) // 2
             assert int(g["monotone"]) == 1
             a, rr, w, ml = int(g["appended"]), int(g["compactions"]), int(g["work"]), int(g["max_len"])
-            assert w == a + k * rr and rr * B2 <= a and ml <= k + B2 + B - 1
-            if mode != "free":
+            assert w == a + k * rr and ml <= k + B2 + B - 1
+            assert warm or rr * B2 <= a
+            if not free:
                 ms = mst[s]
                 assert (a, rr, w, ml) == (ms.A, ms.R, ms.W, ms.max_len), (r, s)
 
@@ -402,3 +410,16 @@ def test_partial_block_first_without_threshold(dtype, schedule):
     cfg = {"slices": 1, "block": B, "presample": ts.PRESAMPLE_OFF, "order_group": 1, "schedule": schedule}
     _check(x, 64, f"partial-first seed={seed}", seed=seed, cfg=cfg)
     _check(x, 64, f"partial-first stats seed={seed}", seed=seed, cfg=cfg, stats=True)
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+@pytest.mark.parametrize("warmup", [1, 3])
+@pytest.mark.parametrize("family", ["normal", "ascending", "ties", "specials"])
+def test_warmup_window(dtype, warmup, family):
+    """The warm-up window (the plan's own schedule, split and whole rows) gives the oracle's
+    result; the plan reports the window and turns the presampled start off."""
+    x = gen.rows_family(family, dtype, 31, 6, 150000)
+    for cfg in ({"warmup": warmup}, {"warmup": warmup, "slices": 1}, {"warmup": warmup, "block": 1024}):
+        plan = ts.ds_topk_plan(6, 150000, 700, dtype, cfg)
+        assert plan["warmup"] == warmup and plan["presample"] == ts.PRESAMPLE_OFF
+        _check(x, 700, f"warm-up {family} {cfg}", seed=warmup, cfg=cfg)

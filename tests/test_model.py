@@ -382,3 +382,58 @@ def test_first_positions_follow_the_grouped_order(m, group, depth):
     assert len(firsts) <= depth and all(0 <= b < m for b in firsts)
     if m >= depth * group:
         assert len(firsts) == depth  # no padding among the first positions of a long order
+
+
+# ----------------------------------------------------------------------------- warm-up window
+@pytest.mark.parametrize("family", ["normal", "ascending", "descending", "ties", "specials"])
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+@pytest.mark.parametrize("warmup", [1, 2, 5])
+def test_warmup_window_matches_oracle(family, dtype, warmup):
+    x = gen.rows_family(family, dtype, 21, 3, 20000)
+    for r in range(3):
+        got, st = model.deepselect_row(x[r], 300, 1024, 2048, "feistel", seed=r + 4, row_id=r, warmup=warmup)
+        _, want = otk.topk(x[r:r + 1], 300)
+        assert got.tolist() == want[0].tolist()
+        s = st[0]
+        assert s.W == s.A + 300 * s.R and s.max_len <= 300 + 2048 + 1024 - 1
+        assert (s.reads == 1).all()
+
+
+def test_warmup_threshold_is_the_windows_kth_element():
+    """After a window of w blocks (w*B > k, below the k + B2 trigger) the first threshold is
+    the k-th best element of those w blocks, found here by the sorting oracle."""
+    x = gen.rows_family("normal", gen.FP32, 22, 1, 40 * 1024)[0]
+    k, B, B2 = 700, 1024, 8192
+    for w in (1, 2, 3, 6):
+        order = model.block_order("feistel", 40, seed=w, row=0)
+        _, st = model.deepselect_range(model.widen(x), (~np.signbit(model.widen(x))).astype(np.int64), 0, x.size,
+                                       k, B, B2, order, warmup=w)
+        blocks = np.concatenate([np.arange(int(b) * B, int(b) * B + B) for b in order[:w]])
+        if w * B <= k:
+            assert not st.thresholds or st.call_sizes[0] >= k + B2
+            continue
+        _, idx = otk.topk(x[None, blocks], k)
+        kth = int(blocks[idx[0, -1]])
+        assert st.thresholds[0].j == kth and st.call_sizes[0] == w * B
+
+
+@pytest.mark.parametrize("kind", ["normal", "ascending"])
+def test_warmup_work_against_the_bound(kind):
+    """A and W with a warm-up window, over block-order seeds, against the boxed bound (the
+    window only adds a compaction at a fixed point of the order) and against the run without
+    a window on the same orders (i.i.d. rows: the window appends fewer elements)."""
+    n, k, B, B2 = 131072, 512, 1024, 4096
+    row = _bound_row(kind, n)
+    bound = model.expected_work_bound(n, k, B, B2)
+    a0, a1, w1 = [], [], []
+    for s in range(40):
+        _, st0 = model.deepselect_row(row, k, B, B2, "feistel", seed=s + 1, row_id=s % 3)
+        _, st1 = model.deepselect_row(row, k, B, B2, "feistel", seed=s + 1, row_id=s % 3, warmup=1)
+        a0.append(st0[0].A)
+        a1.append(st1[0].A)
+        w1.append(st1[0].W)
+    mean = float(np.mean(w1))
+    half = 1.96 * float(np.std(w1)) / math.sqrt(len(w1))
+    assert mean + half <= bound, (kind, mean, half, bound)
+    if kind == "normal":
+        assert np.mean(a1) < np.mean(a0)

@@ -46,7 +46,7 @@ class ds_config(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("slack", ctypes.c_int32), ("slices", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("presample", ctypes.c_int32), ("order_group", ctypes.c_int32),
                 ("merge", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("depth", ctypes.c_int32), ("output", ctypes.c_int32)]
+                ("depth", ctypes.c_int32), ("output", ctypes.c_int32), ("warmup", ctypes.c_int32)]
 
 
 STATS_FIELDS = ["appended", "compactions", "work", "max_len", "reads", "index_sum", "monotone", "slice_lo",
@@ -110,7 +110,8 @@ def _cfg(cfg: Optional[Dict[str, int]]):
         return None
     c = ds_config(int(cfg.get("block", 0)), int(cfg.get("slack", 0)), int(cfg.get("slices", 0)),
                   int(cfg.get("waves", 0)), int(cfg.get("presample", 0)), int(cfg.get("order_group", 0)),
-                  int(cfg.get("merge", 0)), int(cfg.get("schedule", 0)), 0, int(cfg.get("output", 0)))
+                  int(cfg.get("merge", 0)), int(cfg.get("schedule", 0)), 0, int(cfg.get("output", 0)),
+                  int(cfg.get("warmup", 0)))
     return ctypes.pointer(c)
 
 
@@ -121,7 +122,7 @@ def ds_topk_plan(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, 
         raise DSError(st, "ds_topk_plan")
     return {"block": out.block, "slack": out.slack, "slices": out.slices, "waves": out.waves,
             "presample": out.presample, "order_group": out.order_group, "merge": out.merge,
-            "schedule": out.schedule, "depth": out.depth, "output": out.output}
+            "schedule": out.schedule, "depth": out.depth, "output": out.output, "warmup": out.warmup}
 
 
 def ds_topk_workspace_size(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, int]] = None) -> int:

@@ -58,6 +58,7 @@ struct Plan {
   bool lockstep;    // the design note's schedule: a barrier and the buffer check after every block
   bool unsorted;    // the outputs may hold the top k in any order (DS_OUTPUT_UNSORTED)
   bool idx64;       // int64 output indices (DS_OUTPUT_INDEX_INT64)
+  int warmup;       // blocks of the warm-up window
   // merge (slices > 1): DS_MERGE_LISTS (levels of the list-merge kernel over sorted slice
   // lists, group[l] lists merged together at level l) or DS_MERGE_SELECT (the merge kernel)
   int merge;
@@ -97,7 +98,7 @@ int check_basic(int64_t rows, int64_t n, int k, int dtype) {
 int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK) return st;
-  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (c.block < 0 || c.slack < 0 || c.slices < 0 || c.waves < 0) return DS_ERR_INVALID_ARG;
   if (c.presample != DS_PRESAMPLE_AUTO && c.presample != DS_PRESAMPLE_OFF && c.presample != DS_PRESAMPLE_ON)
     return DS_ERR_INVALID_ARG;
@@ -108,6 +109,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
     return DS_ERR_INVALID_ARG;
   if (c.depth != 0) return DS_ERR_INVALID_ARG;  // reported by the plan, never forced
   if ((c.output & ~(DS_OUTPUT_UNSORTED | DS_OUTPUT_INDEX_INT64)) != 0) return DS_ERR_INVALID_ARG;
+  if (c.warmup < 0) return DS_ERR_INVALID_ARG;
   const int chunk = chunk_elems(dtype);
   const int eb = elem_bytes(dtype);
 
@@ -204,7 +206,8 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   p.slice_len = slice_len;
   p.sort_cap = sort_cap;
   p.lds = lds;
-  p.presample = c.presample != DS_PRESAMPLE_OFF && k <= 64 * kSelectShapes[shape].waves;
+  p.presample = c.presample != DS_PRESAMPLE_OFF && c.warmup == 0 && k <= 64 * kSelectShapes[shape].waves;
+  p.warmup = c.warmup;
   // groups of two blocks pay off on long slices (consecutive loads in flight); short slices
   // keep single blocks, which randomise adversarial (sorted) slices better
   p.order_group = c.order_group ? c.order_group : ((slice_len + block - 1) / block >= 8 ? 2 : 1);
@@ -289,6 +292,7 @@ int run_select(const Plan& pl, const void* x, const int32_t* lens, int64_t rows,
   sp.group_shift = pl.order_group == 4 ? 2 : (pl.order_group == 2 ? 1 : 0);
   sp.lockstep = pl.lockstep ? 1 : 0;
   sp.unsorted = pl.unsorted && pl.slices == 1 ? 1 : 0;
+  sp.warmup = pl.warmup;
   return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }
 
@@ -468,6 +472,7 @@ int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg
   out->schedule = p.lockstep ? DS_SCHEDULE_LOCKSTEP : DS_SCHEDULE_FREE;
   out->depth = ds::depth_for(kSelectShapes[p.shape].waves, kSelectShapes[p.shape].cpw);
   out->output = (p.unsorted ? DS_OUTPUT_UNSORTED : 0) | (p.idx64 ? DS_OUTPUT_INDEX_INT64 : 0);
+  out->warmup = p.warmup;
   return DS_OK;
 }
 

@@ -1358,8 +1358,8 @@ struct BodyOut {
 template <int DT, int WAVES, int CPW, int D, bool MERGE, bool STATS>
 __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amdgpu_buffer_rsrc_t rs, uint32_t len,
                                                 uint32_t idx_base, uint32_t k, uint32_t B2, const BlockOrder& ord,
-                                                uint32_t ilo, uint32_t ihi, bool lockstep, bool presample,
-                                                uint32_t gshift, const OutSpec* fso, BodyOut& out) {
+                                                uint32_t ilo, uint32_t ihi, bool lockstep, uint32_t warm,
+                                                bool presample, uint32_t gshift, const OutSpec* fso, BodyOut& out) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t IB = MERGE ? 8 : (DT == DS_BF16 ? 2 : 4);  // bytes per item
   constexpr uint32_t VEC = 16 / IB;                            // items per lane per chunk
@@ -1393,6 +1393,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   uint32_t mode = 0, thr_s = ~0u, thr_n = ~0u;  // mode 0: accept everything (no threshold yet)
   uint32_t t_key = 0, t_idx = 0, maxkey = 0;
   uint32_t nsurv = 0, hpar = 0;
+  uint32_t warm_left = warm;  // blocks of the warm-up window still to come
   bool sur_a = false;  // survivors in set A (else set B)
   // key range of the entries appended before the first compaction (the select kernel tracks
   // it; the merge kernel does not)
@@ -1775,9 +1776,16 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
 #pragma unroll
     for (uint32_t t = 0; t < CPW; ++t) bf[t] = load16(rs, addr(bid_ref, t));
 
-    if (lockstep) {
+    // the warm-up window: the first `warm` blocks of the order (the last group's padding
+    // step does not count)
+    const bool in_window = warm_left != 0;
+    if (bid < m && warm_left != 0) --warm_left;
+    if (lockstep || in_window) {
       // the design note's schedule: every wave has appended its share of the block, then the
-      // check; a second barrier keeps the length still until every wave has read it
+      // check; a second barrier keeps the length still until every wave has read it. The
+      // warm-up window's blocks run this way too, and after its last one the buffer is
+      // compacted as soon as it holds more than k entries: T is then the k-th best of the
+      // window's elements
       if constexpr (STATS) {
         if (st0) t_mark = wall_clock64();
       }
@@ -1789,7 +1797,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
       if constexpr (STATS) {
         if (st0) sc.st_max = max(sc.st_max, static_cast<unsigned long long>(nsurv + napp));
       }
-      if (nsurv + napp >= k + B2)
+      if (nsurv + napp >= k + B2 || (in_window && warm_left == 0 && nsurv + napp > k))
         in_loop(napp);
       else
         lds_sync();
@@ -1906,6 +1914,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), false, STATS>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
                                                                    slice_lo + len - 1u, p.lockstep != 0,
+                                                                   static_cast<uint32_t>(p.warmup),
                                                                    p.presample != 0, gshift,
                                                                    own_sort ? &fso : nullptr, bo);
 
@@ -2026,7 +2035,7 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   const OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), true, false>(L, sc, rs, len, 0u, k, B2, ord, 0u,
-                                                                  static_cast<uint32_t>(p.n - 1), false,
+                                                                  static_cast<uint32_t>(p.n - 1), false, 0u,
                                                                   p.presample != 0, 0u, &fso, bo);
   if (bo.sorted) return;
   if (p.unsorted) {

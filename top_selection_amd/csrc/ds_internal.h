@@ -39,6 +39,7 @@ struct SelectParams {
   int32_t group_shift;       // log2 of G: the block order is random over groups of G blocks
   int32_t lockstep;          // nonzero: a barrier and the buffer check after every block
   int32_t unsorted;          // slices == 1: the k survivors may be written in any order
+  int32_t warmup;            // blocks of the warm-up window (0: none)
 };
 
 // The merge of split rows. The merge kernel: one workgroup per row runs DeepSelect over the
