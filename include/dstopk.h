@@ -121,6 +121,7 @@ typedef struct ds_config {
   int32_t depth; /* output only (ds_topk_plan): blocks in flight per wave; zero on input */
   int32_t output;
   int32_t warmup;
+  int32_t share;
 } ds_config;
 /*
  *   output     flags for the outputs' form (zero: sorted, int32 indices).
@@ -143,7 +144,21 @@ typedef struct ds_config {
  *              after the w-th, a buffer of more than k entries is compacted, so T becomes
  *              the k-th best of the window. Then the schedule continues as planned. A
  *              window turns the presampled start off. Zero (default): no window.
+ *   share      DS_SHARE_ON: the slices of a split row share a threshold (design note,
+ *              "Implementation", cluster paragraph: the parts of a row work toward one
+ *              top-k; tutorial chapter 37, section 4.7). Each slice publishes its threshold
+ *              (the presampled T0 and every compaction's k-th entry) to a per-row word with
+ *              an atomic maximum and filters with the larger of its own and the row's; every
+ *              published value ranks at or below the row's k-th element, so the result is
+ *              unchanged and only the work shrinks (counters become timing-dependent). The
+ *              row words take rows * 8 bytes (rounded up to 16) at the start of the workspace
+ *              and are zeroed by a small kernel before each select launch. Zero (auto): ON
+ *              for split rows without the presampled start (large k), else OFF. The plan
+ *              reports ON, or OFF for split rows (AUTO when the plan has one slice).
  */
+#define DS_SHARE_AUTO 0
+#define DS_SHARE_OFF 1
+#define DS_SHARE_ON 2
 
 /*
  * Per-(row, slice) counters of one run, filled when ds_topk_ex gets a stats pointer.

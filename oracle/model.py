@@ -226,7 +226,8 @@ def radix_select_topk(v: np.ndarray, pos: np.ndarray, j: np.ndarray, cand: np.nd
 def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B: int, B2: int,
                      order: np.ndarray, keys: Optional[np.ndarray] = None,
                      presample: Optional[Presample] = None,
-                     firsts: Optional[List[int]] = None, warmup: int = 0) -> Tuple[np.ndarray, RunStats]:
+                     firsts: Optional[List[int]] = None, warmup: int = 0,
+                     shared: Optional[List[int]] = None) -> Tuple[np.ndarray, RunStats]:
     """DeepSelectTopk over the elements [lo, hi) of a row (indices stay row-relative).
 
     ``order`` lists the blocks of the range in processing order (block b covers
@@ -236,7 +237,12 @@ def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B
     With ``warmup`` = w > 0 (the warm-up window of TileLang tutorial chapter 37, section
     5.2(1)) the buffer is also compacted right after the w-th block of the order when it
     holds more than k entries, so that T is the k-th best of the window's elements.
-    Returns the kept positions (at most k, unordered) and the run's counts.
+    With ``shared`` (a one-element list: the row's published threshold as a composite
+    key << 32 | (~index & 0xFFFFFFFF), 0 for none; needs ``keys``) the range shares its
+    threshold with the row's other ranges (the cluster split of the design note,
+    "Implementation"): it reads the row's at its start, and whenever its own threshold is set
+    (T0, a compaction) it publishes it with a maximum and reads back the row's; it appends
+    only elements ranking above the larger of the two. Returns the kept positions (at most k, unordered) and the run's counts.
     """
     n = hi - lo
     assert n >= 1 and k >= 1 and B >= 1 and B2 >= 1
@@ -251,9 +257,18 @@ def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B
     def whole(b: int) -> bool:
         return lo + (b + 1) * B <= hi
 
+    adopted = shared[0] if shared is not None else 0  # the row's threshold as last read (sharing)
+
+    def publish(c: int) -> None:
+        nonlocal adopted
+        if shared is not None:
+            shared[0] = max(shared[0], c)
+            adopted = shared[0]
+
     if presample is not None and whole(int(order[0])):
         covered = [b for b in (firsts or [int(order[0])]) if whole(b)]
         t0 = presample_key([keys[lo + b * B:lo + (b + 1) * B] for b in covered], k, presample)
+        publish(t0 << 32)  # index ~0: ties with T0 rank above it
     for position, b in enumerate(order):
         blo, bhi = lo + int(b) * B, min(lo + (int(b) + 1) * B, hi)
         js = np.arange(blo, bhi, dtype=np.int64)
@@ -264,6 +279,9 @@ def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B
             keep = js[keys[js] >= np.uint64(t0)]
         else:
             keep = js
+        if adopted:
+            comp = (keys[keep].astype(np.uint64) << np.uint64(32)) | (~keep.astype(np.uint64) & np.uint64(0xFFFFFFFF))
+            keep = keep[comp > np.uint64(adopted)]
         cand = np.concatenate([cand, keep])
         st.A += int(keep.size)
         st.max_len = max(st.max_len, int(cand.size))
@@ -275,6 +293,8 @@ def deepselect_range(v: np.ndarray, pos: np.ndarray, lo: int, hi: int, k: int, B
             worst = cand[_order(v[cand], pos[cand], cand)[-1]]
             thr = Pair(float(v[worst]), int(pos[worst]), int(worst))
             st.thresholds.append(thr)
+            if shared is not None:
+                publish((int(keys[worst]) << 32) | (~int(worst) & 0xFFFFFFFF))
     st.W += int(cand.size)
     st.call_sizes.append(int(cand.size))
     return radix_select_topk(v, pos, jall, cand, k), st
@@ -301,14 +321,16 @@ def first_positions(m: int, group: int, depth: int, seed: int, row_id: int, slic
 def deepselect_row(row: np.ndarray, k: int, B: int, B2: int, family: str = "feistel", seed: int = 0,
                    row_id: int = 0, slice_len: Optional[int] = None, group: int = 1,
                    presample_waves: Optional[int] = None,
-                   presample_depth: int = 4, warmup: int = 0) -> Tuple[np.ndarray, List[RunStats]]:
+                   presample_depth: int = 4, warmup: int = 0,
+                   share: bool = False) -> Tuple[np.ndarray, List[RunStats]]:
     """DeepSelect on one row (bf16 bits or float32), optionally split into slices.
 
     ``group`` > 1 draws the Feistel order over groups of blocks; ``presample_waves`` (the
     workgroup's waves) turns on the presampled start, over the whole blocks among the first
     ``presample_depth`` positions of the order; ``warmup`` > 0 adds the warm-up window's
-    compaction after that many blocks. Returns the top-k indices in output order and the
-    per-slice counts.
+    compaction after that many blocks; ``share`` runs the slices one after another with a
+    shared row threshold (one order of events the concurrent slices can take). Returns the
+    top-k indices in output order and the per-slice counts.
     """
     v = widen(row)
     pos = (~np.signbit(v)).astype(np.int64)
@@ -319,20 +341,23 @@ def deepselect_row(row: np.ndarray, k: int, B: int, B2: int, family: str = "feis
         slice_len = -(-n // B) * B
     assert slice_len % B == 0 and slice_len >= B
     keys, ps = None, None
-    if presample_waves is not None:
+    if presample_waves is not None or share:
         keys = keys_of(row)
+    if presample_waves is not None:
         bf16 = row.dtype == np.uint16
         ps = Presample(presample_waves, 8 if bf16 else 4, 16 if bf16 else 32)
     if group != 1 and family != "feistel":
         raise ValueError("grouped orders are Feistel orders")
     stats = []
     kept_all = []
+    row_shared = [0]
     for s, lo in enumerate(range(0, n, slice_len)):
         hi = min(lo + slice_len, n)
         m = -(-(hi - lo) // B)
         order = grouped_order(m, group, seed, row_id, s) if group != 1 else block_order(family, m, seed, row_id, s)
         firsts = first_positions(m, group, presample_depth, seed, row_id, s, family)
-        kept, st = deepselect_range(v, pos, lo, hi, k, B, B2, order, keys, ps, firsts, warmup)
+        kept, st = deepselect_range(v, pos, lo, hi, k, B, B2, order, keys, ps, firsts, warmup,
+                                    row_shared if share else None)
         stats.append(st)
         kept_all.append(kept)
     union = np.concatenate(kept_all)

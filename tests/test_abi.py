@@ -80,10 +80,13 @@ def test_forced_plans(dtype, n, k, slices):
     per = -(-n // slices)
     assert p["slices"] == -(-n // (-(-per // p["block"]) * p["block"]))
     ws = ts.ds_topk_workspace_size(8, n, k, dtype, {"slices": slices})
-    assert ws == _list_merge_ws(8, slices, k)
+    # split rows without the presampled start share a threshold word per row (8 rows: 64 bytes)
+    shared = 64 if slices > 1 and p["presample"] == ts.PRESAMPLE_OFF else 0
+    assert p["share"] == (ts.SHARE_AUTO if slices == 1 else (ts.SHARE_ON if shared else ts.SHARE_OFF))
+    assert ws == shared + _list_merge_ws(8, slices, k)
     assert p["merge"] == (0 if slices == 1 else ts.MERGE_LISTS)
     sel = ts.ds_topk_workspace_size(8, n, k, dtype, {"slices": slices, "merge": ts.MERGE_SELECT})
-    assert sel == (0 if slices == 1 else 8 * ((slices * k + 1) // 2 * 2) * 8)
+    assert sel == (0 if slices == 1 else shared + 8 * ((slices * k + 1) // 2 * 2) * 8)
 
 
 def _even(v):
@@ -210,4 +213,19 @@ def test_warmup_in_plan():
     assert ts.ds_topk_plan(4, 65536, 64, ts.BF16, {"slices": 2})["warmup"] == 0
     with pytest.raises(ts.DSError) as e:
         ts.ds_topk_plan(4, 65536, 64, ts.BF16, {"slices": 2, "warmup": -1})
+    assert e.value.status == ts.DS_ERR_INVALID_ARG
+
+
+def test_share_in_plan():
+    base = {"slices": 4}
+    assert ts.ds_topk_plan(4, 65536, 64, ts.BF16, base)["share"] == ts.SHARE_OFF  # presampled start
+    big = ts.ds_topk_plan(4, 1 << 20, 4096, ts.BF16, {"slices": 32})
+    assert big["presample"] == ts.PRESAMPLE_OFF and big["share"] == ts.SHARE_ON
+    assert ts.ds_topk_plan(4, 1 << 20, 4096, ts.BF16, {"slices": 32, "share": ts.SHARE_OFF})["share"] == ts.SHARE_OFF
+    assert ts.ds_topk_plan(4, 65536, 64, ts.BF16, dict(base, share=ts.SHARE_ON))["share"] == ts.SHARE_ON
+    assert ts.ds_topk_plan(4, 65536, 64, ts.BF16, {"slices": 1, "share": ts.SHARE_ON})["share"] == ts.SHARE_AUTO
+    plain = ts.ds_topk_workspace_size(6, 65536, 64, ts.BF16, base)
+    assert ts.ds_topk_workspace_size(6, 65536, 64, ts.BF16, dict(base, share=ts.SHARE_ON)) == plain + 48
+    with pytest.raises(ts.DSError) as e:
+        ts.ds_topk_plan(4, 65536, 64, ts.BF16, dict(base, share=3))
     assert e.value.status == ts.DS_ERR_INVALID_ARG

@@ -146,7 +146,8 @@ def test_counters_match_model(mode, dtype, n, k, block, slack, slices):
     x = gen.rows_family("normal", dtype, 17, 9, n)  # 8 rows dealt to the XCDs, 1 in plain order
     x[1] = gen.rows_family("ascending", dtype, 18, 1, n)[0]
     free = mode in ("free", "warm-up-free")
-    cfg = {"slices": slices, "schedule": ts.SCHEDULE_FREE if free else ts.SCHEDULE_LOCKSTEP}
+    # no shared row threshold: with it the counters depend on how the slices interleave
+    cfg = {"slices": slices, "schedule": ts.SCHEDULE_FREE if free else ts.SCHEDULE_LOCKSTEP, "share": ts.SHARE_OFF}
     if mode.startswith("warm-up"):
         cfg["warmup"] = 2
     if block:

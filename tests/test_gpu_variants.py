@@ -171,3 +171,51 @@ def test_ragged_two_launches(merge):
     torch.cuda.synchronize()
     wv, wi = otk.topk_ragged(x, lens, k)
     assert_same(x, k, to_numpy_vals(vals), idx.cpu().numpy(), wv, wi, f"ragged two launches merge={merge}")
+
+
+SHARED = [
+    ("indexer", "c2", gen.BF16, 16, 131072, 512, {}),
+    ("descending-32", "descending", gen.FP32, 6, 1 << 20, 512, {"slices": 32}),
+    ("ascending-k4096", "ascending", gen.BF16, 4, 1 << 20, 4096, {"slices": 32}),
+    ("ties-select", "ties", gen.FP32, 8, 300000, 300, {"slices": 8, "merge": ts.MERGE_SELECT}),
+    ("specials-small-block", "specials", gen.BF16, 9, 70001, 100, {"block": 1024, "slices": 5}),
+    ("normal-lockstep", "normal", gen.FP32, 8, 200000, 64, {"slices": 5, "schedule": ts.SCHEDULE_LOCKSTEP}),
+]
+
+
+@pytest.mark.parametrize("case", SHARED, ids=[c[0] for c in SHARED])
+def test_shared_row_threshold(case):
+    """Slices sharing a row threshold give the oracle's result on every family, with counters
+    that keep the invariants that do not depend on timing; the shared run appends no more
+    than the unshared one on a descending row split in 32 (its first slice publishes first)."""
+    label, kind, dtype, rows, n, k, cfg = case
+    x = _make(kind, dtype, rows, n, 69)
+    cfg = dict(cfg, share=ts.SHARE_ON)
+    assert ts.ds_topk_plan(rows, n, k, dtype, cfg)["share"] == ts.SHARE_ON
+    want = otk.topk(x, k)
+    for seed in (1, 2):
+        gv, gi, plan, st = _run(x, k, cfg, seed=seed, stats=True)
+        assert_same(x, k, gv, gi, want[0], want[1], f"shared {label} seed={seed}")
+        B, B2 = plan["block"], plan["slack"]
+        for r in range(rows):
+            for s in range(plan["slices"]):
+                g = st[r, s]
+                a, rr, w, ml = int(g["appended"]), int(g["compactions"]), int(g["work"]), int(g["max_len"])
+                assert w == a + k * rr and rr * B2 <= a and ml <= k + B2 + B - 1 and int(g["monotone"]) == 1
+                assert int(g["reads"]) == int(g["slice_len"])
+    if label == "descending-32":
+        _, _, _, st_plain = _run(x, k, dict(cfg, share=ts.SHARE_OFF), stats=True)
+        a_shared = int(st["appended"].sum())
+        a_plain = int(st_plain["appended"].sum())
+        say(f"[gpu] shared threshold, descending rows in 32 slices: appended {a_shared} vs {a_plain} unshared")
+        assert a_shared <= 1.05 * a_plain
+
+
+def test_shared_row_threshold_ragged():
+    rows, n, k = 12, 131072, 512
+    x = gen.WORKLOADS["c2_indexer"].make(rows=rows)
+    cfg = {"share": ts.SHARE_ON, "slices": 4}
+    lens = _lens(rows, n, k, ts.ds_topk_plan(rows, n, k, gen.BF16, cfg)["block"], 70)
+    gv, gi, _, _ = _run(x, k, cfg, lens)
+    wv, wi = otk.topk_ragged(x, lens, k)
+    assert_same(x, k, gv, gi, wv, wi, "shared ragged")

@@ -437,3 +437,31 @@ def test_warmup_work_against_the_bound(kind):
     assert mean + half <= bound, (kind, mean, half, bound)
     if kind == "normal":
         assert np.mean(a1) < np.mean(a0)
+
+
+# ----------------------------------------------------------------------------- shared row threshold
+@pytest.mark.parametrize("family", ["normal", "ascending", "descending", "ties", "specials", "neg"])
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.FP32])
+def test_shared_threshold_matches_oracle(family, dtype):
+    """Slices that publish their thresholds to the row and filter with the row's still give
+    the oracle's top-k (every published value ranks at or below the row's k-th element)."""
+    x = gen.rows_family(family, dtype, 23, 2, 40000)
+    for r in range(2):
+        for slice_len, presample in ((4096, None), (8192, 16), (12288, 16)):
+            got, st = model.deepselect_row(x[r], 500, 1024, 1024, "feistel", seed=r + 9, row_id=r,
+                                           slice_len=slice_len, presample_waves=presample, share=True)
+            _, want = otk.topk(x[r:r + 1], 500)
+            assert got.tolist() == want[0].tolist(), (family, dtype, r, slice_len)
+            for s in st:
+                assert s.W == s.A + 500 * s.R and s.max_len <= 500 + 1024 + 1024 - 1
+
+
+def test_shared_threshold_cuts_work_on_a_descending_row():
+    """A descending row split in eight: with the first slice's thresholds shared, the later
+    slices append a fraction of what they append alone."""
+    x = gen.rows_family("descending", gen.FP32, 24, 1, 65536)[0]
+    plain = model.deepselect_row(x, 512, 1024, 1024, "feistel", seed=3, slice_len=8192)[1]
+    shared = model.deepselect_row(x, 512, 1024, 1024, "feistel", seed=3, slice_len=8192, share=True)[1]
+    a_plain = sum(s.A for s in plain[1:])
+    a_shared = sum(s.A for s in shared[1:])
+    assert shared[0].A == plain[0].A and a_shared < 0.25 * a_plain, (a_shared, a_plain)

@@ -12,11 +12,12 @@ from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
-# (label, input, k), each input smaller than the one before: the largest plan the array
-# holds (k = 4096 over 64 rows of 131072: exactly the array's size), the indexer workload at
-# full size, then smaller split plans
-CASES = [("bf16 64x131072 k4096 (array size)", lambda: gen.rows_family("normal", gen.BF16, 83, 64, 131072), 4096),
-         ("indexer 64x131072 k512", lambda: gen.WORKLOADS["c2_indexer"].make(), 512),
+# (label, input, k), each input smaller than the one before: a plan near the array's size
+# (k = 4096 over 63 rows of 131072: 4 slices' lists and the shared row thresholds, 8258048
+# of its 8388608 bytes), indexer rows, then smaller split plans
+CASES = [("bf16 63x131072 k4096 (near the array size)", lambda: gen.rows_family("normal", gen.BF16, 83, 63, 131072),
+          4096),
+         ("indexer rows 48x131072 k512", lambda: gen.WORKLOADS["c2_indexer"].make(rows=48), 512),
          ("fp32 3x300000 k64 ties", lambda: gen.rows_family("ties", gen.FP32, 82, 3, 300000), 64),
          ("bf16 5x100000 k100", lambda: gen.rows_family("normal", gen.BF16, 81, 5, 100000), 100)]
 

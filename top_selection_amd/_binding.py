@@ -30,6 +30,7 @@ PRESAMPLE_AUTO, PRESAMPLE_OFF, PRESAMPLE_ON = 0, 1, 2
 MERGE_AUTO, MERGE_LISTS, MERGE_SELECT = 0, 1, 2
 SCHEDULE_AUTO, SCHEDULE_FREE, SCHEDULE_LOCKSTEP = 0, 1, 2
 OUTPUT_UNSORTED, OUTPUT_INDEX_INT64 = 1, 2
+SHARE_AUTO, SHARE_OFF, SHARE_ON = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdstopk.so")
@@ -46,7 +47,8 @@ class ds_config(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("slack", ctypes.c_int32), ("slices", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("presample", ctypes.c_int32), ("order_group", ctypes.c_int32),
                 ("merge", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("depth", ctypes.c_int32), ("output", ctypes.c_int32), ("warmup", ctypes.c_int32)]
+                ("depth", ctypes.c_int32), ("output", ctypes.c_int32), ("warmup", ctypes.c_int32),
+                ("share", ctypes.c_int32)]
 
 
 STATS_FIELDS = ["appended", "compactions", "work", "max_len", "reads", "index_sum", "monotone", "slice_lo",
@@ -111,7 +113,7 @@ def _cfg(cfg: Optional[Dict[str, int]]):
     c = ds_config(int(cfg.get("block", 0)), int(cfg.get("slack", 0)), int(cfg.get("slices", 0)),
                   int(cfg.get("waves", 0)), int(cfg.get("presample", 0)), int(cfg.get("order_group", 0)),
                   int(cfg.get("merge", 0)), int(cfg.get("schedule", 0)), 0, int(cfg.get("output", 0)),
-                  int(cfg.get("warmup", 0)))
+                  int(cfg.get("warmup", 0)), int(cfg.get("share", 0)))
     return ctypes.pointer(c)
 
 
@@ -122,7 +124,8 @@ def ds_topk_plan(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, 
         raise DSError(st, "ds_topk_plan")
     return {"block": out.block, "slack": out.slack, "slices": out.slices, "waves": out.waves,
             "presample": out.presample, "order_group": out.order_group, "merge": out.merge,
-            "schedule": out.schedule, "depth": out.depth, "output": out.output, "warmup": out.warmup}
+            "schedule": out.schedule, "depth": out.depth, "output": out.output, "warmup": out.warmup,
+            "share": out.share}
 
 
 def ds_topk_workspace_size(rows: int, n: int, k: int, dtype: int, cfg: Optional[Dict[str, int]] = None) -> int:

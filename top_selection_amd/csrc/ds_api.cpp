@@ -59,6 +59,8 @@ struct Plan {
   bool unsorted;    // the outputs may hold the top k in any order (DS_OUTPUT_UNSORTED)
   bool idx64;       // int64 output indices (DS_OUTPUT_INDEX_INT64)
   int warmup;       // blocks of the warm-up window
+  bool share;       // split rows share a threshold word per row (DS_SHARE_ON)
+  size_t share_bytes;  // the row words at the start of the workspace (before the lists)
   // merge (slices > 1): DS_MERGE_LISTS (levels of the list-merge kernel over sorted slice
   // lists, group[l] lists merged together at level l) or DS_MERGE_SELECT (the merge kernel)
   int merge;
@@ -98,7 +100,7 @@ int check_basic(int64_t rows, int64_t n, int k, int dtype) {
 int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
   int st = check_basic(rows, n, k, dtype);
   if (st != DS_OK) return st;
-  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  const ds_config c = cfg ? *cfg : ds_config{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (c.block < 0 || c.slack < 0 || c.slices < 0 || c.waves < 0) return DS_ERR_INVALID_ARG;
   if (c.presample != DS_PRESAMPLE_AUTO && c.presample != DS_PRESAMPLE_OFF && c.presample != DS_PRESAMPLE_ON)
     return DS_ERR_INVALID_ARG;
@@ -110,6 +112,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   if (c.depth != 0) return DS_ERR_INVALID_ARG;  // reported by the plan, never forced
   if ((c.output & ~(DS_OUTPUT_UNSORTED | DS_OUTPUT_INDEX_INT64)) != 0) return DS_ERR_INVALID_ARG;
   if (c.warmup < 0) return DS_ERR_INVALID_ARG;
+  if (c.share != DS_SHARE_AUTO && c.share != DS_SHARE_OFF && c.share != DS_SHARE_ON) return DS_ERR_INVALID_ARG;
   const int chunk = chunk_elems(dtype);
   const int eb = elem_bytes(dtype);
 
@@ -218,7 +221,13 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
     const int64_t entries = slices * static_cast<int64_t>(k);
     if (entries * 8 > kMaxSliceBytes) return DS_ERR_UNSUPPORTED;
     p.ws_row_a = (entries + 1) & ~int64_t(1);
-    p.ws_bytes = static_cast<size_t>(rows) * static_cast<size_t>(p.ws_row_a) * 8;
+    // sharing pays where slices start without a presampled threshold (large k): their first
+    // compactions come late, and a row threshold prunes them earlier (measured on MI355X:
+    // long rows at k = 4096 in 32 slices, 10 % faster); with a presampled start the extra
+    // zeroing launch costs more than it saves
+    p.share = c.share == DS_SHARE_ON || (c.share == DS_SHARE_AUTO && !p.presample);
+    p.share_bytes = p.share ? (static_cast<size_t>(rows) * 8 + 15) & ~size_t(15) : 0;
+    p.ws_bytes = p.share_bytes + static_cast<size_t>(rows) * static_cast<size_t>(p.ws_row_a) * 8;
     p.merge = c.merge ? c.merge : DS_MERGE_LISTS;
     if (p.merge == DS_MERGE_LISTS) {
       // the fewest levels of at most gmax lists each, then the smallest group size per level
@@ -268,6 +277,11 @@ int check_call(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k
   return DS_OK;
 }
 
+// The workspace is [shared row thresholds (sharing only)][slice lists][first list-merge level].
+uint2* lists_of(const Plan& pl, void* ws) {
+  return ws ? reinterpret_cast<uint2*>(static_cast<uint8_t*>(ws) + pl.share_bytes) : nullptr;
+}
+
 int run_select(const Plan& pl, const void* x, const int32_t* lens, int64_t rows, int64_t n, int64_t row_stride, int k,
                uint64_t seed, void* out_vals, void* out_idx, void* ws, ds_stats* stats, hipStream_t stream) {
   (void)hipGetLastError();  // clear a stale error so a launch failure is reported as ours
@@ -282,7 +296,7 @@ int run_select(const Plan& pl, const void* x, const int32_t* lens, int64_t rows,
   sp.slack = pl.slack;
   sp.sort_cap = pl.sort_cap;
   sp.seed = seed;
-  sp.ws = static_cast<uint2*>(ws);
+  sp.ws = lists_of(pl, ws);
   sp.ws_row_entries = pl.ws_row_a;
   sp.out_vals = out_vals;
   sp.out_idx = ds::IdxOut{out_idx, pl.idx64 ? 1 : 0};
@@ -293,6 +307,10 @@ int run_select(const Plan& pl, const void* x, const int32_t* lens, int64_t rows,
   sp.lockstep = pl.lockstep ? 1 : 0;
   sp.unsorted = pl.unsorted && pl.slices == 1 ? 1 : 0;
   sp.warmup = pl.warmup;
+  if (pl.share) {  // the row words start at zero (below every element) in every call
+    sp.share = static_cast<unsigned long long*>(ws);
+    if (ds::launch_zero_words(sp.share, rows, stream) != hipSuccess) return DS_ERR_LAUNCH;
+  }
   return ds::launch_select(pl.dtype, pl.shape, sp, rows, pl.lds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
 }
 
@@ -301,7 +319,7 @@ int run_merge(const Plan& pl, const int32_t* lens, int64_t rows, int64_t n, int 
   if (pl.slices <= 1) return DS_OK;
   (void)hipGetLastError();
   ds::MergeParams mp{};
-  mp.ws = static_cast<const uint2*>(ws);
+  mp.ws = lists_of(pl, ws);
   mp.entries = static_cast<int64_t>(pl.slices) * k;
   mp.row_entries = (mp.entries + 1) & ~int64_t(1);
   mp.n = n;
@@ -318,7 +336,7 @@ int run_merge(const Plan& pl, const int32_t* lens, int64_t rows, int64_t n, int 
   if (pl.merge == DS_MERGE_SELECT)
     return ds::launch_merge(pl.dtype, mp, rows, pl.mlds, stream) == hipSuccess ? DS_OK : DS_ERR_LAUNCH;
   // list merge: level l reads one workspace region and writes the other (or the outputs)
-  uint2* const region[2] = {static_cast<uint2*>(ws), static_cast<uint2*>(ws) + rows * pl.ws_row_a};
+  uint2* const region[2] = {lists_of(pl, ws), lists_of(pl, ws) + rows * pl.ws_row_a};
   const int64_t row_of[2] = {pl.ws_row_a, pl.ws_row_b};
   int64_t lists = pl.slices;
   for (int l = 0; l < pl.levels; ++l) {
@@ -473,6 +491,7 @@ int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg
   out->depth = ds::depth_for(kSelectShapes[p.shape].waves, kSelectShapes[p.shape].cpw);
   out->output = (p.unsorted ? DS_OUTPUT_UNSORTED : 0) | (p.idx64 ? DS_OUTPUT_INDEX_INT64 : 0);
   out->warmup = p.warmup;
+  out->share = p.share ? DS_SHARE_ON : (p.slices > 1 ? DS_SHARE_OFF : DS_SHARE_AUTO);
   return DS_OK;
 }
 

@@ -351,6 +351,7 @@ struct Scalars {
   uint32_t rmax[kMaxWaves];    // compaction
   uint32_t lkey[kListCap];     // pivot-bin entries
   uint32_t lidx[kListCap];
+  uint32_t shr[2];             // the row's shared threshold as read by thread 0 (low, high word)
   // counters (stats runs only; thread 0 keeps them): appended A, compactions R, work W,
   // largest buffer, threshold monotone, compaction time, block barrier time, start of the
   // final compaction, elements read and the sum of their indices
@@ -1359,7 +1360,8 @@ template <int DT, int WAVES, int CPW, int D, bool MERGE, bool STATS>
 __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amdgpu_buffer_rsrc_t rs, uint32_t len,
                                                 uint32_t idx_base, uint32_t k, uint32_t B2, const BlockOrder& ord,
                                                 uint32_t ilo, uint32_t ihi, bool lockstep, uint32_t warm,
-                                                bool presample, uint32_t gshift, const OutSpec* fso, BodyOut& out) {
+                                                unsigned long long* share, bool presample, uint32_t gshift,
+                                                const OutSpec* fso, BodyOut& out) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t IB = MERGE ? 8 : (DT == DS_BF16 ? 2 : 4);  // bytes per item
   constexpr uint32_t VEC = 16 / IB;                            // items per lane per chunk
@@ -1392,6 +1394,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   // threshold state (uniform across the workgroup; it changes only at compactions)
   uint32_t mode = 0, thr_s = ~0u, thr_n = ~0u;  // mode 0: accept everything (no threshold yet)
   uint32_t t_key = 0, t_idx = 0, maxkey = 0;
+  uint32_t f_idx = 0;  // the filter's index threshold (its key threshold is in thr_s / thr_n)
   uint32_t nsurv = 0, hpar = 0;
   uint32_t warm_left = warm;  // blocks of the warm-up window still to come
   bool sur_a = false;  // survivors in set A (else set B)
@@ -1434,10 +1437,20 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
       sc.reads = 0;
       sc.index_sum = 0;
     }
+    if (share) {  // what the row's other slices have published so far
+      const uint64_t g = __hip_atomic_load(share, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sc.shr[0] = static_cast<uint32_t>(g);
+      sc.shr[1] = static_cast<uint32_t>(g >> 32);
+    }
   }
   if (tab)
     for (uint32_t i = tid; i < ng; i += NT) L.ordt[i] = ord.at(i);
   lds_sync();
+  if (share && (sc.shr[0] | sc.shr[1]) != 0) {
+    // filter with the row's threshold from the start (no own threshold yet)
+    f_idx = ~sc.shr[0];
+    filter_thresholds<DT>(sc.shr[1], mode, thr_s, thr_n);
+  }
 
   bool sorted = false;
   // A compaction of the nsurv survivors and the napp entries appended since the last one.
@@ -1477,6 +1490,33 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   };
 
   // In-loop compaction (every wave calls it at the same barrier count), then the new filter.
+  // The filter's threshold: the slice's own (T0 or the last compaction's k-th entry), or, with
+  // a shared row threshold, the larger of it and the row's. The slice publishes its own to
+  // the row's word with an atomic maximum and reads back what the row's slices published so
+  // far. Every published value ranks at or below the row's k-th element (a slice's k-th best
+  // so far, or a lower bound of it), so filtering with it drops nothing of the row's top k;
+  // compactions keep the slice's own threshold (the buffer may hold entries below the row's).
+  auto set_filter = [&]() {
+    uint32_t fk = t_key, fi = t_idx;
+    if (share) {
+      if (tid == 0) {
+        const uint64_t old =
+            __hip_atomic_fetch_max(share, static_cast<unsigned long long>(comp_of(t_key, t_idx)), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        sc.shr[0] = static_cast<uint32_t>(old);
+        sc.shr[1] = static_cast<uint32_t>(old >> 32);
+      }
+      lds_sync();
+      const uint64_t g = (static_cast<uint64_t>(sc.shr[1]) << 32) | sc.shr[0];
+      if (g > comp_of(fk, fi)) {
+        fk = static_cast<uint32_t>(g >> 32);
+        fi = ~static_cast<uint32_t>(g);
+      }
+    }
+    f_idx = fi;
+    filter_thresholds<DT>(fk, mode, thr_s, thr_n);
+  };
+
   auto in_loop = [&](uint32_t napp) {
     [[maybe_unused]] const uint64_t prev_c = comp_of(t_key, t_idx);
     [[maybe_unused]] const bool had_t = nsurv != 0;
@@ -1493,7 +1533,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     }
     nsurv = k;
     if constexpr (!MERGE)
-      filter_thresholds<DT>(t_key, mode, thr_s, thr_n);
+      set_filter();
     else
       mode = 1;
   };
@@ -1621,9 +1661,9 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
           }
         }
         presample_from(lmax);
-        filter_thresholds<DT>(t_key, mode, thr_s, thr_n);
+        set_filter();
       }
-      const bool strict = idx_base + blk_lo > t_idx;
+      const bool strict = idx_base + blk_lo > f_idx;
       const uint32_t thr = strict ? thr_s : thr_n;
       if (mode == 0 && blk_lo + B <= len) {
         // accept everything: each wave stores its chunks (raw) contiguously
@@ -1915,6 +1955,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), false, STATS>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
                                                                    slice_lo + len - 1u, p.lockstep != 0,
                                                                    static_cast<uint32_t>(p.warmup),
+                                                                   p.share ? p.share + row : nullptr,
                                                                    p.presample != 0, gshift,
                                                                    own_sort ? &fso : nullptr, bo);
 
@@ -2036,7 +2077,7 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), true, false>(L, sc, rs, len, 0u, k, B2, ord, 0u,
                                                                   static_cast<uint32_t>(p.n - 1), false, 0u,
-                                                                  p.presample != 0, 0u, &fso, bo);
+                                                                  nullptr, p.presample != 0, 0u, &fso, bo);
   if (bo.sorted) return;
   if (p.unsorted) {
     for (uint32_t i = tid; i < k; i += NT)

@@ -40,6 +40,7 @@ struct SelectParams {
   int32_t lockstep;          // nonzero: a barrier and the buffer check after every block
   int32_t unsorted;          // slices == 1: the k survivors may be written in any order
   int32_t warmup;            // blocks of the warm-up window (0: none)
+  unsigned long long* share; // NULL, or one shared threshold word per row (zero on entry)
 };
 
 // The merge of split rows. The merge kernel: one workgroup per row runs DeepSelect over the
@@ -123,5 +124,6 @@ hipError_t launch_merge_lists(int dtype, const MergeParams& p, int64_t rows, hip
 hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 int64_t probe_read_groups(int64_t bytes);
 hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+hipError_t launch_zero_words(unsigned long long* p, int64_t n, hipStream_t stream);
 
 }  // namespace ds

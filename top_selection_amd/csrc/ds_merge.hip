@@ -147,6 +147,20 @@ hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hip
   return hipGetLastError();
 }
 
+// Zeroes n 64-bit words (the shared row thresholds before a call's select launch): a kernel,
+// not a memset, so that a captured graph replays it like any other launch.
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned long long* p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0ull;
+}
+
+hipError_t launch_zero_words(unsigned long long* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t g = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<uint32_t>(g > 1024 ? 1024 : g)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
   const int64_t g = probe_read_groups(bytes);
   hipLaunchKernelGGL(probe_copy_kernel, dim3(static_cast<uint32_t>(g)), dim3(kProbeThreads), 0, stream,
