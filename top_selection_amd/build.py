@@ -28,13 +28,12 @@ FLAGS = [
 ]
 
 # (object name, source, extra flags)
-UNITS = [("select_bf16", "ds_select.hip", ["-DDS_PART_DT=0", "-DDS_PART_STATS=0"]),
-         ("select_fp32", "ds_select.hip", ["-DDS_PART_DT=1", "-DDS_PART_STATS=0"]),
-         ("select_bf16_stats", "ds_select.hip", ["-DDS_PART_DT=0", "-DDS_PART_STATS=1"]),
-         ("select_fp32_stats", "ds_select.hip", ["-DDS_PART_DT=1", "-DDS_PART_STATS=1"]),
-         ("merge", "ds_merge.hip", []),
-         ("noalloc", "ds_noalloc.hip", []),
-         ("api", "ds_api.cpp", [])]
+UNITS = [(f"select_{dt}{'_stats' if st else ''}{'_ext' if ex else ''}", "ds_select.hip",
+          [f"-DDS_PART_DT={d}", f"-DDS_PART_STATS={st}", f"-DDS_PART_EXT={ex}"])
+         for d, dt in ((0, "bf16"), (1, "fp32")) for st in (0, 1) for ex in (0, 1)] + [
+    ("merge", "ds_merge.hip", []),
+    ("noalloc", "ds_noalloc.hip", []),
+    ("api", "ds_api.cpp", [])]
 
 NOISE = "packed-fp32-ops"
 

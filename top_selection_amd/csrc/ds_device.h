@@ -1883,7 +1883,9 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
 }
 
 // --------------------------------------------------------------------------- select kernel
-template <int DT, int WAVES, int CPW, bool STATS>
+// EXT: the instantiation that serves ragged rows, the warm-up window and the shared row
+// threshold; the plain one (EXT = false) has none of their code.
+template <int DT, int WAVES, int CPW, bool STATS, bool EXT>
 __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t EB = DT == DS_BF16 ? 2 : 4;
@@ -1898,9 +1900,11 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   xcd_unit(blockIdx.x, static_cast<uint32_t>(p.slices), gridDim.x / static_cast<uint32_t>(p.slices), row, slice);
   const uint32_t slice_lo = slice * static_cast<uint32_t>(p.slice_len);
   int64_t n_row = p.n;  // this row's length
-  if (p.lens) {
-    const int64_t l = p.lens[row];
-    n_row = l < 0 ? 0 : (l < n_row ? l : n_row);
+  if constexpr (EXT) {
+    if (p.lens) {
+      const int64_t l = p.lens[row];
+      n_row = l < 0 ? 0 : (l < n_row ? l : n_row);
+    }
   }
   const int64_t rest = n_row - static_cast<int64_t>(slice_lo);
   const uint32_t len = rest <= 0 ? 0u : static_cast<uint32_t>(min(p.slice_len, rest));
@@ -1910,7 +1914,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   [[maybe_unused]] uint64_t t_start = 0;
   if constexpr (STATS) t_start = wall_clock64();
 
-  if (len == 0) {
+  if (EXT && len == 0) {
     // a slice past its row's end (ragged rows): its k entries are all padding, which ranks
     // below every element (the row's outputs past its length read index -1)
     if (p.slices == 1) {
@@ -1954,8 +1958,8 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), false, STATS>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
                                                                    slice_lo + len - 1u, p.lockstep != 0,
-                                                                   static_cast<uint32_t>(p.warmup),
-                                                                   p.share ? p.share + row : nullptr,
+                                                                   EXT ? static_cast<uint32_t>(p.warmup) : 0u,
+                                                                   EXT && p.share ? p.share + row : nullptr,
                                                                    p.presample != 0, gshift,
                                                                    own_sort ? &fso : nullptr, bo);
 

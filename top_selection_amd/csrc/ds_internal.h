@@ -109,11 +109,17 @@ int topk_auto(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k,
               void* out_vals, int32_t* out_idx, void* stream, WorkspaceSource get_ws);
 
 // The select-kernel launcher of one element type and counter mode (one object each).
-#define DS_SELECT_PART_NAME(dt, st) launch_select_part_##dt##_##st
-hipError_t DS_SELECT_PART_NAME(0, 0)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream);
-hipError_t DS_SELECT_PART_NAME(0, 1)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream);
-hipError_t DS_SELECT_PART_NAME(1, 0)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream);
-hipError_t DS_SELECT_PART_NAME(1, 1)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream);
+#define DS_SELECT_PART_NAME(dt, st, ex) launch_select_part_##dt##_##st##_##ex
+#define DS_DECLARE_SELECT_PART(dt, st, ex) \
+  hipError_t DS_SELECT_PART_NAME(dt, st, ex)(int shape, const SelectParams& p, int64_t rows, size_t lds, hipStream_t stream)
+DS_DECLARE_SELECT_PART(0, 0, 0);
+DS_DECLARE_SELECT_PART(0, 0, 1);
+DS_DECLARE_SELECT_PART(0, 1, 0);
+DS_DECLARE_SELECT_PART(0, 1, 1);
+DS_DECLARE_SELECT_PART(1, 0, 0);
+DS_DECLARE_SELECT_PART(1, 0, 1);
+DS_DECLARE_SELECT_PART(1, 1, 0);
+DS_DECLARE_SELECT_PART(1, 1, 1);
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,

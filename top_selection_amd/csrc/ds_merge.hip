@@ -110,16 +110,24 @@ size_t select_lds_bytes(int k, int block, int slack, int waves) {
   return (2 * (k4 + pc + kDummySlots) + 2 * k4 + 2 * kBins + kOrdCap) * 4 + sizeof(Scalars);
 }
 
-// The counters are a separate instantiation (its own object), so the kernel that runs
-// without them carries no counter code.
+// The counters and the extended features (ragged rows, the warm-up window, the shared row
+// threshold) are separate instantiations (objects of their own), so the kernel of a plain
+// call carries none of their code.
 hipError_t launch_select(int dtype, int shape_index, const SelectParams& p, int64_t rows, size_t lds_bytes,
                          hipStream_t stream) {
   const size_t dyn = lds_bytes - sizeof(Scalars);
-  if (dtype == DS_BF16)
-    return p.stats ? DS_SELECT_PART_NAME(0, 1)(shape_index, p, rows, dyn, stream)
-                   : DS_SELECT_PART_NAME(0, 0)(shape_index, p, rows, dyn, stream);
-  return p.stats ? DS_SELECT_PART_NAME(1, 1)(shape_index, p, rows, dyn, stream)
-                 : DS_SELECT_PART_NAME(1, 0)(shape_index, p, rows, dyn, stream);
+  const bool ext = p.lens || p.warmup || p.share;
+  const int part = (dtype == DS_BF16 ? 0 : 4) + (p.stats ? 2 : 0) + (ext ? 1 : 0);
+  switch (part) {
+    case 0: return DS_SELECT_PART_NAME(0, 0, 0)(shape_index, p, rows, dyn, stream);
+    case 1: return DS_SELECT_PART_NAME(0, 0, 1)(shape_index, p, rows, dyn, stream);
+    case 2: return DS_SELECT_PART_NAME(0, 1, 0)(shape_index, p, rows, dyn, stream);
+    case 3: return DS_SELECT_PART_NAME(0, 1, 1)(shape_index, p, rows, dyn, stream);
+    case 4: return DS_SELECT_PART_NAME(1, 0, 0)(shape_index, p, rows, dyn, stream);
+    case 5: return DS_SELECT_PART_NAME(1, 0, 1)(shape_index, p, rows, dyn, stream);
+    case 6: return DS_SELECT_PART_NAME(1, 1, 0)(shape_index, p, rows, dyn, stream);
+    default: return DS_SELECT_PART_NAME(1, 1, 1)(shape_index, p, rows, dyn, stream);
+  }
 }
 
 hipError_t launch_merge_lists(int dtype, const MergeParams& p, int64_t rows, hipStream_t stream) {
