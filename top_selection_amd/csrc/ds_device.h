@@ -1196,8 +1196,9 @@ __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_
 // same step with clamped, always valid indices; equal entries of earlier lists count as
 // above). Padding (composite 0) ranks below every element; it is placed only when the lists
 // hold fewer than k elements together, as padding. Places the entries of lists [l0, l1)
-// (all lists are loaded and searched).
-template <int DT, int WAVES, uint32_t MAXS>
+// (all lists are loaded and searched); each thread places EB entries at a time, their
+// searches interleaved step by step (long lists: the searches' LDS round trips overlap).
+template <int DT, int WAVES, uint32_t MAXS, uint32_t EB>
 __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint32_t k, uint32_t pk, uint64_t* lds,
                                               void* out_vals, IdxOut out_idx, uint2* pairs, uint64_t at0,
                                               uint32_t l0, uint32_t l1) {
@@ -1267,30 +1268,44 @@ __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint
 #pragma unroll
     for (uint32_t q = 0; q < MAXS; ++q) nq[q] = q < S ? k : 0u;
   }
-  for (uint32_t e = l0 * k + tid; e < l1 * k; e += NT) {
-    uint32_t s = 0;
+  const uint32_t e_end = l1 * k;
+  for (uint32_t e0 = l0 * k + tid; e0 < e_end; e0 += EB * NT) {
+    uint64_t c[EB];
+    uint32_t s[EB], pos[EB][MAXS];
+    bool act[EB];
 #pragma unroll
-    for (uint32_t q = 1; q < MAXS; ++q) s += (q < S && e >= q * k) ? 1u : 0u;
-    const uint64_t c = lw[e];
-    if (c < T) continue;
-    uint32_t pos[MAXS];
+    for (uint32_t b = 0; b < EB; ++b) {
+      const uint32_t e = e0 + b * NT;
+      s[b] = 0;
 #pragma unroll
-    for (uint32_t q = 0; q < MAXS; ++q) pos[q] = 0;
-    for (uint32_t step = top_n; step > 0; step >>= 1) {
-      uint64_t x[MAXS];
+      for (uint32_t q = 1; q < MAXS; ++q) s[b] += (q < S && e >= q * k) ? 1u : 0u;
+      c[b] = e < e_end ? lw[e] : 0ull;
+      act[b] = e < e_end && c[b] >= T;  // entries below T are searched but not placed
 #pragma unroll
-      for (uint32_t q = 0; q < MAXS; ++q)  // always a valid address; empty prefixes never move pos
-        x[q] = lw[min(q, S - 1u) * k + min(pos[q] + step, max(nq[q], 1u)) - 1u];
-#pragma unroll
-      for (uint32_t q = 0; q < MAXS; ++q) {
-        const bool above = x[q] > c || (q < s && x[q] == c);
-        pos[q] = (pos[q] + step <= nq[q] && above) ? pos[q] + step : pos[q];
-      }
+      for (uint32_t q = 0; q < MAXS; ++q) pos[b][q] = 0;
     }
-    uint32_t rank = e - s * k;
+    for (uint32_t step = top_n; step > 0; step >>= 1) {
+      uint64_t x[EB][MAXS];
 #pragma unroll
-    for (uint32_t q = 0; q < MAXS; ++q) rank += (q < S && q != s) ? pos[q] : 0u;
-    if (rank < k) store_out<DT>(out_vals, out_idx, pairs, at0 + rank, c);
+      for (uint32_t b = 0; b < EB; ++b)
+#pragma unroll
+        for (uint32_t q = 0; q < MAXS; ++q)  // always a valid address; empty prefixes never move pos
+          x[b][q] = lw[min(q, S - 1u) * k + min(pos[b][q] + step, max(nq[q], 1u)) - 1u];
+#pragma unroll
+      for (uint32_t b = 0; b < EB; ++b)
+#pragma unroll
+        for (uint32_t q = 0; q < MAXS; ++q) {
+          const bool above = x[b][q] > c[b] || (q < s[b] && x[b][q] == c[b]);
+          pos[b][q] = (pos[b][q] + step <= nq[q] && above) ? pos[b][q] + step : pos[b][q];
+        }
+    }
+#pragma unroll
+    for (uint32_t b = 0; b < EB; ++b) {
+      uint32_t rank = e0 + b * NT - s[b] * k;
+#pragma unroll
+      for (uint32_t q = 0; q < MAXS; ++q) rank += (q < S && q != s[b]) ? pos[b][q] : 0u;
+      if (act[b] && rank < k) store_out<DT>(out_vals, out_idx, pairs, at0 + rank, c[b]);
+    }
   }
 }
 
@@ -2098,7 +2113,7 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
 // when the level has one group). Each workgroup places p.per_wg lists of one group; the
 // grid is rows x groups x ceil(group / per_wg), and workgroups past a short last group's
 // lists return at once.
-template <int DT, int WAVES, uint32_t MAXS>
+template <int DT, int WAVES, uint32_t MAXS, uint32_t EB>
 __global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(MergeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const uint32_t S = static_cast<uint32_t>(p.lists), G = static_cast<uint32_t>(p.group);
@@ -2116,7 +2131,7 @@ __global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(MergeParams p) 
   const uint2* src = p.ws + row * p.row_entries + static_cast<uint64_t>(first) * k;
   uint2* pairs = p.dst ? p.dst + row * p.dst_row_entries + static_cast<uint64_t>(g) * k : nullptr;
   const uint64_t at0 = p.dst ? 0u : row * k;
-  merge_lists_t<DT, WAVES, MAXS>(src, gl, k, pk, reinterpret_cast<uint64_t*>(lds), p.out_vals, p.out_idx, pairs, at0,
+  merge_lists_t<DT, WAVES, MAXS, EB>(src, gl, k, pk, reinterpret_cast<uint64_t*>(lds), p.out_vals, p.out_idx, pairs, at0,
                                  l0, min(l0 + per, gl));
 }
 

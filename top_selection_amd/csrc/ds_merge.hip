@@ -56,12 +56,13 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(u32x4* dst, c
 // Rows per list-merge launch (the grid's z dimension; a multiple of 8, see xcd_unit).
 constexpr int64_t kMaxGridRows = 65528;
 
-// One instantiation per bound on the lists merged together.
-template <int DT, uint32_t MAXS>
+// One instantiation per bound on the lists merged together, and per number of entries a
+// thread searches at once.
+template <int DT, uint32_t MAXS, uint32_t EB>
 hipError_t launch_merge_lists_t(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
-  auto kern = merge_lists_kernel<DT, kListMergeWaves, MAXS>;
+  auto kern = merge_lists_kernel<DT, kListMergeWaves, MAXS, EB>;
   {
-    const hipError_t e = allow_lds<merge_lists_kernel<DT, kListMergeWaves, MAXS>>(lds);
+    const hipError_t e = allow_lds<merge_lists_kernel<DT, kListMergeWaves, MAXS, EB>>(lds);
     if (e != hipSuccess) return e;
   }
   const int64_t G = p.group, wpg = (G + p.per_wg - 1) / p.per_wg, groups = (p.lists + G - 1) / G;
@@ -81,11 +82,17 @@ hipError_t launch_merge_lists_t(const MergeParams& p, int64_t rows, size_t lds, 
 template <int DT>
 hipError_t launch_merge_lists_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
   const int32_t g = p.group < p.lists ? p.group : p.lists;
-  if (g <= 2) return launch_merge_lists_t<DT, 2>(p, rows, lds, stream);
-  if (g <= 4) return launch_merge_lists_t<DT, 4>(p, rows, lds, stream);
-  if (g <= 8) return launch_merge_lists_t<DT, 8>(p, rows, lds, stream);
+  // long lists: every thread searches several entries at once (small groups keep the
+  // registers of the interleaved searches in bounds)
+  const bool longl = p.k >= 1024;
+  if (g <= 2) return longl ? launch_merge_lists_t<DT, 2, 4>(p, rows, lds, stream)
+                           : launch_merge_lists_t<DT, 2, 1>(p, rows, lds, stream);
+  if (g <= 4) return longl ? launch_merge_lists_t<DT, 4, 4>(p, rows, lds, stream)
+                           : launch_merge_lists_t<DT, 4, 1>(p, rows, lds, stream);
+  if (g <= 8) return longl ? launch_merge_lists_t<DT, 8, 2>(p, rows, lds, stream)
+                           : launch_merge_lists_t<DT, 8, 1>(p, rows, lds, stream);
   static_assert(kMaxListGroup == 16, "instantiations cover groups up to kMaxListGroup");
-  return launch_merge_lists_t<DT, kMaxListGroup>(p, rows, lds, stream);
+  return launch_merge_lists_t<DT, kMaxListGroup, 1>(p, rows, lds, stream);
 }
 
 template <int DT>
