@@ -380,7 +380,7 @@ def write_sq(workload, k, folder, command):
     log(f"[bench] wrote {path}")
 
 
-def write_trace(workload, trace_dir, command):
+def write_trace(workload, k, trace_dir, command):
     """Summary of a rocprofv3 --kernel-trace --stats run of bench.py into profiles/."""
     import csv
     import glob
@@ -392,10 +392,11 @@ def write_trace(workload, trace_dir, command):
     with open(paths[0]) as f:
         rows = list(csv.DictReader(f))
     lines = [
-        f"# Kernel trace, {workload}",
+        f"# Kernel trace, {workload} (k = {k})",
         "",
-        f"Workload: {w.description}; the bench's default plan, its timed steps plus warmup (graph, eager and "
-        f"warm passes, the select-only graph and one parity call).",
+        f"Workload: {w.description} (k = {k} here); the bench's default plan, its timed steps plus warmup "
+        f"(graph, eager and warm passes, the select-only graph, the probe reads, the per-call steps and one "
+        f"parity call).",
         "",
         "Command (on one MI355X, from the repository root; R is the repository path):",
         "",
@@ -413,7 +414,7 @@ def write_trace(workload, trace_dir, command):
         lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} % |")
     lines.append("")
-    path = os.path.join(ROOT, "profiles", f"kernels_{workload}_trace.md")
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}_k{k}_trace.md")
     with open(path, "w") as fh:
         fh.write("\n".join(lines))
     log(f"[bench] wrote {path}")
@@ -479,7 +480,8 @@ def main() -> int:
         write_counters(args.workload, *args.write_counters)
         return 0
     if args.write_trace:
-        write_trace(args.workload, *args.write_trace)
+        from workloads import gen as _gen
+        write_trace(args.workload, args.k or _gen.WORKLOADS[args.workload].ks[0], *args.write_trace)
         return 0
     if args.write_sq:
         from workloads import gen as _gen
