@@ -96,14 +96,16 @@ extern "C" {
  *   schedule   when the buffer is checked. DS_SCHEDULE_LOCKSTEP is the design note's schedule
  *              ("Algorithm", the DeepSelectTopk pseudocode): every wave of the workgroup
  *              filters its share of a block, a workgroup barrier follows, and then the buffer
- *              is compacted if it holds at least k + B2 entries. DS_SCHEDULE_FREE (the
- *              default; zero means it) drops the barrier after every block: each wave streams
+ *              is compacted if it holds at least k + B2 entries. DS_SCHEDULE_FREE drops the
+ *              barrier after every block: each wave streams
  *              its shares on its own, reserves buffer space with one atomic and checks the
  *              length itself after every share; a wave that sees k + B2 or more stops at a
  *              barrier and the waves compact together. A wave appends at most one more share
  *              after the length crosses k + B2, so the buffer bound k + B2 + B of the design
  *              note's notes still holds. The result is the same for both; only the counters
- *              (which elements were appended with which threshold) differ.
+ *              (which elements were appended with which threshold) differ. Zero (auto): FREE,
+ *              or LOCKSTEP when B2 < B / 2 (the buffer then fills within a block, and the
+ *              once-per-block check measured faster).
  */
 #define DS_SCHEDULE_AUTO 0
 #define DS_SCHEDULE_FREE 1

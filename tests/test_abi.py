@@ -187,10 +187,16 @@ def test_order_group_plan_field():
 
 
 def test_schedule_plan_field():
-    """The free-running schedule is the default; the lockstep schedule can be forced; other
-    values are rejected before any launch."""
+    """The free-running schedule is the default unless B2 < B / 2; either can be forced;
+    other values are rejected before any launch."""
     base = {"slices": 2}
-    assert ts.ds_topk_plan(4, 100000, 64, ts.BF16, base)["schedule"] == ts.SCHEDULE_FREE
+    for n, k in ((100000, 64), (131072, 512), (1 << 20, 4096), (1 << 28, 32)):
+        p = ts.ds_topk_plan(4, n, k, ts.BF16, base)
+        want = ts.SCHEDULE_LOCKSTEP if 2 * p["slack"] < p["block"] else ts.SCHEDULE_FREE
+        assert p["schedule"] == want, (n, k, p)
+        assert ts.ds_topk_plan(4, n, k, ts.BF16, dict(base, schedule=ts.SCHEDULE_FREE))["schedule"] == \
+            ts.SCHEDULE_FREE
+    assert ts.ds_topk_plan(4, 131072, 512, ts.BF16, {"slices": 4})["schedule"] == ts.SCHEDULE_FREE  # the indexer
     assert ts.ds_topk_plan(4, 100000, 64, ts.BF16, dict(base, schedule=ts.SCHEDULE_LOCKSTEP))["schedule"] == \
         ts.SCHEDULE_LOCKSTEP
     with pytest.raises(ts.DSError) as e:
