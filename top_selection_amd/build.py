@@ -25,6 +25,9 @@ FLAGS = [
     "-Wall",
     # never let the compiler form packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # LDS atomics here are issued by one lane on purpose; the atomic optimizer's wave
+    # reduction around them only adds instructions
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 # (object name, source, extra flags)
