@@ -1,5 +1,6 @@
-// Internal interface between the C-ABI layer (ds_api.cpp) and the HIP kernels
-// (ds_kernels.hip). Not installed; the public interface is include/dstopk.h.
+// Internal interface between the C-ABI layer (ds_api.cpp) and the HIP kernels (ds_device.h,
+// ds_select.hip, ds_merge.hip, ds_noalloc.hip). Not installed; the public interface is
+// include/dstopk.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
