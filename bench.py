@@ -97,9 +97,8 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
     idx = None if w.values_only else torch.empty((rows, k), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(src):
-        ts.ds_topk_slices(src, k, seed=seed, workspace=ws, out_vals=vals, out_idx=idx, indices=idx is not None)
-        ts.ds_topk_merge(rows, n, k, w.dtype, seed=seed, workspace=ws, out_vals=vals, out_idx=idx)
+    def step(src):  # one library call: the select launch and the merge launches
+        ts.ds_topk_ex(src, k, seed=seed, workspace=ws, out_vals=vals, out_idx=idx, indices=idx is not None)
 
     log(f"[bench] {w.name}: plan {plan}, pool {copies} copies, warmup {warmup}")
     for i in range(warmup):
@@ -107,11 +106,18 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
     torch.cuda.synchronize()
 
     def timed(get_src):
+        """K steps launched one by one (one library call each) between two events; then K
+        select launches with an event pair around each (host launch latency included)."""
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
-        mids = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
         t0.record(stream)
+        for i in range(steps):
+            step(get_src(i))
+        t1.record(stream)
+        torch.cuda.synchronize()
+        total = t0.elapsed_time(t1)
+        mids = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for i in range(steps):
             a, b = mids[i]
             a.record(stream)
@@ -119,9 +125,7 @@ def time_workload(ts, torch, w, k, steps, warmup, pool_mib, seed=1, verify=True)
                               indices=idx is not None)
             b.record(stream)
             ts.ds_topk_merge(rows, n, k, w.dtype, seed=seed, workspace=ws, out_vals=vals, out_idx=idx)
-        t1.record(stream)
         torch.cuda.synchronize()
-        total = t0.elapsed_time(t1)
         sel = [a.elapsed_time(b) for a, b in mids]
         return total / steps, sum(sel) / len(sel)
 
@@ -529,8 +533,8 @@ def main() -> int:
         "timing": "K steps captured in one HIP graph, replayed between two events",
         "eager": {"value": round(r["in_bytes"] / (r["ms_eager"] * 1e-3) / 1e9, 2),
                   "ms_per_step": round(r["ms_eager"], 6), "select_us": round(r["sel_eager"] * 1e3, 3),
-                  "note": "the same K steps launched one by one; select_us spans event to event around "
-                          "each select launch (host launch latency included)"},
+                  "note": "the same K steps launched one by one (one ds_topk_ex call each); select_us spans "
+                          "event to event around each select launch (host launch latency included)"},
         "warm": {"value": round(r["in_bytes"] / (r["ms_warm"] * 1e-3) / 1e9, 2), "ms_per_step": round(r["ms_warm"], 6),
                  "note": "same input buffer every step (may be served by the Infinity Cache)"},
         "pages_style_gbs": round((r["in_bytes"] + w.rows * k * (w.elem_bytes + (0 if w.values_only else 4)))

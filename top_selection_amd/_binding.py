@@ -151,10 +151,17 @@ def dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
 
 
-def _stream_handle(stream) -> Optional[int]:
+def _stream_handle(stream, device=None) -> Optional[int]:
+    """The hipStream_t of `stream`, or of torch's current stream on `device` (read without
+    building a Stream object when torch offers the raw accessor)."""
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        index = device.index if device is not None and device.index is not None else torch.cuda.current_device()
+        return raw(index)
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _prep(x, k: int, values: bool, indices: bool, out_vals, out_idx, idx64: bool = False):
@@ -190,7 +197,7 @@ def ds_topk(x, k: int, seed: int = 0, values: bool = True, indices: bool = True,
     rows, n, rs, dt, out_vals, out_idx = _prep(x, k, values, indices, out_vals, out_idx)
     st = lib().ds_topk(x.data_ptr() if rows else None, rows, n, rs, k, dt, seed & 0xFFFFFFFFFFFFFFFF,
                        out_vals.data_ptr() if out_vals is not None else None,
-                       out_idx.data_ptr() if out_idx is not None else None, _stream_handle(stream))
+                       out_idx.data_ptr() if out_idx is not None else None, _stream_handle(stream, x.device))
     if st != DS_OK:
         raise DSError(st, "ds_topk")
     return out_vals, out_idx
@@ -204,7 +211,7 @@ def ds_topk_noalloc(x, k: int, seed: int = 0, values: bool = True, indices: bool
     rows, n, rs, dt, out_vals, out_idx = _prep(x, k, values, indices, out_vals, out_idx)
     st = lib().ds_topk_noalloc(x.data_ptr() if rows else None, rows, n, rs, k, dt, seed & 0xFFFFFFFFFFFFFFFF,
                                out_vals.data_ptr() if out_vals is not None else None,
-                               out_idx.data_ptr() if out_idx is not None else None, _stream_handle(stream))
+                               out_idx.data_ptr() if out_idx is not None else None, _stream_handle(stream, x.device))
     if st != DS_OK:
         raise DSError(st, "ds_topk_noalloc")
     return out_vals, out_idx
@@ -236,7 +243,7 @@ def ds_topk_ex(x, k: int, seed: int = 0, workspace=None, cfg: Optional[Dict[str,
                           seed & 0xFFFFFFFFFFFFFFFF,
                           out_vals.data_ptr() if out_vals is not None else None,
                           out_idx.data_ptr() if out_idx is not None else None, ws_ptr, ws_bytes, _cfg(cfg),
-                          stats.data_ptr() if stats is not None else None, _stream_handle(stream))
+                          stats.data_ptr() if stats is not None else None, _stream_handle(stream, x.device))
     if st != DS_OK:
         raise DSError(st, "ds_topk_ex")
     return out_vals, out_idx
@@ -252,7 +259,7 @@ def ds_topk_slices(x, k: int, seed: int = 0, workspace=None, cfg: Optional[Dict[
                               seed & 0xFFFFFFFFFFFFFFFF,
                               out_vals.data_ptr() if out_vals is not None else None,
                               out_idx.data_ptr() if out_idx is not None else None, ws_ptr, ws_bytes, _cfg(cfg),
-                              stats.data_ptr() if stats is not None else None, _stream_handle(stream))
+                              stats.data_ptr() if stats is not None else None, _stream_handle(stream, x.device))
     if st != DS_OK:
         raise DSError(st, "ds_topk_slices")
     return out_vals, out_idx
@@ -266,7 +273,8 @@ def ds_topk_merge(rows: int, n: int, k: int, dtype: int, seed: int = 0, workspac
     st = lib().ds_topk_merge(_lens_ptr(lens, rows), rows, n, k, dtype, seed & 0xFFFFFFFFFFFFFFFF,
                              out_vals.data_ptr() if out_vals is not None else None,
                              out_idx.data_ptr() if out_idx is not None else None, ws_ptr, ws_bytes, _cfg(cfg),
-                             _stream_handle(stream))
+                             _stream_handle(stream, out_vals.device if out_vals is not None else
+                                            (out_idx.device if out_idx is not None else None)))
     if st != DS_OK:
         raise DSError(st, "ds_topk_merge")
     return out_vals, out_idx
@@ -288,7 +296,7 @@ def ds_probe_read(src, sink=None, stream=None):
     words = int(lib().ds_probe_sink_words(nbytes))
     if sink is None:
         sink = torch.empty(words, dtype=torch.int32, device=src.device)
-    st = lib().ds_probe_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream_handle(stream))
+    st = lib().ds_probe_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream_handle(stream, src.device))
     if st != DS_OK:
         raise DSError(st, "ds_probe_read")
     return sink
@@ -298,7 +306,7 @@ def ds_probe_copy(dst, src, stream=None):
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst too small")
-    st = lib().ds_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream_handle(stream))
+    st = lib().ds_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream_handle(stream, src.device))
     if st != DS_OK:
         raise DSError(st, "ds_probe_copy")
     return dst

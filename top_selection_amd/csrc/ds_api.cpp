@@ -2,6 +2,7 @@
 // workspace cache of ds_topk, and dispatch to the HIP kernels. Validation is pure host
 // code and runs before any HIP call, so every error path works without a GPU.
 #include <algorithm>
+#include <cstring>
 #include <cmath>
 #include <map>
 #include <mutex>
@@ -268,6 +269,38 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   return DS_OK;
 }
 
+// make_plan behind a one-entry cache per thread: a caller that repeats the same call (the
+// usual case in a serving or training loop) skips the planning.
+struct PlanMemo {
+  bool valid = false;
+  int64_t rows = 0, n = 0;
+  int k = 0, dtype = 0, cus = 0;
+  bool has_cfg = false;
+  ds_config cfg{};
+  int status = DS_OK;
+  Plan plan{};
+};
+
+int cached_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, int cus, Plan* out) {
+  thread_local PlanMemo memo;
+  const bool same = memo.valid && memo.rows == rows && memo.n == n && memo.k == k && memo.dtype == dtype &&
+                    memo.cus == cus && memo.has_cfg == (cfg != nullptr) &&
+                    (!cfg || std::memcmp(&memo.cfg, cfg, sizeof(ds_config)) == 0);
+  if (!same) {
+    memo.valid = true;
+    memo.rows = rows;
+    memo.n = n;
+    memo.k = k;
+    memo.dtype = dtype;
+    memo.cus = cus;
+    memo.has_cfg = cfg != nullptr;
+    memo.cfg = cfg ? *cfg : ds_config{};
+    memo.status = make_plan(rows, n, k, dtype, cfg, cus, &memo.plan);
+  }
+  if (memo.status == DS_OK) *out = memo.plan;
+  return memo.status;
+}
+
 int check_call(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k, int dtype, const void* out_vals,
                const void* out_idx) {
   int st = check_basic(rows, n, k, dtype);
@@ -374,7 +407,7 @@ int plan_with_workspace(int64_t rows, int64_t n, int k, int dtype, const ds_conf
     cus = device_cu_count();
     if (cus <= 0) return DS_ERR_DEVICE;
   }
-  int st = make_plan(rows, n, k, dtype, cfg, cus, p);
+  int st = cached_plan(rows, n, k, dtype, cfg, cus, p);
   if (st != DS_OK) return st;
   if (p->ws_bytes) {
     if (!workspace || ws_bytes < p->ws_bytes) return DS_ERR_WORKSPACE;
@@ -444,7 +477,7 @@ int topk_auto(const void* x, int64_t rows, int64_t n, int64_t row_stride, int k,
   const int cus = device_cu_count();
   if (cus <= 0) return DS_ERR_DEVICE;
   Plan p;
-  st = make_plan(rows, n, k, dtype, nullptr, cus, &p);
+  st = cached_plan(rows, n, k, dtype, nullptr, cus, &p);
   if (st != DS_OK) return st;
   void* ws = nullptr;
   if (p.ws_bytes) {
@@ -482,7 +515,7 @@ int ds_topk_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg
     if (cus <= 0) return DS_ERR_DEVICE;
   }
   Plan p;
-  st = make_plan(rows, n, k, dtype, cfg, cus, &p);
+  st = cached_plan(rows, n, k, dtype, cfg, cus, &p);
   if (st != DS_OK) return st;
   out->block = p.block;
   out->slack = p.slack;
@@ -509,7 +542,7 @@ int ds_topk_workspace_size(int64_t rows, int64_t n, int k, int dtype, const ds_c
     if (cus <= 0) return DS_ERR_DEVICE;
   }
   Plan p;
-  st = make_plan(rows, n, k, dtype, cfg, cus, &p);
+  st = cached_plan(rows, n, k, dtype, cfg, cus, &p);
   if (st != DS_OK) return st;
   *bytes = p.ws_bytes;
   return DS_OK;
