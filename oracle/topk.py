@@ -14,7 +14,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle_topk.cpp")
-_LIB = os.path.join(_HERE, "liboracle_topk.so")
+# DS_ORACLE_LIB names another build of the same source (the sanitizer test's); it is then
+# loaded as it is, not rebuilt
+_LIB = os.environ.get("DS_ORACLE_LIB") or os.path.join(_HERE, "liboracle_topk.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -32,7 +34,8 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
+            if not os.environ.get("DS_ORACLE_LIB"):
+                build()
             lib = ctypes.CDLL(_LIB)
             lib.oracle_topk.restype = ctypes.c_int
             lib.oracle_topk.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,

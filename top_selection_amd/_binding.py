@@ -33,7 +33,8 @@ OUTPUT_UNSORTED, OUTPUT_INDEX_INT64 = 1, 2
 SHARE_AUTO, SHARE_OFF, SHARE_ON = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdstopk.so")
+# DS_LIBRARY names another build of the library (e.g. one with host-side sanitizers)
+LIB_PATH = os.environ.get("DS_LIBRARY") or os.path.join(_HERE, "libdstopk.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dstopk.h")
 
 

@@ -47,15 +47,23 @@ def _run(cmd):
     return res.returncode, msgs
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (the device code is built as
+# usual): a separate library for checking the host code, loaded through DS_LIBRARY with the
+# clang ASan runtime preloaded.
+HOST_SANITIZERS = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, jobs: int = 0, out: str = OUT, extra_flags=()) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     tag = "%d" % os.getpid()
+    flags = FLAGS + list(extra_flags)
     cmds = []
     objs = []
     for name, src, extra in UNITS:
         obj = os.path.join(OBJDIR, f"{name}.{tag}.o")
         objs.append(obj)
-        cmds.append([HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + flags + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 1))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(_run, cmds))
@@ -73,16 +81,24 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
             if os.path.exists(o):
                 os.remove(o)
         raise RuntimeError("hipcc failed")
-    tmp = OUT + ".tmp" + tag
-    rc, msgs = _run([HIPCC] + FLAGS + ["-shared", "-o", tmp] + objs)
+    tmp = out + ".tmp" + tag
+    rc, msgs = _run([HIPCC] + flags + ["-shared", "-o", tmp] + objs)
     for o in objs:
         os.remove(o)
     if rc != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
         raise RuntimeError(f"hipcc link failed ({rc})")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libdstopk.so for gfx950")
+    ap.add_argument("--host-sanitizers", metavar="LIB",
+                    help="build a copy with host-side ASan/UBSan at LIB instead of the library in place")
+    args = ap.parse_args()
+    if args.host_sanitizers:
+        print(build(verbose=True, out=os.path.abspath(args.host_sanitizers), extra_flags=HOST_SANITIZERS))
+    else:
+        print(build(verbose=True))
