@@ -290,6 +290,15 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
   return z ^ (z >> 31);
 }
 
+// A copy of a uniform value in a vector register: arithmetic on it runs in the vector units.
+// The CU's waves share one scalar unit, so uniform set-up arithmetic that every wave repeats
+// (the block order's keys, the first block ids) is cheaper spread over the SIMDs.
+__device__ __forceinline__ uint32_t to_vgpr(uint32_t s) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
+  return v;
+}
+
 __device__ __forceinline__ uint32_t lowbias32(uint32_t x) {
   x ^= x >> 16;
   x *= 0x7FEB352Du;
@@ -305,10 +314,15 @@ struct BlockOrder {
 
   __device__ void init(uint64_t seed, uint32_t row, uint32_t slice, uint32_t m_) {
     constexpr uint64_t G = 0x9E3779B97F4A7C15ull;
-    uint64_t h = mix64(seed + G * (static_cast<uint64_t>(row) + 1));
+    // lane l derives key l & 3 in vector registers; the four keys are then read back
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const uint64_t vseed = (static_cast<uint64_t>(to_vgpr(static_cast<uint32_t>(seed >> 32))) << 32) |
+                           to_vgpr(static_cast<uint32_t>(seed));
+    uint64_t h = mix64(vseed + G * (static_cast<uint64_t>(to_vgpr(row)) + 1));
     h = mix64(h + G * (static_cast<uint64_t>(slice) + 1));
+    const uint32_t mine = static_cast<uint32_t>(mix64(h + G * static_cast<uint64_t>((lane & 3u) + 1)));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) key[r] = static_cast<uint32_t>(mix64(h + G * static_cast<uint64_t>(r + 1)));
+    for (int r = 0; r < 4; ++r) key[r] = __builtin_amdgcn_readlane(mine, r);
     uint32_t b = 2;
     while ((1u << b) < m_) b += 2;
     half = b / 2;
@@ -1433,9 +1447,11 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   // set-up below (their ids come from the permutation directly, the rest from its table).
   u32x4 buf[D][CPW];
   uint32_t bids[D];
+  // the first D block ids: lane l evaluates position l mod D in vector registers (see to_vgpr)
+  const uint32_t first_bid = bid_direct(to_vgpr(0u) + lane % static_cast<uint32_t>(D));
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    bids[d] = bid_direct(d);
+    bids[d] = __builtin_amdgcn_readlane(first_bid, d);
 #pragma unroll
     for (uint32_t t = 0; t < CPW; ++t) buf[d][t] = load16(rs, addr(bids[d], t));
   }
