@@ -1768,25 +1768,24 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
               kmx = h[e] ? max(kmx, key) : kmx;
             }
           }
-          uint64_t mk[VEC];
-          uint32_t tot = 0;
+          // positions by vector arithmetic only (the CU's waves share one scalar unit): the
+          // lane's hit count, its exclusive prefix over the wave, one reservation; every
+          // element then goes to its slot or, if it is no hit, to the lane's dummy slot
+          uint32_t cnt = 0;
 #pragma unroll
-          for (uint32_t e = 0; e < VEC; ++e) {
-            mk[e] = ballot(h[e]);
-            tot += popc(mk[e]);
-          }
+          for (uint32_t e = 0; e < VEC; ++e) cnt += h[e] ? 1u : 0u;
+          const uint32_t incl = wave_incl_scan(cnt);
+          const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
           if (tot) {
-            uint32_t pos = app0 + reserve(tot, seen);
+            uint32_t pos = app0 + reserve(tot, seen) + incl - cnt;
             reserved = true;
             const uint32_t j0 = idx_base + first;
 #pragma unroll
             for (uint32_t e = 0; e < VEC; ++e) {
-              if (mk[e]) {
-                const uint32_t q = h[e] ? mbcnt(mk[e], pos) : L.dummy + lane;
-                L.ck[q] = s[t][e];
-                L.ci[q] = j0 + e;
-                pos += popc(mk[e]);
-              }
+              const uint32_t q = h[e] ? pos : L.dummy + lane;
+              L.ck[q] = s[t][e];
+              L.ci[q] = j0 + e;
+              pos += h[e] ? 1u : 0u;
             }
           }
         }
