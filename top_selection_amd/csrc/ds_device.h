@@ -232,9 +232,10 @@ __device__ __forceinline__ float value_of_key(uint32_t key) {
 }
 
 // Value-space bins: bin(v) = clamp((v - lo) * scale, 0, kBins - 1), truncated, for a window
-// [lo, hi] with scale = kBins / (hi - lo). Each step is a correctly rounded fp32 operation
-// (no contraction), so the bin is a non-decreasing function of the key and every thread that
-// evaluates it gets the same bin; values above hi land in the top bin.
+// [lo, hi] with scale = kBins times the hardware reciprocal of (hi - lo). Any positive scale
+// serves: each step is a deterministic fp32 operation (no contraction), so the bin is a
+// non-decreasing function of the key and every thread that evaluates it gets the same bin;
+// values above hi land in the top bin.
 struct VBins {
   float lo, scale;
 };
@@ -253,7 +254,7 @@ __device__ __forceinline__ bool vbins_of(uint32_t klo, uint32_t khi, VBins& vb) 
   const float lo = value_of_key<DT>(klo), hi = value_of_key<DT>(khi);
   const float span = hi - lo;
   vb.lo = lo;
-  vb.scale = static_cast<float>(kBins) / span;
+  vb.scale = static_cast<float>(kBins) * __builtin_amdgcn_rcpf(span);
   return __builtin_isfinite(lo) && __builtin_isfinite(hi) && span > 0.0f && __builtin_isfinite(span) &&
          __builtin_isfinite(vb.scale) && vb.scale > 0.0f;
 }
@@ -366,6 +367,7 @@ struct Scalars {
   uint32_t lkey[kListCap];     // pivot-bin entries
   uint32_t lidx[kListCap];
   uint32_t shr[2];             // the row's shared threshold as read by thread 0 (low, high word)
+  uint32_t big;                // one-pass final sort: a bin too full for it (falls back)
   // counters (stats runs only; thread 0 keeps them): appended A, compactions R, work W,
   // largest buffer, threshold monotone, compaction time, block barrier time, start of the
   // final compaction, elements read and the sum of their indices
@@ -501,7 +503,10 @@ __device__ __forceinline__ void scan_select(const uint32_t* h, uint32_t need, ui
 // the list is ranked to place the rest and find the threshold.
 //
 // With so (final call only) and a single value pass, the survivors are written sorted to
-// *so instead (sorted = true): a counting sort over the value bins (see below).
+// *so instead (sorted = true): a counting sort over the value bins (see below). A final call
+// with at most kFinalPer entries per thread takes the one-pass form of it (final_sorted),
+// which may use cbuf (room for k + 3 composites) and falls back to the above when a bin is
+// too full.
 //
 // Barriers: two per histogram pass (after the counts; after the scan result is published),
 // one after the scatter and one after the list is ranked.
@@ -737,11 +742,206 @@ __device__ __forceinline__ void scatter_all(const Segs& sg, uint32_t tid, uint32
   }
 }
 
+// Entries per thread that the one-pass final sort keeps in registers.
+constexpr uint32_t kFinalPer = 4;
+
+// The value of a raw score (the bits of the element; for bf16 the element sits in the top
+// half of the word): the same float as value_of_key(key_of_score(s)).
+template <int DT>
+__device__ __forceinline__ float value_of_score(uint32_t s) {
+  if constexpr (DT == DS_BF16)
+    return __uint_as_float(s & 0xFFFF0000u);
+  else
+    return __uint_as_float(s);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t vbin_of_value(float v, const VBins& vb) {
+#pragma clang fp contract(off)
+  const float t = (v - vb.lo) * vb.scale;
+  return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(t, 0.0f, static_cast<float>(kBins - 1u)));
+}
+
+// One-pass final compaction with sorted output, for at most kFinalPer * NT entries and
+// usable value bins (the common end of a stream). Every thread keeps up to kFinalPer
+// entries in registers and takes each one's place in its value bin from the histogram's
+// returning atomic (its arrival slot). All threads scan the bins together (BPT bins each,
+// then the wave totals); the bin that holds the k-th best entry is the pivot bin, and each
+// bin above it gets its first output slot (higher bins first). An entry above the pivot bin
+// is stored as a composite at its bin's first slot plus its arrival slot in cbuf, then ranked
+// against its bin's entries for its output position; the pivot bin's entries (a short list)
+// are ranked by one wave. When the pivot bin holds more than kListCap entries or a bin above
+// it more than kSortedBinCap, false is returned before any output is written, and the pass is
+// handed to the general compaction as its first value pass (the histogram in its layout, the
+// appended entries converted to keys in place, the waves' largest keys in sc.red). The
+// histograms here are plain (bin b at index b) until then; on success both are left dirty
+// (this is a stream's last compaction).
+// h is the current histogram (zero on entry), hs the other one; cbuf has room for k
+// composites and may overlap the entries (they are all in registers before it is written).
+template <int WAVES, int DT, bool RAW>
+__device__ __forceinline__ bool final_sorted(const Segs& sg, uint32_t k, const OutSpec so, const VBins& vb,
+                                             uint32_t* h, uint32_t* hs, uint64_t* cbuf, Scalars& sc,
+                                             uint32_t& tkey, uint32_t& tidx) {
+  constexpr uint32_t NT = WAVES * 64;
+  constexpr uint32_t BPT = kBins / NT;  // bins per thread in the scan
+  static_assert(kBins % NT == 0 && BPT >= 2 && BPT <= 32, "bins per thread");
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t n = sg.n0 + sg.n1;  // k < n <= kFinalPer * NT
+
+  // histogram with arrival slots; the entries stay in registers
+  uint32_t key[kFinalPer], id[kFinalPer], bin[kFinalPer], arr[kFinalPer];
+#pragma unroll
+  for (uint32_t j = 0; j < kFinalPer; ++j) {
+    const uint32_t e = tid + j * NT;
+    key[j] = 0;
+    id[j] = kSentinelIdx;
+    bin[j] = 0;
+    arr[j] = 0;
+    if (j * NT < n && e < n) {
+      const bool app = e < sg.n1;
+      const uint32_t w = app ? sg.k1[e] : sg.k0[e - sg.n1];
+      id[j] = app ? sg.i1[e] : sg.i0[e - sg.n1];
+      const bool raw = RAW && app;
+      key[j] = raw ? key_of_score<DT>(w) : w;
+      bin[j] = vbin_of_value<DT>(raw ? value_of_score<DT>(w) : value_of_key<DT>(w), vb);
+      arr[j] = __atomic_fetch_add(lds_ptr(&h[bin[j]]), 1u, __ATOMIC_RELAXED);
+    }
+  }
+  if (tid == 0) sc.big = 0;
+  lds_sync();
+
+  // bin scan: thread t holds bins [kBins - BPT (t + 1), kBins - BPT t), highest first in c[]
+  const uint32_t lo = kBins - BPT * (tid + 1u);
+  uint32_t c[BPT];
+#pragma unroll
+  for (uint32_t g = 0; g < BPT / 2; ++g) {
+    const uint2 q = *reinterpret_cast<const uint2*>(h + lo + 2u * g);
+    c[BPT - 1u - 2u * g] = q.x;
+    c[BPT - 2u - 2u * g] = q.y;
+  }
+  uint32_t s = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < BPT; ++i) s += c[i];
+  const uint32_t incl = wave_incl_scan(s);
+  if (lane == 63) sc.red[wave] = incl;
+  lds_sync();
+  // entries in higher bins: this wave's lanes below, then the earlier waves (an inclusive
+  // scan of the wave totals over the first lanes, read at the previous wave)
+  uint32_t wt = lane < static_cast<uint32_t>(WAVES) ? sc.red[lane] : 0u;
+  wt += __builtin_amdgcn_update_dpp(0u, wt, 0x111, 0xF, 0xF, true);
+  wt += __builtin_amdgcn_update_dpp(0u, wt, 0x112, 0xF, 0xF, true);
+  wt += __builtin_amdgcn_update_dpp(0u, wt, 0x114, 0xF, 0xF, true);
+  wt += __builtin_amdgcn_update_dpp(0u, wt, 0x118, 0xF, 0xF, true);
+  static_assert(WAVES <= 16, "wave totals scanned within one row of lanes");
+  const uint32_t wv = uni(wave);
+  uint32_t start = incl - s + (wv ? __builtin_amdgcn_readlane(wt, wv - 1u) : 0u);
+  uint32_t st[BPT];
+  bool big = false;
+#pragma unroll
+  for (uint32_t i = 0; i < BPT; ++i) {
+    st[i] = start;
+    const uint32_t end = start + c[i];
+    if (start < k && end >= k) {  // the pivot bin: it holds rank k - 1 (ranks from 0, best first)
+      sc.pub[0] = lo + BPT - 1u - i;
+      sc.pub[1] = start;
+      sc.pub[2] = c[i];
+      big = big || c[i] > kListCap;
+    } else if (end < k) {
+      big = big || c[i] > kSortedBinCap;
+    }
+    start = end;
+  }
+#pragma unroll
+  for (uint32_t g = 0; g < BPT / 2; ++g)
+    *reinterpret_cast<uint2*>(hs + lo + 2u * g) = make_uint2(st[BPT - 1u - 2u * g], st[BPT - 2u - 2u * g]);
+  if (big) sc.big = 1;
+  lds_sync();
+  if (sc.big) {
+    // Hand this pass to the general compaction as its first value pass: the counts in its
+    // bin layout (every read of h was before the last barrier but one), the other histogram
+    // zero, the appended entries as keys, and each wave's largest key.
+#pragma unroll
+    for (uint32_t i = 0; i < BPT; ++i) {
+      h[hslot(lo + BPT - 1u - i)] = c[i];
+      hs[lo + i] = 0;
+    }
+    uint32_t mx = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kFinalPer; ++j) {
+      const uint32_t e = tid + j * NT;
+      if (j * NT < n && e < n) {
+        mx = max(mx, key[j]);
+        if (RAW && e < sg.n1) sg.k1[e] = key[j];
+      }
+    }
+    mx = wave_max32(mx);
+    if (lane == 0) sc.red[wave] = mx;
+    lds_sync();
+    return false;
+  }
+  const uint32_t pbin = sc.pub[0], above = sc.pub[1], pcnt = sc.pub[2];
+
+  // entries above the pivot bin to their bins' slots, the pivot bin's to the list
+#pragma unroll
+  for (uint32_t j = 0; j < kFinalPer; ++j) {
+    if (j * NT < n && tid + j * NT < n) {
+      if (bin[j] > pbin) {
+        cbuf[hs[bin[j]] + arr[j]] = comp_of(key[j], id[j]);
+      } else if (bin[j] == pbin) {
+        sc.lkey[arr[j]] = key[j];
+        sc.lidx[arr[j]] = id[j];
+      }
+    }
+  }
+  lds_sync();
+
+  // an entry above the pivot bin: its bin's first slot plus the bin's entries that rank above it
+#pragma unroll
+  for (uint32_t j = 0; j < kFinalPer; ++j) {
+    if (j * NT < n && tid + j * NT < n && bin[j] > pbin) {
+      const uint32_t s0 = hs[bin[j]], end = s0 + h[bin[j]];
+      const uint64_t me = comp_of(key[j], id[j]);
+      uint32_t r = 0;
+      for (uint32_t m = s0; m < end; m += 4u) {
+        // four at a time: the reads past the bin's end (masked out) stay inside cbuf's k + 3
+        // slots, since the bin ends at most at slot k - 1
+        uint64_t o[4];
+#pragma unroll
+        for (uint32_t u = 0; u < 4; ++u) o[u] = cbuf[m + u];
+#pragma unroll
+        for (uint32_t u = 0; u < 4; ++u) r += (m + u < end && o[u] > me) ? 1u : 0u;
+      }
+      store_out<DT>(so.vals, so.idx, so.pairs, so.row * k + s0 + r, me);
+    }
+  }
+  // the pivot bin's list: the k - above best of it follow the entries above it
+  if (wave == WAVES - 1) {
+    const bool have = lane < pcnt;
+    const uint32_t lk = have ? sc.lkey[lane] : 0u, li = have ? sc.lidx[lane] : kSentinelIdx;
+    const uint64_t mine = comp_of(lk, li);
+    uint32_t rank = 0;
+    for (uint32_t m = 0; m < pcnt; ++m) rank += readlane64(mine, m) > mine ? 1u : 0u;
+    const uint32_t need = k - above;
+    if (have && rank < need) store_out<DT>(so.vals, so.idx, so.pairs, so.row * k + above + rank, mine);
+    const uint64_t piv = ballot(have && rank == need - 1u);
+    const uint32_t pl = piv ? static_cast<uint32_t>(__builtin_ctzll(piv)) : 0u;
+    if (lane == 0) {
+      sc.pub[3] = __builtin_amdgcn_readlane(lk, pl);
+      sc.pub[4] = __builtin_amdgcn_readlane(li, pl);
+      ++sc.st_p;
+    }
+  }
+  lds_sync();
+  tkey = sc.pub[3];
+  tidx = sc.pub[4];
+  return true;
+}
+
 template <int WAVES, int DT, bool RAW>
 __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, bool fin, bool have_t,
                         uint32_t key_hi, uint32_t ilo, uint32_t ihi, Scalars& sc, uint32_t* hist2, uint32_t& hpar,
                         uint32_t& tkey, uint32_t& tidx, uint32_t& maxkey, uint32_t vlo_key, uint32_t vhi_key,
-                        bool vok, const OutSpec* so, bool& sorted, uint32_t* clear) {
+                        bool vok, const OutSpec* so, bool& sorted, uint32_t* clear, uint64_t* cbuf) {
   constexpr uint32_t NT = WAVES * 64;
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t n = sg.n0 + sg.n1;
@@ -780,6 +980,13 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
   pv.k = k;
   pv.vbin_p = 0;
   pv.vm = vok && vbins_of<DT>(vlo_key, vhi_key, pv.vb);
+  bool one_pass = fin && so && pv.vm && n <= kFinalPer * NT;
+  if (one_pass &&
+      final_sorted<WAVES, DT, RAW>(sg, k, *so, pv.vb, hist2 + kBins * (hpar & 1u), hist2 + kBins * ((hpar + 1u) & 1u),
+                                   cbuf, sc, tkey, tidx)) {
+    sorted = true;
+    return;
+  }
   bool open = have_t, first = true;
   uint32_t need = k, above_total = 0, cnt = 0, seen_max = 0;
   for (;;) {
@@ -787,18 +994,21 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
     const uint32_t shift = bl > kLogBins ? bl - kLogBins : 0u;
     uint32_t* h = hist2 + kBins * (hpar & 1u);
     uint32_t* hz = hist2 + kBins * ((hpar + 1u) & 1u);
-    // the other histogram was last read by the previous scan, before the last barrier
-    for (uint32_t b = 4u * tid; b < kBins; b += 4u * NT) *reinterpret_cast<uint4*>(hz + b) = make_uint4(0, 0, 0, 0);
-    if (!pv.tie) {
-      uint32_t mx = hist_all<DT>(sg, tid, NT, pv.plo, pv.phi, open, shift, h, RAW && first, pv.vm, pv.vb);
-      if (first) {
-        mx = wave_max32(mx);
-        if (lane == 0) sc.red[wave] = mx;
+    if (!one_pass) {  // else the one-pass form already made this (first) pass
+      // the other histogram was last read by the previous scan, before the last barrier
+      for (uint32_t b = 4u * tid; b < kBins; b += 4u * NT) *reinterpret_cast<uint4*>(hz + b) = make_uint4(0, 0, 0, 0);
+      if (!pv.tie) {
+        uint32_t mx = hist_all<DT>(sg, tid, NT, pv.plo, pv.phi, open, shift, h, RAW && first, pv.vm, pv.vb);
+        if (first) {
+          mx = wave_max32(mx);
+          if (lane == 0) sc.red[wave] = mx;
+        }
+      } else {
+        ties_all(sg, tid, NT, pv.pkey, pv.iplo, pv.iphi, shift, h);
       }
-    } else {
-      ties_all(sg, tid, NT, pv.pkey, pv.iplo, pv.iphi, shift, h);
+      lds_sync();
     }
-    lds_sync();
+    one_pass = false;
     ++hpar;
     if (tid == 0) ++sc.st_p;
     if (wave == 0) {
@@ -1516,7 +1726,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     }
     compact<WAVES, DT, !MERGE>(sg, to_a ? L.ck : L.bk, to_a ? L.ci : L.bi, k, fin, nsurv != 0, key_hi, ilo, ihi, sc,
                                L.hist, hpar, t_key, t_idx, maxkey, vlo, vhi, vok, fin ? fso : nullptr, sorted,
-                               fin ? nullptr : &sc.len);
+                               fin ? nullptr : &sc.len, reinterpret_cast<uint64_t*>(L.ck));
     sur_a = to_a;
   };
 
