@@ -313,7 +313,7 @@ struct BlockOrder {
   uint32_t key[4];
   uint32_t half, mask, m;
 
-  __device__ void init(uint64_t seed, uint32_t row, uint32_t slice, uint32_t m_) {
+  __device__ __forceinline__ void init(uint64_t seed, uint32_t row, uint32_t slice, uint32_t m_) {
     constexpr uint64_t G = 0x9E3779B97F4A7C15ull;
     // lane l derives key l & 3 in vector registers; the four keys are then read back
     const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
@@ -1610,6 +1610,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   constexpr uint32_t key_hi = DT == DS_BF16 ? 0xFFFFu : 0xFFFFFFFFu;  // largest possible key
   static_assert(D >= 2 && D <= 4, "two to four buffers");
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t wave_s = uni(wave);  // the same, known to the compiler as uniform
   const uint32_t m = (len + B - 1) / B;
 
   // Block order: the permutation `ord` is over groups of 2^gshift consecutive blocks (ng of
@@ -1906,6 +1907,71 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
       }
       const bool strict = idx_base + blk_lo > f_idx;
       const uint32_t thr = strict ? thr_s : thr_n;
+      // The hits of the block, appended raw. ONE: a positive threshold (mode 1), compiled on
+      // its own so that the hit masks are never merged across the modes' branches.
+      auto filter_hits = [&](auto one) {
+        constexpr bool ONE = decltype(one)::value;
+        // a score that never passes this mode's compare (for the stream's tail)
+        constexpr uint32_t NEVER = ONE ? 0x80000000u : 0xFFFFFFFFu;
+        uint32_t kmn = ~0u, kmx = 0;  // key range of the hits while there is no threshold
+        // One reservation per chunk: only that chunk's hit masks are live. Hits are stored raw;
+        // a lane without a hit in an element that some lane of the wave hit writes its dummy
+        // slot instead, so the stores need no exec-mask changes.
+#pragma unroll
+        for (uint32_t t = 0; t < CPW; ++t) {
+          const uint32_t cfirst = blk_lo + (wave_s + t * WAVES) * CHUNK;  // the chunk's first element
+          const uint32_t first = cfirst + lane * VEC;
+          if (cfirst + CHUNK > len_opaque) {  // the stream's tail chunk, or a chunk past its end
+#pragma unroll
+            for (uint32_t e = 0; e < VEC; ++e) s[t][e] = first + e < len_opaque ? s[t][e] : NEVER;
+          }
+          // the hit masks are computed once, on straight-line code (no mask merging)
+          bool h[VEC];
+#pragma unroll
+          for (uint32_t e = 0; e < VEC; ++e) {
+            if constexpr (ONE)
+              h[e] = static_cast<int32_t>(s[t][e]) > static_cast<int32_t>(thr);
+            else  // mode 2, or mode 0 (thr ~0: every non-NaN score passes)
+              h[e] = s[t][e] < thr;
+          }
+          if (!ONE && mode == 0) {
+#pragma unroll
+            for (uint32_t e = 0; e < VEC; ++e) {
+              const uint32_t key = key_of_score<DT>(s[t][e]);
+              kmn = h[e] ? min(kmn, key) : kmn;
+              kmx = h[e] ? max(kmx, key) : kmx;
+            }
+          }
+          // positions by vector arithmetic only (the CU's waves share one scalar unit): the
+          // lane's hit count, its exclusive prefix over the wave, one reservation; every
+          // element then goes to its slot or, if it is no hit, to the lane's dummy slot
+          uint32_t cnt = 0;
+#pragma unroll
+          for (uint32_t e = 0; e < VEC; ++e) cnt += h[e] ? 1u : 0u;
+          const uint32_t incl = wave_incl_scan(cnt);
+          const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+          if (tot) {
+            uint32_t pos = app0 + reserve(tot, seen) + incl - cnt;
+            reserved = true;
+            const uint32_t j0 = idx_base + first;
+#pragma unroll
+            for (uint32_t e = 0; e < VEC; ++e) {
+              const uint32_t q = h[e] ? pos : L.dummy + lane;
+              L.ck[q] = s[t][e];
+              L.ci[q] = j0 + e;
+              pos += h[e] ? 1u : 0u;
+            }
+          }
+        }
+        if (!ONE && mode == 0) {
+          rmin_w = min(rmin_w, wave_min32(kmn));
+          rmax_w = max(rmax_w, wave_max32(kmx));
+          if (lane == 0) {
+            sc.rmin[wave] = rmin_w;
+            sc.rmax[wave] = rmax_w;
+          }
+        }
+      };
       if (mode == 0 && blk_lo + B <= len) {
         // accept everything: each wave stores its chunks (raw) contiguously
         const uint32_t pos = app0 + reserve(SHARE, seen);
@@ -1949,64 +2015,10 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
             }
           }
         }
+      } else if (mode == 1) {
+        filter_hits(std::true_type{});
       } else {
-        uint32_t kmn = ~0u, kmx = 0;  // key range of the hits while there is no threshold
-        // one reservation per chunk: only that chunk's hit masks are live. Hits are stored raw;
-        // a lane without a hit in an element that some lane of the wave hit writes its dummy
-        // slot instead, so the stores need no exec-mask changes.
-#pragma unroll
-        for (uint32_t t = 0; t < CPW; ++t) {
-          const uint32_t cfirst = blk_lo + (wave + t * WAVES) * CHUNK;  // the chunk's first element
-          const uint32_t first = cfirst + lane * VEC;
-          bool h[VEC];
-          if (mode == 1) {
-#pragma unroll
-            for (uint32_t e = 0; e < VEC; ++e) h[e] = static_cast<int32_t>(s[t][e]) > static_cast<int32_t>(thr);
-          } else {  // mode 2; without a threshold thr is ~0 and every (non-NaN) score passes
-#pragma unroll
-            for (uint32_t e = 0; e < VEC; ++e) h[e] = s[t][e] < thr;
-          }
-          if (cfirst + CHUNK > len_opaque) {  // the stream's tail chunk, or a chunk past its end
-#pragma unroll
-            for (uint32_t e = 0; e < VEC; ++e) h[e] = h[e] && first + e < len_opaque;
-          }
-          if (mode == 0) {
-#pragma unroll
-            for (uint32_t e = 0; e < VEC; ++e) {
-              const uint32_t key = key_of_score<DT>(s[t][e]);
-              kmn = h[e] ? min(kmn, key) : kmn;
-              kmx = h[e] ? max(kmx, key) : kmx;
-            }
-          }
-          // positions by vector arithmetic only (the CU's waves share one scalar unit): the
-          // lane's hit count, its exclusive prefix over the wave, one reservation; every
-          // element then goes to its slot or, if it is no hit, to the lane's dummy slot
-          uint32_t cnt = 0;
-#pragma unroll
-          for (uint32_t e = 0; e < VEC; ++e) cnt += h[e] ? 1u : 0u;
-          const uint32_t incl = wave_incl_scan(cnt);
-          const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
-          if (tot) {
-            uint32_t pos = app0 + reserve(tot, seen) + incl - cnt;
-            reserved = true;
-            const uint32_t j0 = idx_base + first;
-#pragma unroll
-            for (uint32_t e = 0; e < VEC; ++e) {
-              const uint32_t q = h[e] ? pos : L.dummy + lane;
-              L.ck[q] = s[t][e];
-              L.ci[q] = j0 + e;
-              pos += h[e] ? 1u : 0u;
-            }
-          }
-        }
-        if (mode == 0) {
-          rmin_w = min(rmin_w, wave_min32(kmn));
-          rmax_w = max(rmax_w, wave_max32(kmx));
-          if (lane == 0) {
-            sc.rmin[wave] = rmin_w;
-            sc.rmax[wave] = rmax_w;
-          }
-        }
+        filter_hits(std::false_type{});
       }
     } else {
       if (presample && i == 0 && blk_lo + B <= len) {
