@@ -87,6 +87,14 @@ __device__ __forceinline__ __attribute__((address_space(3))) T* lds_ptr(T* p) {
   return (__attribute__((address_space(3))) T*)p;
 }
 
+// LDS byte addresses: a word's address, and the word at an address.
+__device__ __forceinline__ uint32_t lds_addr(const uint32_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(const_cast<uint32_t*>(p))));
+}
+__device__ __forceinline__ __attribute__((address_space(3))) uint32_t* lds_at(uint32_t a) {
+  return reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(a));
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 __device__ __forceinline__ uint32_t mbcnt(uint64_t m, uint32_t base) {
@@ -1611,6 +1619,10 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   static_assert(D >= 2 && D <= 4, "two to four buffers");
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t wave_s = uni(wave);  // the same, known to the compiler as uniform
+  // LDS byte addresses of the append buffer, of this lane's dummy slot, and the distance from
+  // a key slot to its index slot
+  const uint32_t ck_addr = lds_addr(L.ck), dummy_addr = ck_addr + 4u * (L.dummy + lane);
+  const uint32_t ci_off = lds_addr(L.ci) - ck_addr;
   const uint32_t m = (len + B - 1) / B;
 
   // Block order: the permutation `ord` is over groups of 2^gshift consecutive blocks (ng of
@@ -1945,21 +1957,26 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
           // positions by vector arithmetic only (the CU's waves share one scalar unit): the
           // lane's hit count, its exclusive prefix over the wave, one reservation; every
           // element then goes to its slot or, if it is no hit, to the lane's dummy slot
-          uint32_t cnt = 0;
+          uint32_t hb[VEC], cnt = 0;  // hb: 1 for a hit
 #pragma unroll
-          for (uint32_t e = 0; e < VEC; ++e) cnt += h[e] ? 1u : 0u;
+          for (uint32_t e = 0; e < VEC; ++e) {
+            hb[e] = h[e] ? 1u : 0u;
+            cnt += hb[e];
+          }
           const uint32_t incl = wave_incl_scan(cnt);
           const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
           if (tot) {
-            uint32_t pos = app0 + reserve(tot, seen) + incl - cnt;
+            // byte addresses: the key slot (the next free one, or the dummy), the index slot
+            // at a fixed distance from it
+            uint32_t pa = ck_addr + 4u * (app0 + reserve(tot, seen) + incl - cnt);
             reserved = true;
             const uint32_t j0 = idx_base + first;
 #pragma unroll
             for (uint32_t e = 0; e < VEC; ++e) {
-              const uint32_t q = h[e] ? pos : L.dummy + lane;
-              L.ck[q] = s[t][e];
-              L.ci[q] = j0 + e;
-              pos += h[e] ? 1u : 0u;
+              const uint32_t a = h[e] ? pa : dummy_addr;
+              *lds_at(a) = s[t][e];
+              *lds_at(a + ci_off) = j0 + e;
+              pa += 4u * hb[e];
             }
           }
         }
