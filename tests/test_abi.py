@@ -196,7 +196,8 @@ def test_schedule_plan_field():
         assert p["schedule"] == want, (n, k, p)
         assert ts.ds_topk_plan(4, n, k, ts.BF16, dict(base, schedule=ts.SCHEDULE_FREE))["schedule"] == \
             ts.SCHEDULE_FREE
-    assert ts.ds_topk_plan(4, 131072, 512, ts.BF16, {"slices": 4})["schedule"] == ts.SCHEDULE_FREE  # the indexer
+    ix = ts.ds_topk_plan(4, 131072, 512, ts.BF16, {"slices": 4})  # the indexer: B2 near sqrt(k (k + B))
+    assert (ix["block"], ix["slack"], ix["schedule"]) == (8192, 2048, ts.SCHEDULE_LOCKSTEP)
     assert ts.ds_topk_plan(4, 100000, 64, ts.BF16, dict(base, schedule=ts.SCHEDULE_LOCKSTEP))["schedule"] == \
         ts.SCHEDULE_LOCKSTEP
     with pytest.raises(ts.DSError) as e:

@@ -19,7 +19,7 @@ CASES = [("bf16 63x131072 k4096 (near the array size)", lambda: gen.rows_family(
           4096),
          ("indexer rows 48x131072 k512", lambda: gen.WORKLOADS["c2_indexer"].make(rows=48), 512),
          ("fp32 3x300000 k64 ties", lambda: gen.rows_family("ties", gen.FP32, 82, 3, 300000), 64),
-         ("bf16 5x100000 k100", lambda: gen.rows_family("normal", gen.BF16, 81, 5, 100000), 100)]
+         ("bf16 2x140000 k100", lambda: gen.rows_family("normal", gen.BF16, 81, 2, 140000), 100)]
 
 
 def _dt(x):
@@ -59,7 +59,7 @@ def test_noalloc_graph_replays_with_calls_between():
     """A captured pair of calls (large, then smaller) replays to the eager results, with
     eager calls on another input overwriting the array between replays."""
     import torch
-    xs = [gen.WORKLOADS["c2_indexer"].make(), gen.rows_family("normal", gen.BF16, 84, 5, 100000)]
+    xs = [gen.WORKLOADS["c2_indexer"].make(), gen.rows_family("normal", gen.BF16, 84, 2, 140000)]
     ks = [512, 100]
     xds = [to_device(x) for x in xs]
     other = to_device(gen.rows_family("normal", gen.BF16, 85, 32, 131072))

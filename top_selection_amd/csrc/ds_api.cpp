@@ -22,10 +22,10 @@ constexpr int64_t kMaxSliceBytes = 0x7FFFFF00;  // buffer offsets are 31-bit
 constexpr int kChunkBf16 = 512, kChunkFp32 = 256;
 constexpr int kMergeBlock = ds::kMergeShape.waves * ds::kMergeShape.cpw * 128;
 // B2 when not forced: the largest of these (and at least k) that fits in LDS and is at most
-// twice sqrt(k (k + B)). The design note's expected-work bound (1 + k/B2)(k + B + B2) H_m is
-// smallest at B2 = sqrt(k (k + B)); on MI355X a compaction costs more, relative to the appends
-// it saves, than the bound counts, and twice that measured best (4096 at k = 512, B = 8192;
-// 1024 at k = 32).
+// 1.5 sqrt(k (k + B)). The design note's expected-work bound (1 + k/B2)(k + B + B2) H_m is
+// smallest at B2 = sqrt(k (k + B)); measured on MI355X, the power of two at or just above it
+// is best (2048 at k = 512, B = 8192: long rows 56 -> 49 us per call, sampler 41 -> 40 us,
+// indexer unchanged; 1024 at k = 32, B = 16384).
 constexpr int kDefaultSlacks[] = {4096, 2048, 1024, 512, 256};
 // default select shapes (indices into kSelectShapes), best first
 // B = 16384 comes first but only takes its own bound-derived B2 (small k: fewer block
@@ -125,7 +125,7 @@ int make_plan(int64_t rows, int64_t n, int k, int dtype, const ds_config* cfg, i
   size_t lds = 0;
   auto fit = [&](int s, bool strict = false) -> bool {
     const int b = kSelectShapes[s].waves * kSelectShapes[s].cpw * chunk;
-    const double cap = 2.0 * std::sqrt(static_cast<double>(k) * (static_cast<double>(k) + b));
+    const double cap = 1.5 * std::sqrt(static_cast<double>(k) * (static_cast<double>(k) + b));
     bool tried = false;
     for (int want : kDefaultSlacks) {
       if (!c.slack && want > cap && want != kDefaultSlacks[sizeof(kDefaultSlacks) / sizeof(int) - 1]) continue;

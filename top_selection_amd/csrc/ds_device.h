@@ -580,14 +580,42 @@ __device__ __forceinline__ uint32_t hist_all(const Segs& sg, uint32_t tid, uint3
                            key_of_score<DT>(kk[u].w));
         *lds_ptr(reinterpret_cast<u32x4*>(kp[u])) = u32x4{kk[u].x, kk[u].y, kk[u].z, kk[u].w};
       }
-      if (vm) {  // value bins spread entries: one atomic each
+      if (vm) {
+        // value bins spread entries: one atomic each, except where most lanes' groups fall
+        // whole into one bin (a sorted stretch of the buffer, whose atomics would all hit a
+        // few addresses): then each run of lanes with the same whole-group bin adds its
+        // entries with one atomic, by the run's first lane
+        uint32_t b[4];
 #pragma unroll
         for (uint32_t q = 0; q < 4; ++q) {
           const uint32_t key = u4get(kk[u], q);
-          if (q < nv[u]) {
-            mx = max(mx, key);
-            atomicAdd(&h[hslot(vbin<DT>(key, vb))], 1u);
+          b[q] = vbin<DT>(key, vb);
+          mx = q < nv[u] ? max(mx, key) : mx;
+        }
+        const bool same = nv[u] == 4u && b[0] == b[1] && b[1] == b[2] && b[2] == b[3];
+        const uint32_t lane = tid & 63u;
+        if (popc(ballot(same)) >= 16u) {
+          const uint32_t rk = same ? b[0] : (0x80000000u | lane);  // a lane of its own otherwise
+          const uint32_t prev = static_cast<uint32_t>(
+              __builtin_amdgcn_ds_bpermute(static_cast<int>(((lane - 1u) & 63u) << 2), static_cast<int>(rk)));
+          const bool first = lane == 0 || rk != prev;
+          // runs end at the next run's first lane or at the first inactive lane
+          const uint64_t stop = ballot(first) | ~ballot(true);
+          if (same) {
+            if (first) {
+              const uint64_t rest = lane == 63u ? 0ull : stop >> (lane + 1u);
+              const uint32_t len = rest ? static_cast<uint32_t>(__builtin_ctzll(rest)) + 1u : 64u - lane;
+              atomicAdd(&h[hslot(b[0])], 4u * len);
+            }
+          } else {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q)
+              if (q < nv[u]) atomicAdd(&h[hslot(b[q])], 1u);
           }
+        } else {
+#pragma unroll
+          for (uint32_t q = 0; q < 4; ++q)
+            if (q < nv[u]) atomicAdd(&h[hslot(b[q])], 1u);
         }
       } else {  // key bins: runs of equal keys are common (ties), one atomic per run
         uint32_t bin[4], cnt[4];
