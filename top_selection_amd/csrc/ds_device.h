@@ -513,8 +513,9 @@ __device__ __forceinline__ void scan_select(const uint32_t* h, uint32_t need, ui
 // With so (final call only) and a single value pass, the survivors are written sorted to
 // *so instead (sorted = true): a counting sort over the value bins (see below). A final call
 // with at most kFinalPer entries per thread takes the one-pass form of it (final_sorted),
-// which may use cbuf (room for k + 3 composites) and falls back to the above when a bin is
-// too full.
+// which may use cbuf (room for round4(k) + 4 composites and k words after them: the append
+// buffer, whose two arrays hold 2 (round4(k) + B + B2) words at least, with B + B2 >= k)
+// and falls back to the above when a bin is too full.
 //
 // Barriers: two per histogram pass (after the counts; after the scan result is published),
 // one after the scatter and one after the list is ranked.
@@ -812,8 +813,9 @@ __device__ __forceinline__ uint32_t vbin_of_value(float v, const VBins& vb) {
 // appended entries converted to keys in place, the waves' largest keys in sc.red). The
 // histograms here are plain (bin b at index b) until then; on success both are left dirty
 // (this is a stream's last compaction).
-// h is the current histogram (zero on entry), hs the other one; cbuf has room for k
-// composites and may overlap the entries (they are all in registers before it is written).
+// h is the current histogram (zero on entry), hs the other one; cbuf has room for k + 3
+// composites and then k bin numbers (cbin, from slot round4(k) + 4 of cbuf) and may overlap the
+// entries (they are all in registers before it is written).
 template <int WAVES, int DT, bool RAW>
 __device__ __forceinline__ bool final_sorted(const Segs& sg, uint32_t k, const OutSpec so, const VBins& vb,
                                              uint32_t* h, uint32_t* hs, uint64_t* cbuf, Scalars& sc,
@@ -917,12 +919,16 @@ __device__ __forceinline__ bool final_sorted(const Segs& sg, uint32_t k, const O
   }
   const uint32_t pbin = sc.pub[0], above = sc.pub[1], pcnt = sc.pub[2];
 
-  // entries above the pivot bin to their bins' slots, the pivot bin's to the list
+  // entries above the pivot bin to their bins' slots (with their bins, in cbin), the pivot
+  // bin's to the list
+  uint32_t* const cbin = reinterpret_cast<uint32_t*>(cbuf + round4(k) + 4u);
 #pragma unroll
   for (uint32_t j = 0; j < kFinalPer; ++j) {
     if (j * NT < n && tid + j * NT < n) {
       if (bin[j] > pbin) {
-        cbuf[hs[bin[j]] + arr[j]] = comp_of(key[j], id[j]);
+        const uint32_t d = hs[bin[j]] + arr[j];
+        cbuf[d] = comp_of(key[j], id[j]);
+        cbin[d] = bin[j];
       } else if (bin[j] == pbin) {
         sc.lkey[arr[j]] = key[j];
         sc.lidx[arr[j]] = id[j];
@@ -931,24 +937,24 @@ __device__ __forceinline__ bool final_sorted(const Segs& sg, uint32_t k, const O
   }
   lds_sync();
 
-  // an entry above the pivot bin: its bin's first slot plus the bin's entries that rank above it
+  // the entry at slot p: its bin's first slot plus the bin's entries that rank above it. Slots
+  // go to threads in order, so a wave's lanes share a few neighbouring bins and only the waves
+  // that hold the crowded bins loop long.
+  for (uint32_t p = tid; p < above; p += NT) {
+    const uint64_t me = cbuf[p];
+    const uint32_t b = cbin[p];
+    const uint32_t s0 = hs[b], end = s0 + h[b];
+    uint32_t r = 0;
+    for (uint32_t m = s0; m < end; m += 4u) {
+      // four at a time: the reads past the bin's end (masked out) stay inside cbuf's k + 3
+      // slots, since the bin ends at most at slot k - 1
+      uint64_t o[4];
 #pragma unroll
-  for (uint32_t j = 0; j < kFinalPer; ++j) {
-    if (j * NT < n && tid + j * NT < n && bin[j] > pbin) {
-      const uint32_t s0 = hs[bin[j]], end = s0 + h[bin[j]];
-      const uint64_t me = comp_of(key[j], id[j]);
-      uint32_t r = 0;
-      for (uint32_t m = s0; m < end; m += 4u) {
-        // four at a time: the reads past the bin's end (masked out) stay inside cbuf's k + 3
-        // slots, since the bin ends at most at slot k - 1
-        uint64_t o[4];
+      for (uint32_t u = 0; u < 4; ++u) o[u] = cbuf[m + u];
 #pragma unroll
-        for (uint32_t u = 0; u < 4; ++u) o[u] = cbuf[m + u];
-#pragma unroll
-        for (uint32_t u = 0; u < 4; ++u) r += (m + u < end && o[u] > me) ? 1u : 0u;
-      }
-      store_out<DT>(so.vals, so.idx, so.pairs, so.row * k + s0 + r, me);
+      for (uint32_t u = 0; u < 4; ++u) r += (m + u < end && o[u] > me) ? 1u : 0u;
     }
+    store_out<DT>(so.vals, so.idx, so.pairs, so.row * k + s0 + r, me);
   }
   // the pivot bin's list: the k - above best of it follow the entries above it
   if (wave == WAVES - 1) {
@@ -1665,9 +1671,14 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
     const uint32_t b = (ord.at(i >> gshift) << gshift) | (i & ((1u << gshift) - 1u));
     return b < m ? b : m;
   };
+  // (the table's first 64 entries are also held in a vector register, lane l entry l, once
+  // it is built: a lookup there is a lane read, with no LDS access queued behind the appends)
+  uint32_t ordv = 0;
   auto bid_of = [&](uint32_t i) -> uint32_t {
     if (i >= m_iter) return m;
-    const uint32_t b = ((tab ? uni(L.ordt[i >> gshift]) : ord.at(i >> gshift)) << gshift) | (i & ((1u << gshift) - 1u));
+    const uint32_t g = i >> gshift;
+    const uint32_t o = !tab ? ord.at(g) : (g < 64u ? __builtin_amdgcn_readlane(ordv, g) : uni(L.ordt[g]));
+    const uint32_t b = (o << gshift) | (i & ((1u << gshift) - 1u));
     return b < m ? b : m;
   };
 
@@ -1728,6 +1739,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   if (tab)
     for (uint32_t i = tid; i < ng; i += NT) L.ordt[i] = ord.at(i);
   lds_sync();
+  if (tab) ordv = L.ordt[lane];  // entries past ng are never read back
   if (share && (sc.shr[0] | sc.shr[1]) != 0) {
     // filter with the row's threshold from the start (no own threshold yet)
     f_idx = ~sc.shr[0];
