@@ -67,15 +67,27 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_
 // the units are dealt to the eight XCDs (workgroup i runs on XCD i mod 8) so that all
 // workgroups of a unit run on one XCD and share its L2; units past the last multiple of 8
 // follow in plain order. Returns the unit and the workgroup's index within it.
+// a / d and a % d for a uniform d >= 1: a shift and a mask when d is a power of two (the usual
+// slice counts), else the division
+__device__ __forceinline__ void divmod_uniform(uint32_t a, uint32_t d, uint32_t& q, uint32_t& r) {
+  if ((d & (d - 1u)) == 0u) {
+    q = a >> __builtin_ctz(d);
+    r = a & (d - 1u);
+  } else {
+    q = a / d;
+    r = a - q * d;
+  }
+}
+
 __device__ __forceinline__ void xcd_unit(uint32_t wg, uint32_t per, uint32_t units, uint32_t& unit, uint32_t& sub) {
   const uint32_t dealt = (units & ~7u) * per;
+  uint32_t q;
   if (wg < dealt) {
-    const uint32_t j = wg >> 3;
-    unit = (wg & 7u) + 8u * (j / per);
-    sub = j % per;
+    divmod_uniform(wg >> 3, per, q, sub);
+    unit = (wg & 7u) + 8u * q;
   } else {
-    unit = (units & ~7u) + (wg - dealt) / per;
-    sub = (wg - dealt) % per;
+    divmod_uniform(wg - dealt, per, q, sub);
+    unit = (units & ~7u) + q;
   }
 }
 
@@ -1664,7 +1676,8 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   // past the last block (the last group's padding, or steps past the end) read nothing. The
   // group order is a table for up to kOrdCap groups, computed on the fly beyond.
   const uint32_t ng = (m + (1u << gshift) - 1u) >> gshift, m_iter = ng << gshift;
-  const bool tab = ng <= kOrdCap;
+  // (a stream of at most D blocks reads only the first D ids, computed directly: no table)
+  const bool tab = ng <= kOrdCap && m_iter > static_cast<uint32_t>(D);
   // block id of the i-th block read, from the permutation itself (direct) or its table
   auto bid_direct = [&](uint32_t i) -> uint32_t {
     if (i >= m_iter) return m;
@@ -2193,9 +2206,14 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
 
 // --------------------------------------------------------------------------- select kernel
 // EXT: the instantiation that serves ragged rows, the warm-up window and the shared row
-// threshold; the plain one (EXT = false) has none of their code.
+// threshold; the plain one (EXT = false) has none of their code. The parameters the first
+// loads depend on come as scalars ahead of the rest, so that the hardware can preload them
+// into scalar registers at wave launch (the build asks for 15 dwords) instead of the waves
+// waiting on a load of the argument block.
 template <int DT, int WAVES, int CPW, bool STATS, bool EXT>
-__global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
+__global__ __launch_bounds__(WAVES * 64) void select_kernel(const uint8_t* px, int64_t pstride, int64_t pn, int64_t pslice_len,
+                                                                  uint64_t pseed, const int32_t* plens, int32_t pslices,
+                                                                  int32_t pgshift, int32_t prows, SelectParams p) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t EB = DT == DS_BF16 ? 2 : 4;
   constexpr uint32_t B = WAVES * CPW * 64 * (16 / EB);
@@ -2206,17 +2224,17 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   const uint32_t tid = threadIdx.x;
   // a row's slices run on one XCD, where the merge of their lists reads them from L2
   uint32_t row, slice;
-  xcd_unit(blockIdx.x, static_cast<uint32_t>(p.slices), gridDim.x / static_cast<uint32_t>(p.slices), row, slice);
-  const uint32_t slice_lo = slice * static_cast<uint32_t>(p.slice_len);
-  int64_t n_row = p.n;  // this row's length
+  xcd_unit(blockIdx.x, static_cast<uint32_t>(pslices), static_cast<uint32_t>(prows), row, slice);
+  const uint32_t slice_lo = slice * static_cast<uint32_t>(pslice_len);
+  int64_t n_row = pn;  // this row's length
   if constexpr (EXT) {
-    if (p.lens) {
-      const int64_t l = p.lens[row];
+    if (plens) {
+      const int64_t l = plens[row];
       n_row = l < 0 ? 0 : (l < n_row ? l : n_row);
     }
   }
   const int64_t rest = n_row - static_cast<int64_t>(slice_lo);
-  const uint32_t len = rest <= 0 ? 0u : static_cast<uint32_t>(min(p.slice_len, rest));
+  const uint32_t len = rest <= 0 ? 0u : static_cast<uint32_t>(min(pslice_len, rest));
   const uint32_t m = (len + B - 1) / B;
   const uint32_t k = static_cast<uint32_t>(p.k);
   const uint32_t B2 = static_cast<uint32_t>(p.slack);
@@ -2226,7 +2244,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   if (EXT && len == 0) {
     // a slice past its row's end (ragged rows): its k entries are all padding, which ranks
     // below every element (the row's outputs past its length read index -1)
-    if (p.slices == 1) {
+    if (pslices == 1) {
       for (uint32_t i = tid; i < k; i += NT) store_out<DT>(p.out_vals, p.out_idx, nullptr, static_cast<uint64_t>(row) * k + i, 0ull);
     } else {
       uint2* const dst = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + static_cast<uint64_t>(slice) * k;
@@ -2234,7 +2252,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
     }
     if constexpr (STATS) {
       if (tid == 0) {
-        ds_stats* o = p.stats + (row * static_cast<uint32_t>(p.slices) + slice);
+        ds_stats* o = p.stats + (row * static_cast<uint32_t>(pslices) + slice);
         *o = ds_stats{};
         o->monotone = 1;
         o->slice_lo = slice_lo;
@@ -2247,22 +2265,22 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
 
   const Lay L = lay_of(lds, k, B2, B);
 
-  const uint8_t* base = p.x + static_cast<uint64_t>(row) * p.row_stride_bytes + static_cast<uint64_t>(slice_lo) * EB;
+  const uint8_t* base = px + static_cast<uint64_t>(row) * pstride + static_cast<uint64_t>(slice_lo) * EB;
   // Range = the slice rounded up to whole 16-byte chunks: the hardware checks whole dwords, so
   // an exact byte count would zero the dword that holds a bf16 row's odd last element. Row
   // starts are 16-byte aligned, so the rounded range never leaves the row's last chunk.
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(base), 0, static_cast<int>((len * EB + 15u) & ~15u), kRsrcWord3);
-  const uint32_t gshift = static_cast<uint32_t>(p.group_shift);
+  const uint32_t gshift = static_cast<uint32_t>(pgshift);
   BlockOrder ord;
-  ord.init(p.seed, row, slice, (m + (1u << gshift) - 1u) >> gshift);
+  ord.init(pseed, row, slice, (m + (1u << gshift) - 1u) >> gshift);
 
   // the final compaction writes the sorted output itself when it can: the row's outputs, or
   // the slice's sorted list for the list merge
   OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
-  if (p.slices > 1)
+  if (pslices > 1)
     fso = OutSpec{nullptr, IdxOut{nullptr, 0}, p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + slice * k, 0};
-  const bool own_sort = p.slices == 1 || p.sorted_lists;
+  const bool own_sort = pslices == 1 || p.sorted_lists;
 
   BodyOut bo;
   deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), false, STATS>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
@@ -2285,7 +2303,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
     }
     lds_sync();
     if (tid == 0) {
-      ds_stats* o = p.stats + (row * static_cast<uint32_t>(p.slices) + slice);
+      ds_stats* o = p.stats + (row * static_cast<uint32_t>(pslices) + slice);
       o->appended = sc.st_a;
       o->compactions = sc.st_r;
       o->work = sc.st_w;
@@ -2305,11 +2323,11 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
 
   if (bo.sorted) {
     // done by the final compaction
-  } else if (p.slices == 1 && p.unsorted) {
+  } else if (pslices == 1 && p.unsorted) {
     // the k survivors as the final compaction left them (no sort)
     for (uint32_t i = tid; i < k; i += NT)
       store_out<DT>(p.out_vals, p.out_idx, nullptr, static_cast<uint64_t>(row) * k + i, comp_of(bo.fk[i], bo.fi[i]));
-  } else if (p.slices == 1) {
+  } else if (pslices == 1) {
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
                               p.out_vals, p.out_idx, nullptr, row);
   } else if (!p.sorted_lists) {
@@ -2324,7 +2342,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(SelectParams p) {
   if constexpr (STATS) {
     if (tid == 0) {
       const uint64_t t_end = wall_clock64();
-      ds_stats* o = p.stats + (row * static_cast<uint32_t>(p.slices) + slice);
+      ds_stats* o = p.stats + (row * static_cast<uint32_t>(pslices) + slice);
       o->t_total_ns = (t_end - t_start) * 10;
       o->t_final_ns = (t_end - sc.st_tf) * 10;
     }
