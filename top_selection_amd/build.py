@@ -31,12 +31,12 @@ FLAGS = [
 ]
 
 # (object name, source, extra flags)
-# (the select kernels' leading scalar arguments, 15 dwords, are preloaded into SGPRs)
+# (the select and list-merge kernels' leading scalar arguments are preloaded into SGPRs)
 UNITS = [(f"select_{dt}{'_stats' if st else ''}{'_ext' if ex else ''}", "ds_select.hip",
           [f"-DDS_PART_DT={d}", f"-DDS_PART_STATS={st}", f"-DDS_PART_EXT={ex}",
            "-mllvm", "-amdgpu-kernarg-preload-count=15"])
          for d, dt in ((0, "bf16"), (1, "fp32")) for st in (0, 1) for ex in (0, 1)] + [
-    ("merge", "ds_merge.hip", []),
+    ("merge", "ds_merge.hip", ["-mllvm", "-amdgpu-kernarg-preload-count=14"]),
     ("noalloc", "ds_noalloc.hip", []),
     ("api", "ds_api.cpp", [])]
 

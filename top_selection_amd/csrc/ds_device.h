@@ -2426,21 +2426,30 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
 // grid is rows x groups x ceil(group / per_wg), and workgroups past a short last group's
 // lists return at once.
 template <int DT, int WAVES, uint32_t MAXS, uint32_t EB>
-__global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(MergeParams p) {
+//
+// The parameters the first loads depend on come as scalars ahead of the rest (the grid's x
+// size gx, groups gy and rows gz among them), preloaded into scalar registers at wave launch.
+__global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(const uint2* pws, int64_t prow_entries, int64_t prow0,
+                                                                 int32_t plists, int32_t pgroup, int32_t pper,
+                                                                 int32_t pk_, int32_t ppk, int32_t gx, int32_t gy,
+                                                                 int32_t gz, MergeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  const uint32_t S = static_cast<uint32_t>(p.lists), G = static_cast<uint32_t>(p.group);
-  const uint32_t per = static_cast<uint32_t>(p.per_wg), k = static_cast<uint32_t>(p.k);
+  const uint32_t S = static_cast<uint32_t>(plists), G = static_cast<uint32_t>(pgroup);
+  const uint32_t per = static_cast<uint32_t>(pper), k = static_cast<uint32_t>(pk_);
   // grid: (workgroups per group, groups, rows of this launch); a row's workgroups run on the
   // XCD that ran its slices (row0 is a multiple of 8), whose L2 holds their lists
-  const uint32_t wpr = gridDim.x * gridDim.y;
+  const uint32_t gxu = static_cast<uint32_t>(gx), wpr = gxu * static_cast<uint32_t>(gy);
   uint32_t lrow, r;
-  xcd_unit(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), wpr, gridDim.z, lrow, r);
-  const uint64_t row = static_cast<uint64_t>(p.row0) + lrow;
-  const uint32_t g = r / gridDim.x, l0 = (r % gridDim.x) * per;
+  xcd_unit(blockIdx.x + gxu * (blockIdx.y + static_cast<uint32_t>(gy) * blockIdx.z), wpr, static_cast<uint32_t>(gz),
+           lrow, r);
+  const uint64_t row = static_cast<uint64_t>(prow0) + lrow;
+  uint32_t g, l0;
+  divmod_uniform(r, gxu, g, l0);
+  l0 *= per;
   const uint32_t first = g * G, gl = min(G, S - first);  // the group's lists
   if (l0 >= gl) return;  // the same for the whole workgroup
-  const uint32_t pk = gl == G ? static_cast<uint32_t>(p.pk) : (k + gl - 1u) / gl;  // ceil(k / gl)
-  const uint2* src = p.ws + row * p.row_entries + static_cast<uint64_t>(first) * k;
+  const uint32_t pk = gl == G ? static_cast<uint32_t>(ppk) : (k + gl - 1u) / gl;  // ceil(k / gl)
+  const uint2* src = pws + row * prow_entries + static_cast<uint64_t>(first) * k;
   uint2* pairs = p.dst ? p.dst + row * p.dst_row_entries + static_cast<uint64_t>(g) * k : nullptr;
   const uint64_t at0 = p.dst ? 0u : row * k;
   merge_lists_t<DT, WAVES, MAXS, EB>(src, gl, k, pk, reinterpret_cast<uint64_t*>(lds), p.out_vals, p.out_idx, pairs, at0,

@@ -72,7 +72,8 @@ hipError_t launch_merge_lists_t(const MergeParams& p, int64_t rows, size_t lds, 
     q.row0 = r0;
     const int64_t nr = rows - r0 < kMaxGridRows ? rows - r0 : kMaxGridRows;
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(wpg), static_cast<uint32_t>(groups), static_cast<uint32_t>(nr)),
-                       dim3(kListMergeWaves * 64), lds, stream, q);
+                       dim3(kListMergeWaves * 64), lds, stream, q.ws, q.row_entries, q.row0, q.lists, q.group, q.per_wg,
+                       q.k, q.pk, static_cast<int32_t>(wpg), static_cast<int32_t>(groups), static_cast<int32_t>(nr), q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
