@@ -1558,10 +1558,16 @@ __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint
 #pragma unroll
       for (uint32_t q = 1; q < MAXS; ++q) s[b] += (q < S && e >= q * k) ? 1u : 0u;
       c[b] = e < e_end ? lw[e] : 0ull;
-      act[b] = e < e_end && c[b] >= T;  // entries below T are searched but not placed
+      act[b] = e < e_end && c[b] >= T;  // entries below T are not placed
 #pragma unroll
       for (uint32_t q = 0; q < MAXS; ++q) pos[b][q] = 0;
     }
+    // a list's entries at or above T are its first ones, so the waves past them have nothing
+    // to place and skip the search
+    bool any = false;
+#pragma unroll
+    for (uint32_t b = 0; b < EB; ++b) any = any || act[b];
+    if (ballot(any) == 0) continue;
     for (uint32_t step = top_n; step > 0; step >>= 1) {
       uint64_t x[EB][MAXS];
 #pragma unroll
