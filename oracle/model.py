@@ -26,8 +26,8 @@ here from its specification:
   mix64(z)      = splitmix64 finaliser: z ^= z>>30; z *= 0xBF58476D1CE4E5B9;
                   z ^= z>>27; z *= 0x94D049BB133111EB; z ^= z>>31   (mod 2^64)
   lowbias32(x)  = x ^= x>>16; x *= 0x7FEB352D; x ^= x>>15; x *= 0x846CA68B; x ^= x>>16 (mod 2^32)
-  h   = mix64(seed + G*(row+1));  h = mix64(h + G*(slice+1));  G = 0x9E3779B97F4A7C15
-  key_r = low 32 bits of mix64(h + G*(r+1)), r = 0..3
+  hs  = mix64(seed)
+  key_r = low 32 bits of mix64(hs XOR (row<<33 | slice<<2 | r)), r = 0..3
   width: the smallest even b >= 2 with 2^b >= m; half = b/2; mask = 2^half - 1
   round (L, R) -> (R, L ^ (lowbias32(R ^ key_r) & mask)), four rounds, value (L<<half)|R
   pi(i) = first value < m on the cycle i -> F(i) -> F(F(i)) ... (cycle walking); m = 1 -> 0.
@@ -63,7 +63,6 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-GOLDEN = 0x9E3779B97F4A7C15
 _M64 = (1 << 64) - 1
 
 
@@ -114,9 +113,8 @@ def _lowbias32(x: np.ndarray) -> np.ndarray:
 
 
 def feistel_keys(seed: int, row: int, slice_: int) -> List[int]:
-    h = mix64(seed + GOLDEN * (row + 1))
-    h = mix64(h + GOLDEN * (slice_ + 1))
-    return [mix64(h + GOLDEN * (r + 1)) & 0xFFFFFFFF for r in range(4)]
+    hs = mix64(seed)
+    return [mix64(hs ^ ((row << 33) | (slice_ << 2) | r)) & 0xFFFFFFFF for r in range(4)]
 
 
 def _feistel_width(m: int) -> int:

@@ -380,8 +380,13 @@ def test_first_positions_follow_the_grouped_order(m, group, depth):
     order = model.grouped_order(m, group, 5, 1, 0) if group > 1 else model.feistel_order(m, 5, 1, 0)
     assert firsts == [int(b) for b in order[:len(firsts)]]
     assert len(firsts) <= depth and all(0 <= b < m for b in firsts)
-    if m >= depth * group:
-        assert len(firsts) == depth  # no padding among the first positions of a long order
+    if group > 1:
+        ng = -(-m // group)
+        drawn = model.feistel_order(ng, 5, 1, 0)[:-(-depth // group)]
+        if m % group == 0 or ng - 1 not in drawn.tolist():
+            assert len(firsts) == min(depth, m)  # padding only comes from a short last group
+    else:
+        assert len(firsts) == min(depth, m)
 
 
 # ----------------------------------------------------------------------------- warm-up window

@@ -319,6 +319,14 @@ uint2* lists_of(const Plan& pl, void* ws) {
   return ws ? reinterpret_cast<uint2*>(static_cast<uint8_t*>(ws) + pl.share_bytes) : nullptr;
 }
 
+// The block order's mixed seed: the splitmix64 finaliser of the call's seed, computed once
+// here (the kernels derive each workgroup's round keys from it).
+uint64_t mix_seed(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
 int run_select(const Plan& pl, const void* x, const int32_t* lens, int64_t rows, int64_t n, int64_t row_stride, int k,
                uint64_t seed, void* out_vals, void* out_idx, void* ws, ds_stats* stats, hipStream_t stream) {
   (void)hipGetLastError();  // clear a stale error so a launch failure is reported as ours
@@ -332,7 +340,7 @@ int run_select(const Plan& pl, const void* x, const int32_t* lens, int64_t rows,
   sp.k = k;
   sp.slack = pl.slack;
   sp.sort_cap = pl.sort_cap;
-  sp.seed = seed;
+  sp.seed = mix_seed(seed);
   sp.ws = lists_of(pl, ws);
   sp.ws_row_entries = pl.ws_row_a;
   sp.out_vals = out_vals;
@@ -365,7 +373,7 @@ int run_merge(const Plan& pl, const int32_t* lens, int64_t rows, int64_t n, int 
   mp.k = k;
   mp.slack = pl.mslack;
   mp.sort_cap = pl.sort_cap;
-  mp.seed = seed;
+  mp.seed = mix_seed(seed);
   mp.out_vals = out_vals;
   mp.out_idx = ds::IdxOut{out_idx, pl.idx64 ? 1 : 0};
   mp.unsorted = pl.unsorted ? 1 : 0;

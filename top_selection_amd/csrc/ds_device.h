@@ -303,8 +303,10 @@ __device__ __forceinline__ uint64_t vbin_first_key(uint32_t b, uint32_t klo, uin
 // --------------------------------------------------------------------------- block order
 // Keyed Feistel bijection on [0, 2^b) (b the smallest even width >= 2 with 2^b >= m),
 // four rounds with the lowbias32 integer hash as round function, restricted to [0, m)
-// by cycle walking. Round keys come from (seed, row, slice) through the splitmix64
-// finaliser. The walk ends because the permutation's cycle through i returns to i < m.
+// by cycle walking. Round key r is the low half of the splitmix64 finaliser of
+// hs ^ (row << 33 | slice << 2 | r), hs = mix64(seed) (one value per call, mixed on the host):
+// distinct (row, slice, r) give distinct inputs to a bijection. The walk ends because the
+// permutation's cycle through i returns to i < m.
 __device__ __forceinline__ uint64_t mix64(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
@@ -333,15 +335,14 @@ struct BlockOrder {
   uint32_t key[4];
   uint32_t half, mask, m;
 
-  __device__ __forceinline__ void init(uint64_t seed, uint32_t row, uint32_t slice, uint32_t m_) {
-    constexpr uint64_t G = 0x9E3779B97F4A7C15ull;
+  // hs: the call's mixed seed, mix64(seed), computed once on the host
+  __device__ __forceinline__ void init(uint64_t hs, uint32_t row, uint32_t slice, uint32_t m_) {
     // lane l derives key l & 3 in vector registers; the four keys are then read back
     const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    const uint64_t vseed = (static_cast<uint64_t>(to_vgpr(static_cast<uint32_t>(seed >> 32))) << 32) |
-                           to_vgpr(static_cast<uint32_t>(seed));
-    uint64_t h = mix64(vseed + G * (static_cast<uint64_t>(to_vgpr(row)) + 1));
-    h = mix64(h + G * (static_cast<uint64_t>(slice) + 1));
-    const uint32_t mine = static_cast<uint32_t>(mix64(h + G * static_cast<uint64_t>((lane & 3u) + 1)));
+    const uint64_t vhs = (static_cast<uint64_t>(to_vgpr(static_cast<uint32_t>(hs >> 32))) << 32) |
+                         to_vgpr(static_cast<uint32_t>(hs));
+    const uint64_t tag = (static_cast<uint64_t>(to_vgpr(row)) << 33) | (static_cast<uint64_t>(slice) << 2) | (lane & 3u);
+    const uint32_t mine = static_cast<uint32_t>(mix64(vhs ^ tag));
 #pragma unroll
     for (int r = 0; r < 4; ++r) key[r] = __builtin_amdgcn_readlane(mine, r);
     uint32_t b = 2;
