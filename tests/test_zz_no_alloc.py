@@ -13,9 +13,9 @@ from workloads import gen
 pytestmark = pytest.mark.gpu
 
 # (label, input, k), each input smaller than the one before: a plan near the array's size
-# (k = 4096 over 63 rows of 131072: 4 slices' lists and the shared row thresholds, 8258048
+# (k = 4096 over 125 rows of 131072: 2 slices' lists and the shared row thresholds, 8193000
 # of its 8388608 bytes), indexer rows, then smaller split plans
-CASES = [("bf16 63x131072 k4096 (near the array size)", lambda: gen.rows_family("normal", gen.BF16, 83, 63, 131072),
+CASES = [("bf16 125x131072 k4096 (near the array size)", lambda: gen.rows_family("normal", gen.BF16, 83, 125, 131072),
           4096),
          ("indexer rows 48x131072 k512", lambda: gen.WORKLOADS["c2_indexer"].make(rows=48), 512),
          ("fp32 3x300000 k64 ties", lambda: gen.rows_family("ties", gen.FP32, 82, 3, 300000), 64),
@@ -91,7 +91,7 @@ def test_noalloc_graph_replays_with_calls_between():
 
 def test_noalloc_refuses_a_plan_beyond_the_array():
     import torch
-    rows, n, k = 100, 131072, 4096
+    rows, n, k = 130, 131072, 4096
     wsb = ts.ds_topk_workspace_size(rows, n, k, ts.BF16)
     assert wsb > ts.DS_NOALLOC_SCRATCH_BYTES
     xd = torch.zeros((rows, n), dtype=torch.bfloat16, device="cuda")
