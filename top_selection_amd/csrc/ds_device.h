@@ -1471,17 +1471,17 @@ __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_
 // at0 + rank, or, with pairs, as pairs at pairs[rank]. The lists are loaded into LDS as
 // composites (lds: S * k 64-bit words, then S 32-bit prefix lengths); an entry's place in
 // the merged order is its position in its own list plus, for every other list, the number
-// of that list's entries that rank above it (binary searches, all lists searched in the
-// same step with clamped, always valid indices; equal entries of earlier lists count as
-// above). Padding (composite 0) ranks below every element; it is placed only when the lists
-// hold fewer than k elements together, as padding. Places the entries of lists [l0, l1)
-// (all lists are loaded and searched); each thread places EB entries at a time, their
-// searches interleaved step by step (long lists: the searches' LDS round trips overlap).
+// of that list's entries that rank above it (binary searches, the other lists searched in
+// the same step; equal entries of earlier lists count as above). Padding (composite 0)
+// ranks below every element; it is placed only when the lists hold fewer than k elements
+// together, as padding. Places the entries of lists [l0, l1) (all lists are loaded); each
+// thread places EB entries at a time, their searches interleaved step by step (long lists:
+// the searches' LDS round trips overlap).
 template <int DT, int WAVES, uint32_t MAXS, uint32_t EB>
 __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint32_t k, uint32_t pk, uint64_t* lds,
                                               void* out_vals, IdxOut out_idx, uint2* pairs, uint64_t at0,
                                               uint32_t l0, uint32_t l1) {
-  constexpr uint32_t NT = WAVES * 64;
+  constexpr uint32_t NT = WAVES * 64, MO = MAXS - 1;  // MO: the other lists an entry searches
   const uint32_t tid = threadIdx.x, total = S * k;
   __attribute__((address_space(3))) uint64_t* lw = lds_ptr(lds);
   // fill: LU 16-byte loads (two entries each) in flight per thread before their LDS writes
@@ -1522,11 +1522,11 @@ __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint
   }
   const uint64_t T = ta > tb ? ta : tb;
   const uint32_t top = 1u << (31u - static_cast<uint32_t>(__builtin_clz(k)));  // largest power of two <= k
-  // nq[q]: the length of list q's prefix at or above T. Entries that rank above an entry at
-  // or above T are themselves above T, so each search stays inside that prefix, and lists
-  // with an empty prefix are not searched. Found for groups of 8 or more lists (for fewer,
+  // maxn: the longest of the lists' prefixes at or above T. Entries that rank above an entry
+  // at or above T are themselves above T, so no count exceeds its list's prefix, and the
+  // searches need only cover maxn places. Found for groups of 8 or more lists (for fewer,
   // the extra search and barrier cost more than they save).
-  uint32_t nq[MAXS], top_n = top;
+  uint32_t top_n = top, maxn = k;
   if constexpr (MAXS >= 8) {
     __attribute__((address_space(3))) uint32_t* nql = lds_ptr(reinterpret_cast<uint32_t*>(lds + S * k));
     if (tid < S) {
@@ -1536,21 +1536,22 @@ __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint
       nql[tid] = n;
     }
     lds_sync();
-    uint32_t maxn = 0;
+    maxn = 0;
 #pragma unroll
-    for (uint32_t q = 0; q < MAXS; ++q) {
-      nq[q] = q < S ? nql[q] : 0u;
-      maxn = max(maxn, nq[q]);
-    }
+    for (uint32_t q = 0; q < MAXS; ++q) maxn = max(maxn, q < S ? nql[q] : 0u);
     top_n = maxn ? 1u << (31u - static_cast<uint32_t>(__builtin_clz(maxn))) : 0u;
-  } else {
-#pragma unroll
-    for (uint32_t q = 0; q < MAXS; ++q) nq[q] = q < S ? k : 0u;
   }
+  // The counts: every count is at most N (k, or the longest prefix); m is the largest power
+  // of two <= N. A first probe at m - 1 leaves a window of m counts, [0, m) or [N - m + 1, N]
+  // (a count of at least m is at least N - m + 1, as N < 2m), and binary steps m/2 ... 1 find
+  // the count inside it (Shar's search for lengths that are not powers of two): every probe
+  // lands inside its list, so the steps need no clamps. An entry's own list is not searched,
+  // and a list before its own, whose equal entries rank above it, is searched for c - 1.
+  const uint32_t N = maxn, m = top_n;
   const uint32_t e_end = l1 * k;
   for (uint32_t e0 = l0 * k + tid; e0 < e_end; e0 += EB * NT) {
-    uint64_t c[EB];
-    uint32_t s[EB], pos[EB][MAXS];
+    uint64_t c[EB], cq[EB][MO];
+    uint32_t s[EB], ad[EB][MO];  // ad: LDS byte address of the list's first entry past the count
     bool act[EB];
 #pragma unroll
     for (uint32_t b = 0; b < EB; ++b) {
@@ -1559,9 +1560,15 @@ __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint
 #pragma unroll
       for (uint32_t q = 1; q < MAXS; ++q) s[b] += (q < S && e >= q * k) ? 1u : 0u;
       c[b] = e < e_end ? lw[e] : 0ull;
-      act[b] = e < e_end && c[b] >= T;  // entries below T are not placed
+      // entries below T are not placed, nor is padding past the first list: the earlier
+      // lists' k entries rank above it
+      act[b] = e < e_end && c[b] >= T && (c[b] != 0u || s[b] == 0u);
 #pragma unroll
-      for (uint32_t q = 0; q < MAXS; ++q) pos[b][q] = 0;
+      for (uint32_t q = 0; q < MO; ++q) {
+        const uint32_t oq = q < s[b] ? q : q + 1u;  // the q-th list other than the entry's own
+        ad[b][q] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lw + min(oq, S - 1u) * k));
+        cq[b][q] = q < s[b] && act[b] ? c[b] - 1u : c[b];
+      }
     }
     // a list's entries at or above T are its first ones, so the waves past them have nothing
     // to place and skip the search
@@ -1569,26 +1576,39 @@ __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint
 #pragma unroll
     for (uint32_t b = 0; b < EB; ++b) any = any || act[b];
     if (ballot(any) == 0) continue;
-    for (uint32_t step = top_n; step > 0; step >>= 1) {
-      uint64_t x[EB][MAXS];
+    auto at = [](uint32_t a) {
+      return *reinterpret_cast<__attribute__((address_space(3))) const uint64_t*>(static_cast<uintptr_t>(a));
+    };
+    if (m > 0) {
+      uint64_t x[EB][MO];
 #pragma unroll
       for (uint32_t b = 0; b < EB; ++b)
 #pragma unroll
-        for (uint32_t q = 0; q < MAXS; ++q)  // always a valid address; empty prefixes never move pos
-          x[b][q] = lw[min(q, S - 1u) * k + min(pos[b][q] + step, max(nq[q], 1u)) - 1u];
+        for (uint32_t q = 0; q < MO; ++q) x[b][q] = at(ad[b][q] + 8u * (m - 1u));
 #pragma unroll
       for (uint32_t b = 0; b < EB; ++b)
 #pragma unroll
-        for (uint32_t q = 0; q < MAXS; ++q) {
-          const bool above = x[b][q] > c[b] || (q < s[b] && x[b][q] == c[b]);
-          pos[b][q] = (pos[b][q] + step <= nq[q] && above) ? pos[b][q] + step : pos[b][q];
-        }
+        for (uint32_t q = 0; q < MO; ++q) ad[b][q] += x[b][q] > cq[b][q] ? 8u * (N - m + 1u) : 0u;
+      for (uint32_t step = m >> 1; step > 0; step >>= 1) {
+#pragma unroll
+        for (uint32_t b = 0; b < EB; ++b)
+#pragma unroll
+          for (uint32_t q = 0; q < MO; ++q) x[b][q] = at(ad[b][q] + 8u * (step - 1u));
+#pragma unroll
+        for (uint32_t b = 0; b < EB; ++b)
+#pragma unroll
+          for (uint32_t q = 0; q < MO; ++q) ad[b][q] += x[b][q] > cq[b][q] ? 8u * step : 0u;
+      }
     }
 #pragma unroll
     for (uint32_t b = 0; b < EB; ++b) {
       uint32_t rank = e0 + b * NT - s[b] * k;
 #pragma unroll
-      for (uint32_t q = 0; q < MAXS; ++q) rank += (q < S && q != s[b]) ? pos[b][q] : 0u;
+      for (uint32_t q = 0; q < MO; ++q) {
+        const uint32_t oq = q < s[b] ? q : q + 1u;
+        const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lw + min(oq, S - 1u) * k));
+        rank += oq < S ? (ad[b][q] - a0) / 8u : 0u;  // past the last list: a clamped copy, not counted
+      }
       if (act[b] && rank < k) store_out<DT>(out_vals, out_idx, pairs, at0 + rank, c[b]);
     }
   }
