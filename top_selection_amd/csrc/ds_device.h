@@ -698,6 +698,7 @@ struct OutSpec {
   IdxOut idx;
   uint2* pairs;
   uint64_t row;
+  bool on = true;  // false: the caller writes the survivors itself (no sorted output here)
 };
 
 // A final compaction sorts its survivors itself (a counting sort over its value bins) when
@@ -1035,7 +1036,7 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
   pv.k = k;
   pv.vbin_p = 0;
   pv.vm = vok && vbins_of<DT>(vlo_key, vhi_key, pv.vb);
-  bool one_pass = fin && so && pv.vm && n <= kFinalPer * NT;
+  bool one_pass = fin && so && so->on && pv.vm && n <= kFinalPer * NT;
   if (one_pass &&
       final_sorted<WAVES, DT, RAW>(sg, k, *so, pv.vb, hist2 + kBins * (hpar & 1u), hist2 + kBins * ((hpar + 1u) & 1u),
                                    cbuf, sc, tkey, tidx)) {
@@ -1075,7 +1076,7 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
       uint32_t bin, above, c;
       scan_select(h, need, lane, bin, above, c);
       uint32_t blo = 0, bhi = 0;
-      if (so && fin && pv.vm && c <= kListCap) {
+      if (so && so->on && fin && pv.vm && c <= kListCap) {
         // Counting sort for the output: each bin above the pivot gets its first slot (the
         // entries of the higher bins come first), written over its count, and blo becomes
         // the largest such count. Lane l holds bins [32 (63 - l), 32 (64 - l)).
@@ -1170,7 +1171,7 @@ __device__ void compact(const Segs& sg, uint32_t* dk, uint32_t* di, uint32_t k, 
   cnt = cnt < kListCap ? cnt : kListCap;  // more only if (key, index) pairs repeat
   // the final pass's histogram holds bin slots when the output can be sorted here
   uint32_t* const slots = hist2 + kBins * ((hpar + 1u) & 1u);
-  const bool srt = so && fin && pv.vm && sc.pub[4] <= kSortedBinCap;
+  const bool srt = so && so->on && fin && pv.vm && sc.pub[4] <= kSortedBinCap;
 
   // scatter: entries above the pivot window go to the destination, the window's to the list
   scatter_all<DT>(sg, tid, NT, lane, pv, dk, di, sc, srt ? slots : nullptr);
@@ -1466,9 +1467,18 @@ __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_
 
 // --------------------------------------------------------------------------- slice merge
 
+// Where a list merge writes its k entries: outputs vals/idx from row offset at0, or pairs.
+struct MergeOut {
+  void* vals;
+  IdxOut idx;
+  uint2* pairs;
+  uint64_t at0;
+};
+
 // Merge of S sorted lists (S <= MAXS <= kMaxListGroup, k entries each, best first, as
 // (key, index) pairs at src[s * k + i]) into their k best, sorted: written to the outputs at
-// at0 + rank, or, with pairs, as pairs at pairs[rank]. The lists are loaded into LDS as
+// at0 + rank, or, with pairs, as pairs at pairs[rank] (outs() gives them, a MergeOut; it is
+// called once the lists are loaded). The lists are loaded into LDS as
 // composites (lds: S * k 64-bit words, then S 32-bit prefix lengths); an entry's place in
 // the merged order is its position in its own list plus, for every other list, the number
 // of that list's entries that rank above it (binary searches, the other lists searched in
@@ -1477,10 +1487,9 @@ __device__ __forceinline__ void sort_and_store(const uint32_t* fk, const uint32_
 // together, as padding. Places the entries of lists [l0, l1) (all lists are loaded); each
 // thread places EB entries at a time, their searches interleaved step by step (long lists:
 // the searches' LDS round trips overlap).
-template <int DT, int WAVES, uint32_t MAXS, uint32_t EB>
+template <int DT, int WAVES, uint32_t MAXS, uint32_t EB, class Outs>
 __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint32_t k, uint32_t pk, uint64_t* lds,
-                                              void* out_vals, IdxOut out_idx, uint2* pairs, uint64_t at0,
-                                              uint32_t l0, uint32_t l1) {
+                                              Outs outs, uint32_t l0, uint32_t l1) {
   constexpr uint32_t NT = WAVES * 64, MO = MAXS - 1;  // MO: the other lists an entry searches
   const uint32_t tid = threadIdx.x, total = S * k;
   __attribute__((address_space(3))) uint64_t* lw = lds_ptr(lds);
@@ -1508,6 +1517,8 @@ __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint
   else
     fill(std::integral_constant<uint32_t, 8>{});
   lds_sync();
+  // the outputs: read now, their loads overlap the searches
+  const MergeOut mo = outs();
   // Entries below T cannot reach the first k places, so they are not searched: one list's
   // k-th entry has k entries (its list's first k) at or above it, and each of the S lists
   // has ceil(k/S) entries at or above the smallest of the lists' ceil(k/S)-th entries; T is
@@ -1609,7 +1620,7 @@ __device__ __forceinline__ void merge_lists_t(const uint2* src, uint32_t S, uint
         const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lw + min(oq, S - 1u) * k));
         rank += oq < S ? (ad[b][q] - a0) / 8u : 0u;  // past the last list: a clamped copy, not counted
       }
-      if (act[b] && rank < k) store_out<DT>(out_vals, out_idx, pairs, at0 + rank, c[b]);
+      if (act[b] && rank < k) store_out<DT>(mo.vals, mo.idx, mo.pairs, mo.at0 + rank, c[b]);
     }
   }
 }
@@ -1659,6 +1670,58 @@ struct BodyOut {
   bool sorted;           // the final compaction already wrote the sorted output
 };
 
+// Stream geometry of a DeepSelect body: items of IB bytes (raw elements, or 8-byte (key,
+// index) pairs for the merge kernel), VEC per lane per 16-byte chunk, blocks of B items (each
+// wave filters CPW chunks of every block).
+template <int DT, int WAVES, int CPW, bool MERGE>
+struct StreamGeom {
+  static constexpr uint32_t IB = MERGE ? 8 : (DT == DS_BF16 ? 2 : 4);  // bytes per item
+  static constexpr uint32_t VEC = 16 / IB;                            // items per lane per chunk
+  static constexpr uint32_t CHUNK = 64 * VEC;
+  static constexpr uint32_t B = WAVES * CPW * CHUNK;
+  // byte offset of this lane's part of chunk t of block bid (no read for bid >= m)
+  static __device__ __forceinline__ uint32_t offset(uint32_t bid, uint32_t t, uint32_t m, uint32_t wave,
+                                                    uint32_t lane) {
+    return bid < m ? (bid * B + (wave + t * WAVES) * CHUNK + lane * VEC) * IB : kNoLoad;
+  }
+};
+
+// Block order: the permutation `ord` is over groups of 2^gshift consecutive blocks; the i-th
+// block read is block (i mod 2^gshift) of group ord(i >> gshift). Positions past the last
+// block (the last group's padding, or steps past the end, i >= m_iter) give the empty id m.
+__device__ __forceinline__ uint32_t order_bid(const BlockOrder& ord, uint32_t i, uint32_t gshift, uint32_t m,
+                                              uint32_t m_iter) {
+  if (i >= m_iter) return m;
+  const uint32_t b = (ord.at(i >> gshift) << gshift) | (i & ((1u << gshift) - 1u));
+  return b < m ? b : m;
+}
+
+// The first D blocks of a stream's order: their ids and their loads in flight. A kernel
+// requests them before the rest of its set-up (parameter reads from the argument block
+// included), so that their latency overlaps all of it.
+template <int D, int CPW>
+struct FirstBlocks {
+  u32x4 buf[D][CPW];
+  uint32_t bids[D];
+};
+
+template <int DT, int WAVES, int CPW, int D, bool MERGE>
+__device__ __forceinline__ void first_blocks(__amdgpu_buffer_rsrc_t rs, uint32_t len, const BlockOrder& ord,
+                                             uint32_t gshift, FirstBlocks<D, CPW>& fb) {
+  using G = StreamGeom<DT, WAVES, CPW, MERGE>;
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+  const uint32_t m = (len + G::B - 1) / G::B;
+  const uint32_t m_iter = ((m + (1u << gshift) - 1u) >> gshift) << gshift;
+  // lane l evaluates position l mod D in vector registers (see to_vgpr)
+  const uint32_t first_bid = order_bid(ord, to_vgpr(0u) + lane % static_cast<uint32_t>(D), gshift, m, m_iter);
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    fb.bids[d] = __builtin_amdgcn_readlane(first_bid, d);
+#pragma unroll
+    for (uint32_t t = 0; t < CPW; ++t) fb.buf[d][t] = load16(rs, G::offset(fb.bids[d], t, m, wave, lane));
+  }
+}
+
 // Schedule. The design note checks the buffer once after each whole block ("lockstep":
 // a workgroup barrier after every block, then the check). By default the waves instead
 // stream independently: each wave filters its share of block after block, reserves buffer
@@ -1681,12 +1744,10 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
                                                 uint32_t idx_base, uint32_t k, uint32_t B2, const BlockOrder& ord,
                                                 uint32_t ilo, uint32_t ihi, bool lockstep, uint32_t warm,
                                                 unsigned long long* share, bool presample, uint32_t gshift,
-                                                const OutSpec* fso, BodyOut& out) {
+                                                FirstBlocks<D, CPW>& fb, const OutSpec* fso, BodyOut& out) {
+  using G = StreamGeom<DT, WAVES, CPW, MERGE>;
   constexpr uint32_t NT = WAVES * 64;
-  constexpr uint32_t IB = MERGE ? 8 : (DT == DS_BF16 ? 2 : 4);  // bytes per item
-  constexpr uint32_t VEC = 16 / IB;                            // items per lane per chunk
-  constexpr uint32_t CHUNK = 64 * VEC;
-  constexpr uint32_t B = WAVES * CPW * CHUNK;
+  constexpr uint32_t VEC = G::VEC, CHUNK = G::CHUNK, B = G::B;
   constexpr uint32_t SHARE = CPW * CHUNK;  // items of one block that one wave filters
   constexpr uint32_t key_hi = DT == DS_BF16 ? 0xFFFFu : 0xFFFFFFFFu;  // largest possible key
   static_assert(D >= 2 && D <= 4, "two to four buffers");
@@ -1698,19 +1759,12 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   const uint32_t ci_off = lds_addr(L.ci) - ck_addr;
   const uint32_t m = (len + B - 1) / B;
 
-  // Block order: the permutation `ord` is over groups of 2^gshift consecutive blocks (ng of
-  // them); the i-th block read is block (i mod 2^gshift) of group ord(i >> gshift). Positions
-  // past the last block (the last group's padding, or steps past the end) read nothing. The
-  // group order is a table for up to kOrdCap groups, computed on the fly beyond.
+  // Block order (order_bid): ng groups of 2^gshift blocks. The group order is a table for up
+  // to kOrdCap groups, computed on the fly beyond.
   const uint32_t ng = (m + (1u << gshift) - 1u) >> gshift, m_iter = ng << gshift;
   // (a stream of at most D blocks reads only the first D ids, computed directly: no table)
   const bool tab = ng <= kOrdCap && m_iter > static_cast<uint32_t>(D);
   // block id of the i-th block read, from the permutation itself (direct) or its table
-  auto bid_direct = [&](uint32_t i) -> uint32_t {
-    if (i >= m_iter) return m;
-    const uint32_t b = (ord.at(i >> gshift) << gshift) | (i & ((1u << gshift) - 1u));
-    return b < m ? b : m;
-  };
   // (the table's first 64 entries are also held in a vector register, lane l entry l, once
   // it is built: a lookup there is a lane read, with no LDS access queued behind the appends)
   uint32_t ordv = 0;
@@ -1741,22 +1795,13 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
   [[maybe_unused]] uint64_t t_mark = 0;
   uint64_t my_reads = 0, my_jsum = 0;
 
-  auto addr = [&](uint32_t bid, uint32_t t) -> uint32_t {
-    return bid < m ? (bid * B + (wave + t * WAVES) * CHUNK + lane * VEC) * IB : kNoLoad;
-  };
+  auto addr = [&](uint32_t bid, uint32_t t) -> uint32_t { return G::offset(bid, t, m, wave, lane); };
 
-  // The first D blocks are requested before anything else, so their latency overlaps the
-  // set-up below (their ids come from the permutation directly, the rest from its table).
-  u32x4 buf[D][CPW];
-  uint32_t bids[D];
-  // the first D block ids: lane l evaluates position l mod D in vector registers (see to_vgpr)
-  const uint32_t first_bid = bid_direct(to_vgpr(0u) + lane % static_cast<uint32_t>(D));
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    bids[d] = __builtin_amdgcn_readlane(first_bid, d);
-#pragma unroll
-    for (uint32_t t = 0; t < CPW; ++t) buf[d][t] = load16(rs, addr(bids[d], t));
-  }
+  // The first D blocks were requested by the kernel (first_blocks) before anything else, so
+  // their latency overlaps the set-up below (their ids come from the permutation directly,
+  // the rest from its table).
+  auto& buf = fb.buf;
+  auto& bids = fb.bids;
 
   // workgroup state: histograms, counters, the order table
   for (uint32_t i = 4u * tid; i < 2u * kBins; i += 4u * NT) *reinterpret_cast<uint4*>(L.hist + i) = make_uint4(0, 0, 0, 0);
@@ -2232,15 +2277,40 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
 }
 
 // --------------------------------------------------------------------------- select kernel
+// The parameter block P at byte offset OFF of the kernel's argument segment, through a
+// pointer the compiler cannot trace back to the segment: reads of it are issued where the
+// code reads them, never hoisted above earlier code.
+template <class P, uint32_t OFF>
+__device__ __forceinline__ const P& params_after_loads() {
+  using KPtr = const __attribute__((address_space(4))) uint8_t*;
+  KPtr a = (KPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(a));
+  return *(const P*)(a + OFF);
+}
+
+// Byte offset of select_kernel's parameter block in its argument segment: the arguments
+// before it, each at its natural alignment (the AMDGPU kernel argument layout), take 64
+// bytes (five 8-byte values, three int32, padding to 8, the lengths pointer). The kernel's
+// signature and this offset change together.
+constexpr uint32_t align_to(uint32_t v, uint32_t a) { return (v + a - 1u) / a * a; }
+constexpr uint32_t kSelectParamsOffset =
+    align_to(align_to(5u * 8u + 3u * 4u, alignof(const int32_t*)) + sizeof(const int32_t*), alignof(SelectParams));
+static_assert(kSelectParamsOffset == 64u, "select_kernel argument layout");
+
+// Byte offset of merge_lists_kernel's parameter block: a pointer, two 8-byte values and eight
+// int32 before it take 56 bytes. The kernel's signature and this offset change together.
+constexpr uint32_t kMergeParamsOffset = align_to(3u * 8u + 8u * 4u, alignof(MergeParams));
+static_assert(kMergeParamsOffset == 56u, "merge_lists_kernel argument layout");
 // EXT: the instantiation that serves ragged rows, the warm-up window and the shared row
 // threshold; the plain one (EXT = false) has none of their code. The parameters the first
 // loads depend on come as scalars ahead of the rest, so that the hardware can preload them
-// into scalar registers at wave launch (the build asks for 15 dwords) instead of the waves
+// into scalar registers at wave launch (14 dwords, up to the row count) instead of the waves
 // waiting on a load of the argument block.
 template <int DT, int WAVES, int CPW, bool STATS, bool EXT>
 __global__ __launch_bounds__(WAVES * 64) void select_kernel(const uint8_t* px, int64_t pstride, int64_t pn, int64_t pslice_len,
-                                                                  uint64_t pseed, const int32_t* plens, int32_t pslices,
-                                                                  int32_t pgshift, int32_t prows, SelectParams p) {
+                                                                  uint64_t pseed, int32_t pslices, int32_t pgshift,
+                                                                  int32_t prows, const int32_t* plens,
+                                                                  [[maybe_unused]] SelectParams p) {
   constexpr uint32_t NT = WAVES * 64;
   constexpr uint32_t EB = DT == DS_BF16 ? 2 : 4;
   constexpr uint32_t B = WAVES * CPW * 64 * (16 / EB);
@@ -2263,14 +2333,14 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(const uint8_t* px, i
   const int64_t rest = n_row - static_cast<int64_t>(slice_lo);
   const uint32_t len = rest <= 0 ? 0u : static_cast<uint32_t>(min(pslice_len, rest));
   const uint32_t m = (len + B - 1) / B;
-  const uint32_t k = static_cast<uint32_t>(p.k);
-  const uint32_t B2 = static_cast<uint32_t>(p.slack);
+  constexpr int D = depth_for(WAVES, CPW);
   [[maybe_unused]] uint64_t t_start = 0;
   if constexpr (STATS) t_start = wall_clock64();
 
   if (EXT && len == 0) {
     // a slice past its row's end (ragged rows): its k entries are all padding, which ranks
     // below every element (the row's outputs past its length read index -1)
+    const uint32_t k = static_cast<uint32_t>(p.k);
     if (pslices == 1) {
       for (uint32_t i = tid; i < k; i += NT) store_out<DT>(p.out_vals, p.out_idx, nullptr, static_cast<uint64_t>(row) * k + i, 0ull);
     } else {
@@ -2284,13 +2354,11 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(const uint8_t* px, i
         o->monotone = 1;
         o->slice_lo = slice_lo;
         o->block = B;
-        o->slack = B2;
+        o->slack = static_cast<uint32_t>(p.slack);
       }
     }
     return;
   }
-
-  const Lay L = lay_of(lds, k, B2, B);
 
   const uint8_t* base = px + static_cast<uint64_t>(row) * pstride + static_cast<uint64_t>(slice_lo) * EB;
   // Range = the slice rounded up to whole 16-byte chunks: the hardware checks whole dwords, so
@@ -2301,21 +2369,31 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(const uint8_t* px, i
   const uint32_t gshift = static_cast<uint32_t>(pgshift);
   BlockOrder ord;
   ord.init(pseed, row, slice, (m + (1u << gshift) - 1u) >> gshift);
+  FirstBlocks<D, CPW> fb;
+  first_blocks<DT, WAVES, CPW, D, false>(rs, len, ord, gshift, fb);
+
+  // The rest of the parameters come from the argument block in memory (the preloaded ones
+  // end with the row count). They are read through a pointer the compiler cannot see
+  // through, so that their loads are issued after the first block loads and their latency
+  // overlaps those (hoisted to the top, the loads' waits came first: register spills of the
+  // loaded values wait for them).
+  const SelectParams& q = params_after_loads<SelectParams, kSelectParamsOffset>();
+  const uint32_t k = static_cast<uint32_t>(q.k);
+  const uint32_t B2 = static_cast<uint32_t>(q.slack);
+  const Lay L = lay_of(lds, k, B2, B);
 
   // the final compaction writes the sorted output itself when it can: the row's outputs, or
   // the slice's sorted list for the list merge
-  OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
+  OutSpec fso{q.out_vals, IdxOut{q.out_idx.p, q.out_idx.wide}, nullptr, row};  // (field by field: in registers)
   if (pslices > 1)
-    fso = OutSpec{nullptr, IdxOut{nullptr, 0}, p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + slice * k, 0};
-  const bool own_sort = pslices == 1 || p.sorted_lists;
+    fso = OutSpec{nullptr, IdxOut{nullptr, 0}, q.ws + static_cast<uint64_t>(row) * q.ws_row_entries + slice * k, 0};
+  fso.on = pslices == 1 || q.sorted_lists;
 
   BodyOut bo;
-  deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), false, STATS>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo,
-                                                                   slice_lo + len - 1u, p.lockstep != 0,
-                                                                   EXT ? static_cast<uint32_t>(p.warmup) : 0u,
-                                                                   EXT && p.share ? p.share + row : nullptr,
-                                                                   p.presample != 0, gshift,
-                                                                   own_sort ? &fso : nullptr, bo);
+  deepselect_body<DT, WAVES, CPW, D, false, STATS>(L, sc, rs, len, slice_lo, k, B2, ord, slice_lo, slice_lo + len - 1u,
+                                                q.lockstep != 0, EXT ? static_cast<uint32_t>(q.warmup) : 0u,
+                                                EXT && q.share ? q.share + row : nullptr, q.presample != 0, gshift,
+                                                fb, &fso, bo);
 
   if constexpr (STATS) {
     const uint32_t lane = tid & 63u;
@@ -2330,7 +2408,7 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(const uint8_t* px, i
     }
     lds_sync();
     if (tid == 0) {
-      ds_stats* o = p.stats + (row * static_cast<uint32_t>(pslices) + slice);
+      ds_stats* o = q.stats + (row * static_cast<uint32_t>(pslices) + slice);
       o->appended = sc.st_a;
       o->compactions = sc.st_r;
       o->work = sc.st_w;
@@ -2350,26 +2428,26 @@ __global__ __launch_bounds__(WAVES * 64) void select_kernel(const uint8_t* px, i
 
   if (bo.sorted) {
     // done by the final compaction
-  } else if (pslices == 1 && p.unsorted) {
+  } else if (pslices == 1 && q.unsorted) {
     // the k survivors as the final compaction left them (no sort)
     for (uint32_t i = tid; i < k; i += NT)
-      store_out<DT>(p.out_vals, p.out_idx, nullptr, static_cast<uint64_t>(row) * k + i, comp_of(bo.fk[i], bo.fi[i]));
+      store_out<DT>(q.out_vals, q.out_idx, nullptr, static_cast<uint64_t>(row) * k + i, comp_of(bo.fk[i], bo.fi[i]));
   } else if (pslices == 1) {
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k,
-                              p.out_vals, p.out_idx, nullptr, row);
-  } else if (!p.sorted_lists) {
-    uint2* const dst = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries + static_cast<uint64_t>(slice) * k;
+                              q.out_vals, q.out_idx, nullptr, row);
+  } else if (!q.sorted_lists) {
+    uint2* const dst = q.ws + static_cast<uint64_t>(row) * q.ws_row_entries + static_cast<uint64_t>(slice) * k;
     for (uint32_t i = tid; i < k; i += NT) dst[i] = make_uint2(bo.fk[i], bo.fi[i]);
   } else {
     // the list-merge kernel merges the slices' sorted lists
-    uint2* const rws = p.ws + static_cast<uint64_t>(row) * p.ws_row_entries;
+    uint2* const rws = q.ws + static_cast<uint64_t>(row) * q.ws_row_entries;
     sort_and_store<DT, WAVES>(bo.fk, bo.fi, L.ck + L.k4, L.ci + L.k4, reinterpret_cast<uint64_t*>(L.hist), k, nullptr,
                               IdxOut{nullptr, 0}, rws + slice * k, 0);
   }
   if constexpr (STATS) {
     if (tid == 0) {
       const uint64_t t_end = wall_clock64();
-      ds_stats* o = p.stats + (row * static_cast<uint32_t>(pslices) + slice);
+      ds_stats* o = q.stats + (row * static_cast<uint32_t>(pslices) + slice);
       o->t_total_ns = (t_end - t_start) * 10;
       o->t_final_ns = (t_end - sc.st_tf) * 10;
     }
@@ -2430,12 +2508,14 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeParams p) {
 
   BlockOrder ord;
   ord.init(p.seed, row, 0x7FFFFFFFu, m);
+  constexpr int D = depth_for(WAVES, CPW);
+  FirstBlocks<D, CPW> fb;
+  first_blocks<DT, WAVES, CPW, D, true>(rs, len, ord, 0u, fb);
 
   const OutSpec fso{p.out_vals, p.out_idx, nullptr, row};
   BodyOut bo;
-  deepselect_body<DT, WAVES, CPW, depth_for(WAVES, CPW), true, false>(L, sc, rs, len, 0u, k, B2, ord, 0u,
-                                                                  static_cast<uint32_t>(p.n - 1), false, 0u,
-                                                                  nullptr, p.presample != 0, 0u, &fso, bo);
+  deepselect_body<DT, WAVES, CPW, D, true, false>(L, sc, rs, len, 0u, k, B2, ord, 0u, static_cast<uint32_t>(p.n - 1),
+                                                  false, 0u, nullptr, p.presample != 0, 0u, fb, &fso, bo);
   if (bo.sorted) return;
   if (p.unsorted) {
     for (uint32_t i = tid; i < k; i += NT)
@@ -2459,7 +2539,7 @@ template <int DT, int WAVES, uint32_t MAXS, uint32_t EB>
 __global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(const uint2* pws, int64_t prow_entries, int64_t prow0,
                                                                  int32_t plists, int32_t pgroup, int32_t pper,
                                                                  int32_t pk_, int32_t ppk, int32_t gx, int32_t gy,
-                                                                 int32_t gz, MergeParams p) {
+                                                                 int32_t gz, [[maybe_unused]] MergeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const uint32_t S = static_cast<uint32_t>(plists), G = static_cast<uint32_t>(pgroup);
   const uint32_t per = static_cast<uint32_t>(pper), k = static_cast<uint32_t>(pk_);
@@ -2477,10 +2557,18 @@ __global__ __launch_bounds__(WAVES * 64) void merge_lists_kernel(const uint2* pw
   if (l0 >= gl) return;  // the same for the whole workgroup
   const uint32_t pk = gl == G ? static_cast<uint32_t>(ppk) : (k + gl - 1u) / gl;  // ceil(k / gl)
   const uint2* src = pws + row * prow_entries + static_cast<uint64_t>(first) * k;
-  uint2* pairs = p.dst ? p.dst + row * p.dst_row_entries + static_cast<uint64_t>(g) * k : nullptr;
-  const uint64_t at0 = p.dst ? 0u : row * k;
-  merge_lists_t<DT, WAVES, MAXS, EB>(src, gl, k, pk, reinterpret_cast<uint64_t*>(lds), p.out_vals, p.out_idx, pairs, at0,
-                                 l0, min(l0 + per, gl));
+  // The output parameters come from the argument block in memory, read through a pointer
+  // the compiler cannot hoist above the lists' loads (their waits would come first).
+  auto outs = [&]() {
+    const MergeParams& q = params_after_loads<MergeParams, kMergeParamsOffset>();
+    MergeOut o;
+    o.vals = q.out_vals;
+    o.idx = IdxOut{q.out_idx.p, q.out_idx.wide};
+    o.pairs = q.dst ? q.dst + row * q.dst_row_entries + static_cast<uint64_t>(g) * k : nullptr;
+    o.at0 = q.dst ? 0u : row * k;
+    return o;
+  };
+  merge_lists_t<DT, WAVES, MAXS, EB>(src, gl, k, pk, reinterpret_cast<uint64_t*>(lds), outs, l0, min(l0 + per, gl));
 }
 
 // Raises kernel KERN's dynamic-LDS limit to at least `lds` bytes on the current device. The

@@ -22,8 +22,8 @@ hipError_t launch_select_shape(const SelectParams& p, int64_t rows, size_t lds, 
   const hipError_t e = allow_lds<select_kernel<DT, W, C, STATS, EXT>>(lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((select_kernel<DT, W, C, STATS, EXT>), dim3(static_cast<uint32_t>(rows * p.slices)), dim3(W * 64),
-                     lds, stream, p.x, p.row_stride_bytes, p.n, p.slice_len, p.seed, p.lens, p.slices, p.group_shift,
-                     static_cast<int32_t>(rows), p);
+                     lds, stream, p.x, p.row_stride_bytes, p.n, p.slice_len, p.seed, p.slices, p.group_shift,
+                     static_cast<int32_t>(rows), p.lens, p);
   return hipGetLastError();
 }
 
