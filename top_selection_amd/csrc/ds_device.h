@@ -952,9 +952,9 @@ __device__ __forceinline__ bool final_sorted(const Segs& sg, uint32_t k, const O
   lds_sync();
 
   // the entry at slot p: its bin's first slot plus the bin's entries that rank above it. Slots
-  // go to threads in order, so a wave's lanes share a few neighbouring bins and only the waves
-  // that hold the crowded bins loop long.
-  for (uint32_t p = tid; p < above; p += NT) {
+  // go in order to the threads from wave 1 on, so a wave's lanes share a few neighbouring bins
+  // and only the waves that hold the crowded bins loop long; wave 0 ranks the pivot bin's list
+  for (uint32_t p = tid - 64u; tid >= 64u && p < above; p += NT - 64u) {
     const uint64_t me = cbuf[p];
     const uint32_t b = cbin[p];
     const uint32_t s0 = hs[b], end = s0 + h[b];
@@ -970,8 +970,9 @@ __device__ __forceinline__ bool final_sorted(const Segs& sg, uint32_t k, const O
     }
     store_out<DT>(so.vals, so.idx, so.pairs, so.row * k + s0 + r, me);
   }
-  // the pivot bin's list: the k - above best of it follow the entries above it
-  if (wave == WAVES - 1) {
+  // the pivot bin's list: the k - above best of it follow the entries above it (wave 0, the
+  // oldest of its SIMD, which the SIMD serves first)
+  if (wave == 0) {
     const bool have = lane < pcnt;
     const uint32_t lk = have ? sc.lkey[lane] : 0u, li = have ? sc.lidx[lane] : kSentinelIdx;
     const uint64_t mine = comp_of(lk, li);
