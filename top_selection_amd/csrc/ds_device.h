@@ -2021,21 +2021,46 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
         // already in flight (the next D - 1 of the order): all of them were requested at the
         // start and arrive together, and more elements give a tighter T0
         uint32_t lmax = 0;
+        if constexpr (DT == DS_BF16) {
+          // two keys per word, with packed 16-bit operations (a bf16's key is its bits with
+          // the sign bit flipped, or all of them for a negative value)
+          using u16x2 = uint16_t __attribute__((ext_vector_type(2)));
+          using i16x2 = int16_t __attribute__((ext_vector_type(2)));
+          u16x2 acc = {0, 0};
+          auto fold = [&](uint32_t w) {
+            const u16x2 x = __builtin_bit_cast(u16x2, w);
+            const u16x2 neg = __builtin_bit_cast(u16x2, __builtin_bit_cast(i16x2, x) >> 15);
+            acc = __builtin_elementwise_max(acc, x ^ (neg | static_cast<uint16_t>(0x8000u)));
+          };
 #pragma unroll
-        for (uint32_t t = 0; t < CPW; ++t) {
+          for (uint32_t t = 0; t < CPW; ++t) {
 #pragma unroll
-          for (uint32_t q = 0; q < VEC; ++q) lmax = max(lmax, key_of_score<DT>(s[t][q]));
-        }
+            for (uint32_t q = 0; q < 4; ++q) fold(bf[t][q]);
+          }
 #pragma unroll
-        for (int d = 1; d < D; ++d) {
-          if (bids[d] < m && bids[d] * B + B <= len) {
+          for (int d = 1; d < D; ++d) {
+            if (bids[d] < m && bids[d] * B + B <= len) {
 #pragma unroll
-            for (uint32_t t = 0; t < CPW; ++t) {
+              for (uint32_t t = 0; t < CPW; ++t) {
 #pragma unroll
-              for (uint32_t q = 0; q < 4; ++q) {
-                const uint32_t w = buf[d][t][q];
-                if constexpr (DT == DS_BF16) lmax = max(lmax, key_of_score<DT>(w << 16));
-                lmax = max(lmax, key_of_score<DT>(w));
+                for (uint32_t q = 0; q < 4; ++q) fold(buf[d][t][q]);
+              }
+            }
+          }
+          lmax = max(static_cast<uint32_t>(acc.x), static_cast<uint32_t>(acc.y));
+        } else {
+#pragma unroll
+          for (uint32_t t = 0; t < CPW; ++t) {
+#pragma unroll
+            for (uint32_t q = 0; q < VEC; ++q) lmax = max(lmax, key_of_score<DT>(s[t][q]));
+          }
+#pragma unroll
+          for (int d = 1; d < D; ++d) {
+            if (bids[d] < m && bids[d] * B + B <= len) {
+#pragma unroll
+              for (uint32_t t = 0; t < CPW; ++t) {
+#pragma unroll
+                for (uint32_t q = 0; q < 4; ++q) lmax = max(lmax, key_of_score<DT>(buf[d][t][q]));
               }
             }
           }
