@@ -58,11 +58,11 @@ constexpr int64_t kMaxGridRows = 65528;
 
 // One instantiation per bound on the lists merged together, and per number of entries a
 // thread searches at once.
-template <int DT, uint32_t MAXS, uint32_t EB>
+template <int DT, uint32_t MAXS, uint32_t EB, int W = kListMergeWaves>
 hipError_t launch_merge_lists_t(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
-  auto kern = merge_lists_kernel<DT, kListMergeWaves, MAXS, EB>;
+  auto kern = merge_lists_kernel<DT, W, MAXS, EB>;
   {
-    const hipError_t e = allow_lds<merge_lists_kernel<DT, kListMergeWaves, MAXS, EB>>(lds);
+    const hipError_t e = allow_lds<merge_lists_kernel<DT, W, MAXS, EB>>(lds);
     if (e != hipSuccess) return e;
   }
   const int64_t G = p.group, wpg = (G + p.per_wg - 1) / p.per_wg, groups = (p.lists + G - 1) / G;
@@ -72,7 +72,7 @@ hipError_t launch_merge_lists_t(const MergeParams& p, int64_t rows, size_t lds, 
     q.row0 = r0;
     const int64_t nr = rows - r0 < kMaxGridRows ? rows - r0 : kMaxGridRows;
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(wpg), static_cast<uint32_t>(groups), static_cast<uint32_t>(nr)),
-                       dim3(kListMergeWaves * 64), lds, stream, q.ws, q.row_entries, q.row0, q.lists, q.group, q.per_wg,
+                       dim3(W * 64), lds, stream, q.ws, q.row_entries, q.row0, q.lists, q.group, q.per_wg,
                        q.k, q.pk, static_cast<int32_t>(wpg), static_cast<int32_t>(groups), static_cast<int32_t>(nr), q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -84,13 +84,15 @@ template <int DT>
 hipError_t launch_merge_lists_dt(const MergeParams& p, int64_t rows, size_t lds, hipStream_t stream) {
   const int32_t g = p.group < p.lists ? p.group : p.lists;
   // long lists: every thread searches several entries at once (small groups keep the
-  // registers of the interleaved searches in bounds)
+  // registers of the interleaved searches in bounds), on 16 waves (a workgroup places one
+  // list either way; k = 4096: two levels 137 -> 134 us, where 16 waves for short lists
+  // were slower)
   const bool longl = p.k >= 1024;
-  if (g <= 2) return longl ? launch_merge_lists_t<DT, 2, 4>(p, rows, lds, stream)
+  if (g <= 2) return longl ? launch_merge_lists_t<DT, 2, 4, 16>(p, rows, lds, stream)
                            : launch_merge_lists_t<DT, 2, 1>(p, rows, lds, stream);
-  if (g <= 4) return longl ? launch_merge_lists_t<DT, 4, 4>(p, rows, lds, stream)
+  if (g <= 4) return longl ? launch_merge_lists_t<DT, 4, 4, 16>(p, rows, lds, stream)
                            : launch_merge_lists_t<DT, 4, 1>(p, rows, lds, stream);
-  if (g <= 8) return longl ? launch_merge_lists_t<DT, 8, 2>(p, rows, lds, stream)
+  if (g <= 8) return longl ? launch_merge_lists_t<DT, 8, 2, 16>(p, rows, lds, stream)
                            : launch_merge_lists_t<DT, 8, 1>(p, rows, lds, stream);
   static_assert(kMaxListGroup == 16, "instantiations cover groups up to kMaxListGroup");
   return launch_merge_lists_t<DT, kMaxListGroup, 1>(p, rows, lds, stream);
