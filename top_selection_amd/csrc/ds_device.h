@@ -2108,18 +2108,20 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
           // positions by vector arithmetic only (the CU's waves share one scalar unit): the
           // lane's hit count, its exclusive prefix over the wave, one reservation; every
           // element then goes to its slot or, if it is no hit, to the lane's dummy slot
-          uint32_t hb[VEC], cnt = 0;  // hb: 1 for a hit
+          // (counted in bytes, 4 a hit, so that one value is both the count and the step of
+          // the slot address)
+          uint32_t hb[VEC], cnt = 0;  // hb: 4 for a hit
 #pragma unroll
           for (uint32_t e = 0; e < VEC; ++e) {
-            hb[e] = h[e] ? 1u : 0u;
+            hb[e] = h[e] ? 4u : 0u;
             cnt += hb[e];
           }
           const uint32_t incl = wave_incl_scan(cnt);
-          const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+          const uint32_t tot = __builtin_amdgcn_readlane(incl, 63) >> 2;
           if (tot) {
             // byte addresses: the key slot (the next free one, or the dummy), the index slot
             // at a fixed distance from it
-            uint32_t pa = ck_addr + 4u * (app0 + reserve(tot, seen) + incl - cnt);
+            uint32_t pa = ck_addr + 4u * (app0 + reserve(tot, seen)) + incl - cnt;
             reserved = true;
             const uint32_t j0 = idx_base + first;
 #pragma unroll
@@ -2127,7 +2129,7 @@ __device__ __forceinline__ void deepselect_body(const Lay& L, Scalars& sc, __amd
               const uint32_t a = h[e] ? pa : dummy_addr;
               *lds_at(a) = s[t][e];
               *lds_at(a + ci_off) = j0 + e;
-              pa += 4u * hb[e];
+              pa += hb[e];
             }
           }
         }
