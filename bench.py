@@ -493,8 +493,8 @@ def main() -> int:
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across GPUs "
-              "without communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (rows would shard "
+              "across GPUs without communication). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch

@@ -297,7 +297,7 @@ int ds_topk_noalloc(const void* x, int64_t rows, int64_t n, int64_t row_stride, 
 
 /*
  * ds_probe_read -- measurement aid, not part of top-k (tutorial chapter 37, section 6.1: the
- * method is judged by how close it comes to reading the input once; this is the plain read
+ * method's measure is how close it comes to reading the input once; this is the plain read
  * of the same bytes): streams `bytes` (a multiple of
  * 16, 16-byte aligned) from src with the same 16-byte loads the scan uses and writes
  * one 32-bit word per workgroup to sink (device, >= ds_probe_sink_words(bytes) words).
